@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs for causal grouped-query attention.
+
+This module holds the workload shapes and the random draws only; it contains none of the
+attention arithmetic, and both the fp64 oracle side and the HIP side take their inputs from it.
+
+Shapes follow the two models of the NanoEuler pages (README translations, configuration
+table): the CPU model (dim 128, 4 query / 2 key-value heads, head size 32, context 512) and
+the GPU model (dim 768, 12 query / 4 key-value heads, head size 64, context 512), plus a long
+context, a planned wider model with RoPE applied in the kernel, and a tiny case.
+
+Recipe (all draws from ``numpy.random.default_rng(seed)``, PCG64, float32, in the order
+q, k, v, dO, each i.i.d. N(0, 1)):
+
+* ``boost_frac > 0``: after the dO draw, ``round(boost_frac * B * Hq * T)`` query rows, picked
+  by ``rng.permutation``, are multiplied by ``boost``; this pushes scores far from zero and
+  exercises the running-maximum bookkeeping of the online softmax.
+* ``dtype == "bf16"``: every draw is rounded to the nearest bfloat16 (ties to even) so that
+  the bf16 kernel inputs and the fp64 oracle inputs are the same numbers.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    T: int
+    D: int
+    dtype: str = "f32"          # "f32" or "bf16"
+    causal: bool = True
+    rope_base: float = 0.0      # 0 disables RoPE
+    boost_frac: float = 0.0
+    boost: float = 1.0
+    note: str = ""
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def flops_fwd(self) -> float:
+        """Algorithmic forward FLOPs: QK^T and PV, causal counted as half of dense."""
+        f = 4.0 * self.B * self.Hq * self.T * self.T * self.D
+        return f / 2 if self.causal else f
+
+    def flops_fwd_bwd(self) -> float:
+        """Forward (2 GEMMs) plus backward (5 GEMMs): 3.5x the forward."""
+        return 3.5 * self.flops_fwd()
+
+    def bytes_fwd_bwd(self) -> int:
+        """Algorithmic HBM bytes: fwd reads q,k,v and writes o,lse; bwd reads q,k,v,o,dO,lse
+        and writes dq,dk,dv."""
+        elt = 2 if self.dtype == "bf16" else 4
+        nq = self.B * self.Hq * self.T * self.D
+        nk = self.B * self.Hkv * self.T * self.D
+        nl = self.B * self.Hq * self.T
+        return elt * 6 * (nq + nk) + 8 * nl
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 4, 2, 64, 32,
+                     note="tiny causal GQA, oracle-checkable in seconds"),
+    "cpu_model": Workload("cpu_model", 8, 4, 2, 512, 32,
+                          note="CPU small-model attention layer shape"),
+    "gpu_model": Workload("gpu_model", 16, 12, 4, 512, 64, boost_frac=0.1, boost=4.0,
+                          note="GPU-model attention layer shape (dim 768)"),
+    "long_ctx": Workload("long_ctx", 4, 12, 4, 4096, 64,
+                         note="long context, tile streaming and causal skipping"),
+    "bf16_rope": Workload("bf16_rope", 16, 16, 4, 1024, 64, dtype="bf16", rope_base=10000.0,
+                          note="bf16 with RoPE applied in the kernel (dim 1024)"),
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Rounds float32 values to the nearest bfloat16 (ties to even), returned as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    return u.view(np.float32).reshape(x.shape)
+
+
+def make_inputs(w: Workload, seed: int = 0) -> dict:
+    """Returns float32 numpy arrays q, k, v, dO for workload ``w``."""
+    rng = np.random.default_rng(seed)
+    qs = (w.B, w.Hq, w.T, w.D)
+    ks = (w.B, w.Hkv, w.T, w.D)
+    q = rng.standard_normal(qs, dtype=np.float32)
+    k = rng.standard_normal(ks, dtype=np.float32)
+    v = rng.standard_normal(ks, dtype=np.float32)
+    dO = rng.standard_normal(qs, dtype=np.float32)
+    if w.boost_frac > 0:
+        rows = w.B * w.Hq * w.T
+        n = int(round(w.boost_frac * rows))
+        idx = rng.permutation(rows)[:n]
+        q.reshape(rows, w.D)[idx] *= np.float32(w.boost)
+    if w.dtype == "bf16":
+        q, k, v, dO = (round_to_bf16(a) for a in (q, k, v, dO))
+    return {"q": q, "k": k, "v": v, "dO": dO}
