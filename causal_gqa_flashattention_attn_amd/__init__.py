@@ -1,0 +1,232 @@
+"""Python binding of ``libne_attn.so``: causal grouped-query FlashAttention for MI355X (gfx950).
+
+The functions named like the C entry points (``ne_attn_fwd``, ``ne_attn_bwd``,
+``ne_attn_fwd_ex``, ``ne_attn_bwd_ex``, ``ne_attn_bwd_workspace_bytes``, ``ne_attn_strerror``)
+only marshal arguments: they read sizes from tensor shapes, pass ``data_ptr()`` and the current
+HIP stream, and raise ``NeAttnError`` on a non-zero status.  All arithmetic happens in the HIP
+kernels.  PyTorch provides device memory and streams.
+
+``forward`` and ``backward`` are conveniences that allocate the outputs with torch and call the
+entry points.
+
+Tensor layout: q, o, dO, dq: [B, Hq, T, D]; k, v, dk, dv: [B, Hkv, T, D]; lse: [B, Hq, T]
+float32; all contiguous on one GPU; float32, or bfloat16 through the ``_ex`` entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "NeAttnError", "library_path", "load", "lib",
+    "ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
+    "ne_attn_bwd_workspace_bytes", "ne_attn_strerror",
+    "forward", "backward",
+    "NE_OK", "NE_ERR_NULL", "NE_ERR_SHAPE", "NE_ERR_UNSUPPORTED", "NE_ERR_ALIGN", "NE_ERR_HIP",
+    "NE_F32", "NE_BF16", "EXPORTED_SYMBOLS",
+]
+
+NE_OK, NE_ERR_NULL, NE_ERR_SHAPE, NE_ERR_UNSUPPORTED, NE_ERR_ALIGN, NE_ERR_HIP = range(6)
+NE_F32, NE_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
+                    "ne_attn_bwd_workspace_bytes", "ne_attn_strerror")
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class NeAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status}: {ne_attn_strerror(status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libne_attn.so")
+
+
+def load():
+    """Loads the built library; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m causal_gqa_flashattention_attn_amd._build`")
+    L = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.ne_attn_fwd.argtypes = [vp] * 5 + [i] * 6 + [vp]
+    L.ne_attn_bwd.argtypes = [vp] * 10 + [i] * 6 + [vp]
+    L.ne_attn_fwd_ex.argtypes = [vp] * 5 + [i] * 7 + [f, vp]
+    L.ne_attn_bwd_ex.argtypes = [vp] * 10 + [i] * 7 + [f, vp]
+    for name in ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex"):
+        getattr(L, name).restype = i
+    L.ne_attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    L.ne_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.ne_attn_strerror.argtypes = [i]
+    L.ne_attn_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def lib():
+    return load()
+
+
+def ne_attn_strerror(status: int) -> str:
+    return load().ne_attn_strerror(int(status)).decode()
+
+
+def ne_attn_bwd_workspace_bytes(B: int, Hq: int, T: int) -> int:
+    return int(load().ne_attn_bwd_workspace_bytes(int(B), int(Hq), int(T)))
+
+
+# ----------------------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return NE_F32
+    if t.dtype == torch.bfloat16:
+        return NE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dims(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, D]")
+    B, Hq, T, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or tuple(k.shape[2:]) != (T, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return B, Hq, k.shape[1], T, D
+
+
+def _check_tensors(ts, dev):
+    for name, t in ts.items():
+        if not t.is_cuda or t.device != dev:
+            raise ValueError(f"{name} must be on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream, dev):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _raise(rc, where):
+    if rc != NE_OK:
+        raise NeAttnError(rc, where)
+
+
+def ne_attn_fwd_ex(q, k, v, o, lse, causal: bool = True, rope_base: float = 0.0, stream=None):
+    torch = _torch()
+    B, Hq, Hkv, T, D = _dims(q, k, v)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have dtype {q.dtype}")
+    if o.shape != q.shape or tuple(lse.shape) != (B, Hq, T) or lse.dtype != torch.float32:
+        raise ValueError("o must match q; lse must be float32 [B, Hq, T]")
+    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse), q.device)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_fwd_ex(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, T, D,
+                                   int(bool(causal)), dt, float(rope_base),
+                                   _stream(stream, q.device))
+    _raise(rc, "ne_attn_fwd_ex")
+
+
+def ne_attn_fwd(q, k, v, o, lse, causal: bool = True, stream=None):
+    torch = _torch()
+    B, Hq, Hkv, T, D = _dims(q, k, v)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if o.shape != q.shape or tuple(lse.shape) != (B, Hq, T):
+        raise ValueError("o must match q; lse must be [B, Hq, T]")
+    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse), q.device)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, T, D,
+                                int(bool(causal)), _stream(stream, q.device))
+    _raise(rc, "ne_attn_fwd")
+
+
+def _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, delta_ws):
+    torch = _torch()
+    B, Hq, Hkv, T, D = _dims(q, k, v)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have dtype {q.dtype}")
+    if o.shape != q.shape or dO.shape != q.shape or dq.shape != q.shape:
+        raise ValueError("o, dO, dq must match q")
+    if dk.shape != k.shape or dv.shape != k.shape:
+        raise ValueError("dk, dv must match k")
+    if tuple(lse.shape) != (B, Hq, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, T]")
+    if delta_ws.dtype != torch.float32 or delta_ws.numel() * 4 < ne_attn_bwd_workspace_bytes(B, Hq, T):
+        raise ValueError("delta_ws must be float32 with at least B*Hq*T elements")
+    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv,
+                        delta_ws=delta_ws), q.device)
+    return B, Hq, Hkv, T, D
+
+
+def ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal: bool = True,
+                   rope_base: float = 0.0, stream=None):
+    torch = _torch()
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, delta_ws)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_bwd_ex(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq), _p(dk),
+                                   _p(dv), _p(delta_ws), B, Hq, Hkv, T, D, int(bool(causal)),
+                                   _dtype_code(q), float(rope_base), _stream(stream, q.device))
+    _raise(rc, "ne_attn_bwd_ex")
+
+
+def ne_attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal: bool = True, stream=None):
+    torch = _torch()
+    if q.dtype != torch.float32:
+        raise TypeError("ne_attn_bwd takes float32 tensors")
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, delta_ws)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_bwd(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq), _p(dk),
+                                _p(dv), _p(delta_ws), B, Hq, Hkv, T, D, int(bool(causal)),
+                                _stream(stream, q.device))
+    _raise(rc, "ne_attn_bwd")
+
+
+# ----------------------------------------------------------------------------- conveniences
+
+def forward(q, k, v, causal: bool = True, rope_base: float = 0.0, stream=None):
+    """Allocates o and lse and runs the forward pass; returns (o, lse)."""
+    torch = _torch()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ne_attn_fwd_ex(q, k, v, o, lse, causal=causal, rope_base=rope_base, stream=stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0, stream=None):
+    """Allocates dq, dk, dv and the delta workspace and runs the backward pass."""
+    torch = _torch()
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, delta, causal=causal, rope_base=rope_base,
+                   stream=stream)
+    return dq, dk, dv

@@ -1,0 +1,622 @@
+// attn_f32.hip -- float32 causal grouped-query FlashAttention for gfx950, forward and backward.
+//
+// The method (NanoEuler's training kernel): exact softmax attention evaluated tile by tile with
+// an online softmax, never storing the T x T score matrix ("nanoeuler: un LLM estilo GPT-2
+// construido desde cero en C y CUDA", second paragraph; "NanoEuler -- Show HN" Japanese README
+// translation, section "Kernels and acceleration"); causal tiles above the diagonal are skipped
+// rather than masked ("NanoEuler: a GPT-2 hand-built in pure C/CUDA" (openai-hub),
+// implementation details, item "causal mask in attention"); query heads share key/value heads
+// (README translations, section "Architecture").
+//
+// All contractions run on the fp32 matrix cores (v_mfma_f32_32x32x2f32).  Every wave owns 32
+// query rows (forward, dQ) or 32 key rows (dK/dV) as the columns of its 32x32 tiles, so softmax
+// statistics are per-lane scalars and probability tiles feed the next MFMA from registers.
+//
+// Kernels:
+//   fwd_f32   one work-group per (batch, kv head, query tile); its waves are the group's query
+//             heads, so every K/V tile staged in LDS serves all of them.  Per wave:
+//             S^T = K Q^T, online softmax (in base 2, scale folded into Q), O^T += V^T P^T.
+//   dq_f32    same decomposition; first computes delta_i = dO_i . o_i for its rows (written to
+//             the workspace for the dK/dV pass), then per tile S^T, P^T = exp2(S^T - lse2),
+//             dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
+//   dkdv_f32  one work-group per (batch, kv head, 32-key block); K and V stay in registers, the
+//             group's query heads are split over the waves, each streaming its own query
+//             blocks through LDS: S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
+//             The waves' partial sums are added in LDS in a fixed order: no atomics anywhere,
+//             so results are reproducible bit for bit.
+#include <math.h>
+
+#include "attn_device.hpp"
+#include "attn_kernels.hpp"
+
+namespace ne {
+
+namespace {
+
+template <int D>
+struct Cfg {
+    static constexpr int LD = D + 4;      // LDS row stride in floats: consecutive rows start 16 B
+                                          // apart modulo 128 B, so 8 lanes reading 16 B from 8
+                                          // rows hit disjoint banks
+    static constexpr int NS = D / 2;      // MFMA k-steps of a contraction over D
+    static constexpr int ND = D / 32;     // 32-wide column blocks of D
+    static constexpr int C4 = D / 4;      // float4 per row
+    static constexpr int RPC = 64 / C4;   // rows per wave-wide float4 chunk
+    static constexpr int CH = 32 / RPC;   // chunks per 32-row tile
+    static constexpr int MAXC = (CH + 1) / 2;  // chunks per wave (query-tile WGs have >= 2 waves)
+};
+
+struct RopeArgs {
+    int on;
+    double log2_base;  // log2(rope_base)
+};
+
+// Rotation of the two adjacent pairs (c, c+1), (c+2, c+3) of a row at position t by
+// t * base^(-2i/D), i = pair index; `inv` applies the transpose.  The angle is reduced modulo
+// one turn in double precision, so the float32 sine and cosine are accurate at any position.
+template <int D>
+__device__ __forceinline__ f32x4 rope4(f32x4 x, int t, int c, const RopeArgs &r, bool inv) {
+    f32x4 y;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int i = c / 2 + p;
+        const double turns = (double)t * exp2(-(2.0 * i / D) * r.log2_base) * 0.15915494309189535;
+        const float frac = (float)(turns - rint(turns));
+        float sn, cs;
+        sincospif(2.0f * frac, &sn, &cs);
+        const float a = x[2 * p], b = x[2 * p + 1];
+        if (!inv) {
+            y[2 * p] = a * cs - b * sn;
+            y[2 * p + 1] = a * sn + b * cs;
+        } else {
+            y[2 * p] = a * cs + b * sn;
+            y[2 * p + 1] = b * cs - a * sn;
+        }
+    }
+    return y;
+}
+
+struct Args {
+    const float *q, *k, *v, *o, *lse, *dO;
+    float *out_o, *out_lse, *dq, *dk, *dv, *delta;
+    int B, Hq, Hkv, T, G;
+    int hpw, rb, nqt;  // query-tile kernels
+    int kw;            // waves of a dK/dV work-group
+    float qscale;      // scale * log2(e)
+    float scale;       // 1 / sqrt(D)
+    RopeArgs rope;
+};
+
+struct QTile {
+    int b, g, h, qt, r0;  // r0: first query row of this wave
+};
+
+// Longest work first: causal query tiles are issued from the last (most key tiles) down.
+__device__ __forceinline__ QTile decode_qtile(const Args &a, bool causal, int wave) {
+    const int nhc = a.G / a.hpw;
+    const int per = a.B * a.Hkv * nhc;
+    const int t = blockIdx.x / per;
+    int r = blockIdx.x % per;
+    QTile c;
+    c.qt = causal ? a.nqt - 1 - t : t;
+    const int hc = r % nhc;
+    r /= nhc;
+    c.g = r % a.Hkv;
+    c.b = r / a.Hkv;
+    c.h = c.g * a.G + hc * a.hpw + wave / a.rb;
+    c.r0 = c.qt * 32 * a.rb + (wave % a.rb) * 32;
+    return c;
+}
+
+// K and V tiles of 32 rows, staged global -> registers -> LDS (padded rows), double buffered.
+template <int D, bool ROPE>
+struct KVStager {
+    using C = Cfg<D>;
+    f32x4 k[C::MAXC], v[C::MAXC];
+
+    __device__ __forceinline__ void load(const float *kg, const float *vg, int tile, int T,
+                                         int wave, int nw, int lane, const RopeArgs &rp) {
+        const int c4 = 4 * (lane % C::C4);
+#pragma unroll
+        for (int i = 0; i < C::MAXC; ++i) {
+            const int c = wave + i * nw;
+            if (c < C::CH) {
+                const int row = tile * 32 + c * C::RPC + lane / C::C4;
+                if (row < T) {
+                    k[i] = ld4(kg + (size_t)row * D + c4);
+                    v[i] = ld4(vg + (size_t)row * D + c4);
+                    if (ROPE) k[i] = rope4<D>(k[i], row, c4, rp, false);
+                } else {
+                    k[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    v[i] = k[i];
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float *sK, float *sV, int wave, int nw, int lane) {
+        const int c4 = 4 * (lane % C::C4);
+#pragma unroll
+        for (int i = 0; i < C::MAXC; ++i) {
+            const int c = wave + i * nw;
+            if (c < C::CH) {
+                const int r = c * C::RPC + lane / C::C4;
+                st4(sK + r * C::LD + c4, k[i]);
+                st4(sV + r * C::LD + c4, v[i]);
+            }
+        }
+    }
+};
+
+// This lane's query row, columns NS*half .. NS*half+NS-1, scaled; rotated first with RoPE.
+template <int D, bool ROPE>
+__device__ __forceinline__ void load_row_half(float (&dst)[Cfg<D>::NS], const float *base, int row,
+                                             int T, int half, float mul, const RopeArgs &rp) {
+    using C = Cfg<D>;
+    const float *src = base + (size_t)min(row, T - 1) * D + C::NS * half;
+#pragma unroll
+    for (int c = 0; c < C::NS / 4; ++c) {
+        f32x4 t = ld4(src + 4 * c);
+        if (ROPE) t = rope4<D>(t, row, C::NS * half + 4 * c, rp, false);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[4 * c + i] = t[i] * mul;
+    }
+}
+
+// S^T tile (32 keys x 32 queries) = K_tile (LDS, padded rows) x this wave's query rows (regs).
+template <int D>
+__device__ __forceinline__ f32x16 scores_t(const float *K, const float (&x)[Cfg<D>::NS], int col,
+                                           int half) {
+    using C = Cfg<D>;
+    f32x16 s = zero16();
+#pragma unroll
+    for (int st = 0; st < C::NS; st += 4) {
+        const f32x4 kk = ld4(K + col * C::LD + C::NS * half + st);
+        s = mfma32(kk[0], x[st + 0], s);
+        s = mfma32(kk[1], x[st + 1], s);
+        s = mfma32(kk[2], x[st + 2], s);
+        s = mfma32(kk[3], x[st + 3], s);
+    }
+    return s;
+}
+
+// acc (D x 32 queries, transposed) += M_tile^T (D x 32 keys) * X (32 keys x 32 queries), with
+// X the accumulator-layout tile in registers and M_tile the LDS tile [key][d].
+template <int D>
+__device__ __forceinline__ void accum_t(f32x16 (&acc)[Cfg<D>::ND], const float *M, const f32x16 &x,
+                                        int col, int half) {
+    using C = Cfg<D>;
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+        const int key = acc_row(st, half);
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd) acc[dd] = mfma32(M[key * C::LD + dd * 32 + col], x[st], acc[dd]);
+    }
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(512) fwd_f32(Args a) {
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(16))) float sK[2][32 * C::LD];
+    __shared__ __attribute__((aligned(16))) float sV[2][32 * C::LD];
+    const int nw = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const QTile c = decode_qtile(a, CAUSAL, wave);
+    const int T = a.T;
+    const int qrow = c.r0 + col;
+    const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
+    const float *kg = a.k + bg * T * D;
+    const float *vg = a.v + bg * T * D;
+
+    float qr[C::NS];
+    load_row_half<D, ROPE>(qr, a.q + bh * T * D, qrow, T, half, a.qscale, a.rope);
+
+    f32x16 acc[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
+    float m = kNegBig, l = 0.f;
+
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
+
+    KVStager<D, ROPE> stg;
+    stg.load(kg, vg, 0, T, wave, nw, lane, a.rope);
+    stg.store(sK[0], sV[0], wave, nw, lane);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        const bool more = j + 1 < ntiles;
+        if (more) stg.load(kg, vg, j + 1, T, wave, nw, lane, a.rope);
+        const int k0 = j * 32;
+        if (c.r0 < T && (!CAUSAL || k0 <= c.r0 + 31)) {
+            f32x16 s = scores_t<D>(sK[buf], qr, col, half);
+            if ((CAUSAL && k0 + 31 > c.r0) || k0 + 32 > T) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = k0 + acc_row(v, half);
+                    if ((CAUSAL && key > qrow) || key >= T) s[v] = -INFINITY;
+                }
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+            mx = fmaxf(mx, swap_halves(mx));
+            const float mnew = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            float ps = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s[v] = fast_exp2(s[v] - mnew);
+                ps += s[v];
+            }
+            l = l * alpha + ps;
+#pragma unroll
+            for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
+            accum_t<D>(acc, sV[buf], s, col, half);
+        }
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], wave, nw, lane);
+        __syncthreads();
+    }
+
+    l += swap_halves(l);
+    if (qrow < T) {
+        const float inv = 1.0f / l;
+        float *orow = a.out_o + (bh * T + qrow) * D;
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                st4(orow + dd * 32 + 8 * u + 4 * half,
+                    f32x4{acc[dd][4 * u] * inv, acc[dd][4 * u + 1] * inv, acc[dd][4 * u + 2] * inv,
+                          acc[dd][4 * u + 3] * inv});
+        if (half == 0) a.out_lse[bh * T + qrow] = m * kLn2 + logf(l);
+    }
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(512) dq_f32(Args a) {
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(16))) float sK[2][32 * C::LD];
+    __shared__ __attribute__((aligned(16))) float sV[2][32 * C::LD];
+    const int nw = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const QTile c = decode_qtile(a, CAUSAL, wave);
+    const int T = a.T;
+    const int qrow = c.r0 + col;
+    const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
+    const float *kg = a.k + bg * T * D;
+    const float *vg = a.v + bg * T * D;
+
+    float qr[C::NS], dor[C::NS];
+    load_row_half<D, ROPE>(qr, a.q + bh * T * D, qrow, T, half, a.qscale, a.rope);
+    load_row_half<D, false>(dor, a.dO + bh * T * D, qrow, T, half, 1.0f, a.rope);
+
+    // delta_i = sum_d dO_id o_id over this row; written once per row for the dK/dV pass.
+    float delta;
+    {
+        float orow[C::NS];
+        load_row_half<D, false>(orow, a.o + bh * T * D, qrow, T, half, 1.0f, a.rope);
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < C::NS; ++i) part += dor[i] * orow[i];
+        delta = part + swap_halves(part);
+    }
+    float lse2;
+    if (qrow < T) {
+        lse2 = a.lse[bh * T + qrow] * kLog2e;
+        if (half == 0) a.delta[bh * T + qrow] = delta;
+    } else {
+        lse2 = INFINITY;  // padding row: P = 0
+        delta = 0.f;
+    }
+
+    f32x16 acc[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
+
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
+
+    KVStager<D, ROPE> stg;
+    stg.load(kg, vg, 0, T, wave, nw, lane, a.rope);
+    stg.store(sK[0], sV[0], wave, nw, lane);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        const bool more = j + 1 < ntiles;
+        if (more) stg.load(kg, vg, j + 1, T, wave, nw, lane, a.rope);
+        const int k0 = j * 32;
+        if (c.r0 < T && (!CAUSAL || k0 <= c.r0 + 31)) {
+            f32x16 p = scores_t<D>(sK[buf], qr, col, half);
+            const bool edge = (CAUSAL && k0 + 31 > c.r0) || k0 + 32 > T;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = k0 + acc_row(v, half);
+                const bool masked = edge && ((CAUSAL && key > qrow) || key >= T);
+                p[v] = masked ? 0.f : fast_exp2(p[v] - lse2);
+            }
+            f32x16 ds = scores_t<D>(sV[buf], dor, col, half);  // dP^T = V dO^T
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
+            accum_t<D>(acc, sK[buf], ds, col, half);  // dQ^T += K^T dS^T
+        }
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], wave, nw, lane);
+        __syncthreads();
+    }
+
+    if (qrow < T) {
+        float *drow = a.dq + (bh * T + qrow) * D;
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int d = dd * 32 + 8 * u + 4 * half;
+                f32x4 x{acc[dd][4 * u] * a.scale, acc[dd][4 * u + 1] * a.scale,
+                        acc[dd][4 * u + 2] * a.scale, acc[dd][4 * u + 3] * a.scale};
+                if (ROPE) x = rope4<D>(x, qrow, d, a.rope, true);
+                st4(drow + d, x);
+            }
+    }
+}
+
+// Floats of LDS per dK/dV wave: a query tile and a dO tile (32 padded rows each), lse2, delta.
+template <int D>
+constexpr int dkdv_wave_floats() { return 2 * 32 * Cfg<D>::LD + 64; }
+
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(256) dkdv_f32(Args a) {
+    using C = Cfg<D>;
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int nw = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const int T = a.T;
+    const int per = a.B * a.Hkv;
+    const int kb = blockIdx.x / per;  // ascending: the first key blocks see the most queries
+    const int g = (blockIdx.x % per) % a.Hkv;
+    const int b = (blockIdx.x % per) / a.Hkv;
+    const size_t bg = (size_t)b * a.Hkv + g;
+    const int krow = kb * 32 + col;
+
+    float kr[C::NS], vr[C::NS];
+    load_row_half<D, ROPE>(kr, a.k + bg * T * D, krow, T, half, a.qscale, a.rope);
+    load_row_half<D, false>(vr, a.v + bg * T * D, krow, T, half, 1.0f, a.rope);
+
+    f32x16 dk[C::ND], dv[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) {
+        dk[dd] = zero16();
+        dv[dd] = zero16();
+    }
+
+    float *sQ = smem + wave * dkdv_wave_floats<D>();
+    float *sO = sQ + 32 * C::LD;  // dO tile
+    float *sL = sO + 32 * C::LD;  // lse * log2(e) of the tile's rows
+    float *sDl = sL + 32;         // delta of the tile's rows
+    const int nqb = (T + 31) / 32;
+    const int i0 = CAUSAL ? kb : 0;
+    const int c4 = 4 * (lane % C::C4);
+
+    for (int hh = wave; hh < a.G; hh += nw) {
+        const size_t bh = (size_t)b * a.Hq + (size_t)g * a.G + hh;
+        const float *qh = a.q + bh * T * D;
+        const float *doh = a.dO + bh * T * D;
+        for (int i = i0; i < nqb; ++i) {
+            // Stage this wave's query block; only this wave reads it, so ordering within the
+            // wave is all that is needed.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+            for (int ch = 0; ch < C::CH; ++ch) {
+                const int r = ch * C::RPC + lane / C::C4;
+                const int row = i * 32 + r;
+                f32x4 tq{0.f, 0.f, 0.f, 0.f}, td{0.f, 0.f, 0.f, 0.f};
+                if (row < T) {
+                    tq = ld4(qh + (size_t)row * D + c4);
+                    td = ld4(doh + (size_t)row * D + c4);
+                    if (ROPE) tq = rope4<D>(tq, row, c4, a.rope, false);
+                }
+                st4(sQ + r * C::LD + c4, tq);
+                st4(sO + r * C::LD + c4, td);
+            }
+            if (lane < 32) {
+                const int row = i * 32 + lane;
+                sL[lane] = row < T ? a.lse[bh * T + row] * kLog2e : INFINITY;
+                sDl[lane] = row < T ? a.delta[bh * T + row] : 0.f;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+
+            // S = Q K'^T (rows: queries acc_row(v, half), column: this lane's key)
+            f32x16 p = zero16();
+#pragma unroll
+            for (int st = 0; st < C::NS; st += 4) {
+                const f32x4 qq = ld4(sQ + col * C::LD + C::NS * half + st);
+                p = mfma32(qq[0], kr[st + 0], p);
+                p = mfma32(qq[1], kr[st + 1], p);
+                p = mfma32(qq[2], kr[st + 2], p);
+                p = mfma32(qq[3], kr[st + 3], p);
+            }
+            f32x16 ds = zero16();
+#pragma unroll
+            for (int st = 0; st < C::NS; st += 4) {
+                const f32x4 oo = ld4(sO + col * C::LD + C::NS * half + st);
+                ds = mfma32(oo[0], vr[st + 0], ds);
+                ds = mfma32(oo[1], vr[st + 1], ds);
+                ds = mfma32(oo[2], vr[st + 2], ds);
+                ds = mfma32(oo[3], vr[st + 3], ds);
+            }
+            const bool diag = CAUSAL && i == kb;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const f32x4 L = ld4(sL + 8 * u + 4 * half);
+                const f32x4 Dl = ld4(sDl + 8 * u + 4 * half);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * u + e;
+                    const int qrow = i * 32 + acc_row(v, half);
+                    const bool masked = diag && krow > qrow;
+                    const float pv = masked ? 0.f : fast_exp2(p[v] - L[e]);
+                    p[v] = pv;
+                    ds[v] = pv * (ds[v] - Dl[e]);
+                }
+            }
+            // dV^T += dO^T P ; dK^T += Q^T dS
+#pragma unroll
+            for (int st = 0; st < 16; ++st) {
+                const int r = acc_row(st, half);
+#pragma unroll
+                for (int dd = 0; dd < C::ND; ++dd) {
+                    dv[dd] = mfma32(sO[r * C::LD + dd * 32 + col], p[st], dv[dd]);
+                    dk[dd] = mfma32(sQ[r * C::LD + dd * 32 + col], ds[st], dk[dd]);
+                }
+            }
+        }
+    }
+
+    // Add the waves' partial dK, dV in LDS (wave order fixed) and write them out.
+    __syncthreads();
+    {
+        float *R = smem + wave * dkdv_wave_floats<D>();
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int d = dd * 32 + 8 * u + 4 * half;
+                st4(R + col * C::LD + d,
+                    f32x4{dk[dd][4 * u] * a.scale, dk[dd][4 * u + 1] * a.scale,
+                          dk[dd][4 * u + 2] * a.scale, dk[dd][4 * u + 3] * a.scale});
+                st4(R + 32 * C::LD + col * C::LD + d,
+                    f32x4{dv[dd][4 * u], dv[dd][4 * u + 1], dv[dd][4 * u + 2], dv[dd][4 * u + 3]});
+            }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 2 * 32 * C::C4; idx += blockDim.x) {
+        const int t = idx / (32 * C::C4);
+        const int r = (idx / C::C4) % 32;
+        const int cc = 4 * (idx % C::C4);
+        f32x4 sum{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < nw; ++w) sum += ld4(smem + w * dkdv_wave_floats<D>() + t * 32 * C::LD + r * C::LD + cc);
+        const int row = kb * 32 + r;
+        if (row < T) {
+            if (t == 0) {
+                if (ROPE) sum = rope4<D>(sum, row, cc, a.rope, true);
+                st4(a.dk + (bg * T + row) * D + cc, sum);
+            } else {
+                st4(a.dv + (bg * T + row) * D + cc, sum);
+            }
+        }
+    }
+}
+
+Args make_args(const Shape &s) {
+    Args a{};
+    a.B = s.B;
+    a.Hq = s.Hq;
+    a.Hkv = s.Hkv;
+    a.T = s.T;
+    a.G = s.G;
+    a.scale = (float)(1.0 / sqrt((double)s.D));
+    a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));
+    a.rope.on = s.rope_base > 0.f;
+    a.rope.log2_base = a.rope.on ? log2((double)s.rope_base) : 0.0;
+    return a;
+}
+
+#define NE_PICK(KERNEL)                                                                      \
+    template <int D>                                                                         \
+    const void *pick_##KERNEL(bool causal, bool rope) {                                      \
+        if (causal) return rope ? (const void *)KERNEL<D, true, true> : (const void *)KERNEL<D, true, false>; \
+        return rope ? (const void *)KERNEL<D, false, true> : (const void *)KERNEL<D, false, false>; \
+    }
+NE_PICK(fwd_f32)
+NE_PICK(dq_f32)
+NE_PICK(dkdv_f32)
+#undef NE_PICK
+
+hipError_t launch(const void *fn, long long blocks, int threads, size_t lds, hipStream_t st, Args &a) {
+    void *params[] = {&a};
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), params, lds, st);
+}
+
+}  // namespace
+
+QTileGeom qtile_geometry(const Shape &s) {
+    QTileGeom g{};
+    g.hpw = 1;
+    for (int d = 8; d >= 1; --d)
+        if (s.G % d == 0) {
+            g.hpw = d;
+            break;
+        }
+    g.rb = g.hpw == 1 ? 2 : 1;
+    g.nwaves = g.hpw * g.rb;
+    g.rows = 32 * g.rb;
+    g.nqt = (s.T + g.rows - 1) / g.rows;
+    g.nblocks = (long long)s.B * s.Hkv * (s.G / g.hpw) * g.nqt;
+    return g;
+}
+
+KBlockGeom kblock_geometry(const Shape &s) {
+    KBlockGeom g{};
+    g.nwaves = 1;
+    for (int d = 4; d >= 1; --d)
+        if (s.G % d == 0) {
+            g.nwaves = d;
+            break;
+        }
+    g.nkb = (s.T + 31) / 32;
+    g.nblocks = (long long)s.B * s.Hkv * g.nkb;
+    return g;
+}
+
+hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const float *v, float *o,
+                          float *lse, hipStream_t st) {
+    Args a = make_args(s);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out_o = o;
+    a.out_lse = lse;
+    const QTileGeom g = qtile_geometry(s);
+    a.hpw = g.hpw;
+    a.rb = g.rb;
+    a.nqt = g.nqt;
+    const bool causal = s.causal != 0, rope = a.rope.on != 0;
+    const void *fn = s.D == 64 ? pick_fwd_f32<64>(causal, rope) : pick_fwd_f32<32>(causal, rope);
+    return launch(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
+}
+
+hipError_t launch_bwd_f32(const Shape &s, const float *q, const float *k, const float *v,
+                          const float *o, const float *lse, const float *dO, float *dq, float *dk,
+                          float *dv, float *delta, hipStream_t st) {
+    Args a = make_args(s);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.dO = dO;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = delta;
+    const QTileGeom gq = qtile_geometry(s);
+    a.hpw = gq.hpw;
+    a.rb = gq.rb;
+    a.nqt = gq.nqt;
+    const bool causal = s.causal != 0, rope = a.rope.on != 0;
+    const void *fq = s.D == 64 ? pick_dq_f32<64>(causal, rope) : pick_dq_f32<32>(causal, rope);
+    hipError_t e = launch(fq, gq.nblocks, 64 * gq.nwaves, 0, st, a);
+    if (e != hipSuccess) return e;
+    const KBlockGeom gk = kblock_geometry(s);
+    a.kw = gk.nwaves;
+    const size_t lds = (size_t)gk.nwaves * (s.D == 64 ? dkdv_wave_floats<64>() : dkdv_wave_floats<32>()) * sizeof(float);
+    const void *fk = s.D == 64 ? pick_dkdv_f32<64>(causal, rope) : pick_dkdv_f32<32>(causal, rope);
+    return launch(fk, gk.nblocks, 64 * gk.nwaves, lds, st, a);
+}
+
+}  // namespace ne

@@ -1,0 +1,42 @@
+// attn_kernels.hpp -- launch descriptions shared by the host entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ne {
+
+// One problem instance.  Element offsets are computed in 64-bit inside the kernels.
+struct Shape {
+    int B, Hq, Hkv, T, D, G;  // G = Hq / Hkv
+    int causal;
+    float rope_base;          // 0: no RoPE
+};
+
+// Work-group composition of the query-tile kernels (forward and dQ): each work-group serves
+// `hpw` query heads of one key/value head and `rb` 32-row blocks per head, i.e. hpw * rb waves,
+// all sharing each K/V tile staged in LDS.
+struct QTileGeom {
+    int hpw, rb, nwaves, rows;  // rows = 32 * rb query rows per head
+    int nqt;                    // query tiles per head
+    long long nblocks;
+};
+
+QTileGeom qtile_geometry(const Shape &s);
+
+// Key-block kernel (dK/dV): one work-group per (b, kv head, 32-key block), `nwaves` waves that
+// split the group's query heads between them and reduce their partial sums in LDS.
+struct KBlockGeom {
+    int nwaves, nkb;
+    long long nblocks;
+};
+
+KBlockGeom kblock_geometry(const Shape &s);
+
+hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const float *v,
+                          float *o, float *lse, hipStream_t st);
+hipError_t launch_bwd_f32(const Shape &s, const float *q, const float *k, const float *v,
+                          const float *o, const float *lse, const float *dO, float *dq,
+                          float *dk, float *dv, float *delta, hipStream_t st);
+
+}  // namespace ne

@@ -1,0 +1,121 @@
+// ne_attn_api.hip -- the C ABI declared in include/ne_attn.h: argument checks, then dispatch to
+// the gfx950 kernels on the caller's stream.  Nothing here allocates, synchronises or keeps
+// state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/ne_attn.h"
+#include "attn_kernels.hpp"
+
+namespace {
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Checks shared by every entry point; fills `s` on success.
+int check_shape(int B, int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                ne::Shape &s) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1) return NE_ERR_SHAPE;
+    if (Hq % Hkv != 0) return NE_ERR_SHAPE;
+    if (D != 32 && D != 64) return NE_ERR_UNSUPPORTED;
+    if (dtype != NE_F32 && dtype != NE_BF16) return NE_ERR_UNSUPPORTED;
+    if (!(rope_base >= 0.f) || !isfinite(rope_base)) return NE_ERR_UNSUPPORTED;
+    // Element counts and grid sizes must stay far from 64-bit and 31-bit limits.
+    const double rows = (double)B * (double)Hq * (double)T;
+    if (rows * D > 9.0e15 || T > (1 << 24)) return NE_ERR_SHAPE;
+    s.B = B;
+    s.Hq = Hq;
+    s.Hkv = Hkv;
+    s.T = T;
+    s.D = D;
+    s.G = Hq / Hkv;
+    s.causal = causal != 0;
+    s.rope_base = rope_base;
+    const ne::QTileGeom gq = ne::qtile_geometry(s);
+    const ne::KBlockGeom gk = ne::kblock_geometry(s);
+    if (gq.nblocks > 0x7fffffffLL || gk.nblocks > 0x7fffffffLL) return NE_ERR_SHAPE;
+    return NE_OK;
+}
+
+int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
+             int Hkv, int T, int D, int causal, int dtype, float rope_base, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+        return NE_ERR_ALIGN;
+    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
+    const hipError_t e = ne::launch_fwd_f32(s, static_cast<const float *>(q),
+                                            static_cast<const float *>(k),
+                                            static_cast<const float *>(v), static_cast<float *>(o),
+                                            lse, stream);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+int bwd_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dO, void *dq, void *dk, void *dv, float *delta_ws, int B, int Hq,
+             int Hkv, int T, int D, int causal, int dtype, float rope_base, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !delta_ws) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
+    if (rc != NE_OK) return rc;
+    const void *ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv, delta_ws};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return NE_ERR_ALIGN;
+    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
+    const hipError_t e = ne::launch_bwd_f32(
+        s, static_cast<const float *>(q), static_cast<const float *>(k),
+        static_cast<const float *>(v), static_cast<const float *>(o), lse,
+        static_cast<const float *>(dO), static_cast<float *>(dq), static_cast<float *>(dk),
+        static_cast<float *>(dv), delta_ws, stream);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ne_attn_fwd(const float *q, const float *k, const float *v, float *o, float *lse, int B,
+                int Hq, int Hkv, int T, int D, int causal, hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, T, D, causal, NE_F32, 0.f, stream);
+}
+
+int ne_attn_bwd(const float *q, const float *k, const float *v, const float *o, const float *lse,
+                const float *dO, float *dq, float *dk, float *dv, float *delta_ws, int B, int Hq,
+                int Hkv, int T, int D, int causal, hipStream_t stream) {
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, B, Hq, Hkv, T, D, causal, NE_F32,
+                    0.f, stream);
+}
+
+int ne_attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                   int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                   hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, T, D, causal, dtype, rope_base, stream);
+}
+
+int ne_attn_bwd_ex(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dO, void *dq, void *dk, void *dv, float *delta_ws, int B, int Hq,
+                   int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                   hipStream_t stream) {
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, B, Hq, Hkv, T, D, causal, dtype,
+                    rope_base, stream);
+}
+
+size_t ne_attn_bwd_workspace_bytes(int B, int Hq, int T) {
+    if (B < 1 || Hq < 1 || T < 1) return 0;
+    return (size_t)4 * (size_t)B * (size_t)Hq * (size_t)T;
+}
+
+const char *ne_attn_strerror(int status) {
+    switch (status) {
+        case NE_OK: return "success";
+        case NE_ERR_NULL: return "null pointer argument";
+        case NE_ERR_SHAPE: return "invalid shape (B, Hq, Hkv, T must be >= 1, Hq a multiple of Hkv, sizes in range)";
+        case NE_ERR_UNSUPPORTED: return "unsupported configuration (D must be 32 or 64, dtype NE_F32 or NE_BF16, rope_base finite and >= 0)";
+        case NE_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case NE_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

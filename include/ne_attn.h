@@ -1,0 +1,115 @@
+/*
+ * ne_attn.h -- C ABI of the causal grouped-query FlashAttention library for MI355X (gfx950).
+ *
+ * What the operation is.  Exact softmax attention of queries against keys and values, computed
+ * tile by tile with an online softmax so that the T x T score matrix is never stored, forward
+ * and backward, as NanoEuler's hand-written training kernel does ("nanoeuler: un LLM estilo
+ * GPT-2 construido desde cero en C y CUDA", second paragraph; "NanoEuler -- Show HN" Japanese
+ * README translation, section "Kernels and acceleration").  Queries see only keys at their own
+ * and earlier positions when causal, and the upper triangle is skipped, not masked after the
+ * fact ("NanoEuler: a GPT-2 hand-built in pure C/CUDA" (openai-hub), implementation details,
+ * item "causal mask in attention").  Query heads share a smaller set of key/value heads
+ * (grouped-query attention) and RoPE is applied to queries and keys (README translations,
+ * section "Architecture").
+ *
+ *   s_ij   = (R_i q_i) . (R_j k_j) / sqrt(D)        (R = identity without RoPE)
+ *   P_ij   = exp(s_ij - lse_i) over keys j <= i (causal) or all j,  lse_i = log sum_j exp(s_ij)
+ *   o_i    = sum_j P_ij v_j
+ *   backward: gradients of sum(dO * o) with respect to the caller's q, k, v.
+ *
+ * Layout (all tensors contiguous, row-major, no strides):
+ *   q, o, dO, dq : [B][Hq][T][D]        k, v, dk, dv : [B][Hkv][T][D]
+ *   lse, delta   : [B][Hq][T]  float32 (natural-log log-sum-exp of the scaled scores)
+ *   Query head h reads key/value head h / (Hq / Hkv).  scale = 1 / sqrt(D).
+ *   RoPE (rope_base > 0): the pair (x[2i], x[2i+1]) of the row at position t (0..T-1) is rotated
+ *   by the angle t * rope_base^(-2i/D).
+ *
+ * Ownership and memory.  Every pointer is a device pointer owned by the caller; the library
+ * allocates and frees nothing, keeps no state and is thread-safe.  Outputs (o, lse, dq, dk, dv,
+ * delta) are fully overwritten; inputs are never written.  Inputs and outputs must not alias.
+ * Pointers must be 16-byte aligned.
+ *
+ * Streams.  Work is enqueued on `stream` (NULL = the null stream) and the call returns without
+ * synchronising.  A fault during execution surfaces at the caller's next synchronisation.
+ *
+ * Errors.  Every entry point returns an ne_status.  Argument errors are detected before any
+ * launch and nothing is enqueued: NE_ERR_NULL (a null pointer), NE_ERR_SHAPE (B, Hq, Hkv or T
+ * below 1, Hq not a multiple of Hkv, sizes whose element count overflows), NE_ERR_UNSUPPORTED
+ * (D not 32 or 64, unknown dtype, negative or non-finite rope_base), NE_ERR_ALIGN (a pointer
+ * not 16-byte aligned).  NE_ERR_HIP reports a failed kernel launch.  No C++ exception crosses
+ * this interface.
+ */
+#ifndef NE_ATTN_H
+#define NE_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's own stream handle. */
+typedef struct ihipStream_t *hipStream_t;
+
+enum ne_status {
+    NE_OK = 0,
+    NE_ERR_NULL = 1,
+    NE_ERR_SHAPE = 2,
+    NE_ERR_UNSUPPORTED = 3,
+    NE_ERR_ALIGN = 4,
+    NE_ERR_HIP = 5
+};
+
+enum ne_dtype {
+    NE_F32 = 0,  /* float32 tensors, float32 arithmetic (fp32 MFMA) */
+    NE_BF16 = 1  /* bfloat16 q, k, v, o, dO, dq, dk, dv; float32 lse/delta; fp32 accumulate */
+};
+
+/*
+ * Forward, float32, no RoPE.  Writes o [B][Hq][T][D] and lse [B][Hq][T].
+ * causal != 0 restricts query i to keys j <= i.
+ */
+int ne_attn_fwd(const float *q, const float *k, const float *v, float *o, float *lse,
+                int B, int Hq, int Hkv, int T, int D, int causal, hipStream_t stream);
+
+/*
+ * Backward, float32, no RoPE.  Takes the o and lse written by ne_attn_fwd for the same inputs
+ * and causal flag, and the incoming gradient dO.  Writes dq, dk, dv, and uses delta_ws as a
+ * caller-owned workspace of ne_attn_bwd_workspace_bytes(B, Hq, T) bytes, into which it writes
+ * delta_i = sum_d dO_id * o_id, float32 [B][Hq][T].  No atomics: results are bitwise
+ * reproducible run to run.
+ */
+int ne_attn_bwd(const float *q, const float *k, const float *v, const float *o,
+                const float *lse, const float *dO, float *dq, float *dk, float *dv,
+                float *delta_ws, int B, int Hq, int Hkv, int T, int D, int causal,
+                hipStream_t stream);
+
+/*
+ * Forward with a dtype (NE_F32 or NE_BF16) and an optional fused RoPE prologue on q and k
+ * (rope_base > 0; 0 disables it).  Tensors are float* for NE_F32 and bfloat16 (uint16 bit
+ * patterns) for NE_BF16; lse is float32 in both.
+ */
+int ne_attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int Hq, int Hkv, int T, int D, int causal, int dtype,
+                   float rope_base, hipStream_t stream);
+
+/*
+ * Backward with a dtype and the same RoPE setting as the forward call.  With RoPE, dq and dk
+ * are gradients with respect to the un-rotated q and k the caller passed.
+ */
+int ne_attn_bwd_ex(const void *q, const void *k, const void *v, const void *o,
+                   const float *lse, const void *dO, void *dq, void *dk, void *dv,
+                   float *delta_ws, int B, int Hq, int Hkv, int T, int D, int causal,
+                   int dtype, float rope_base, hipStream_t stream);
+
+/* Bytes of the backward workspace: 4 * B * Hq * T (0 if an argument is below 1). */
+size_t ne_attn_bwd_workspace_bytes(int B, int Hq, int T);
+
+/* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
+const char *ne_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NE_ATTN_H */
