@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Throughput of causal grouped-query FlashAttention, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpu_model]
+                    [--no-cpu-baseline] [--graph]
+
+One step is one pass of the whole path over one batch of synthetic inputs already resident in
+HBM: the forward kernel (o, lse), then the two backward passes (dq + delta, then dk, dv), i.e.
+exactly what ne_attn_fwd_ex followed by ne_attn_bwd_ex enqueue.  The K timed steps are
+bracketed by device synchronisations; `value` is algorithmic TFLOP/s (causal FLOPs counted as
+half of dense; forward 2 GEMMs, backward 5) over the wall-clock time per step.
+
+Per-kernel durations come from HIP events recorded on the stream the kernels are launched on,
+around every launch of the timed steps.  The `roofline` object describes the kernel with the
+largest average duration; `cpu_baseline` times the fp64 oracle on the host cores on a bounded
+sample of the same workload.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd+bwd TFLOP/s & % MFMA peak, B16 Hq12/Hkv4 T512 D64 causal"
+# MI355X dense matrix-core peaks (256 CUs, 2.4 GHz), TFLOP/s.
+MFMA_PEAK = {"f32": 157.3, "bf16": 2516.6}
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="gpu_model")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum host time spent on the oracle sample")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="run one plain device-to-device copy of this many MiB before the steps "
+                        "(reference dispatch of known size for HBM counter calibration)")
+    p.add_argument("--graph", action="store_true",
+                   help="replay the step from a captured HIP graph instead of eager launches")
+    return p.parse_args()
+
+
+def kernel_flops(w):
+    """Algorithmic FLOPs of each kernel launch: forward = QK^T + PV; the dK/dV pass holds four
+    of the backward's five GEMMs (S, dP, dV, dK); the dQ pass holds dQ = dS K (its recomputed
+    S and dP are not algorithmic work)."""
+    f = w.flops_fwd()
+    return {"fwd": f, "bwd_dq": 0.5 * f, "bwd_dkdv": 2.0 * f}
+
+
+def kernel_bytes(w):
+    """Algorithmic HBM bytes of each launch (inputs read once, outputs written once)."""
+    elt = 2 if w.dtype == "bf16" else 4
+    nq = w.B * w.Hq * w.T * w.D
+    nk = w.B * w.Hkv * w.T * w.D
+    nl = w.B * w.Hq * w.T
+    return {"fwd": elt * (2 * nq + 2 * nk) + 4 * nl,                 # q,k,v -> o, lse
+            "bwd_dq": elt * (4 * nq + 2 * nk) + 4 * 2 * nl,          # q,k,v,o,dO,lse -> dq, delta
+            "bwd_dkdv": elt * (2 * nq + 4 * nk) + 4 * 2 * nl}        # q,k,v,dO,lse,delta -> dk,dv
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "causal_gqa_flashattention_attn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current
+    kernel sources; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("source_digest") != source_digest():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, min_seconds: float):
+    """The fp64 oracle, as it stands, on batch elements 0, 1, 2, ... of the same inputs (one
+    oracle forward + backward call per element, cycling) until `min_seconds` have passed."""
+    import oracle
+    per_b = {n: x[n].reshape((w.B, 1) + x[n].shape[1:]) for n in ("q", "k", "v", "dO")}
+    one = w.with_(B=1)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        b = done % w.B
+        q, k, v, dO = (per_b[n][b] for n in ("q", "k", "v", "dO"))
+        oracle.attn_fwd(q, k, v, causal=w.causal, rope_base=w.rope_base)
+        oracle.attn_bwd(q, k, v, dO, causal=w.causal, rope_base=w.rope_base)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or done >= 64 * w.B:
+            break
+    return {"value": one.flops_fwd_bwd() * done / el / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} single-batch-element fwd+bwd calls of {w.name} "
+                      f"(B=1 Hq{w.Hq} Hkv{w.Hkv} T{w.T} D{w.D}), {el:.1f} s, fp64"}
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: this attention path has no multi-GPU mode "
+                  "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import causal_gqa_flashattention_attn_amd as ne
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[a.workload]
+    x = make_inputs(w, a.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, dO = (torch.from_numpy(x[n]).to(dev).to(dt).contiguous() for n in ("q", "k", "v", "dO"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev)
+    c, rb = w.causal, w.rope_base
+    names = ("fwd", "bwd_dq", "bwd_dkdv")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ne.ne_attn_fwd_ex(q, k, v, o, lse, causal=c, rope_base=rb)
+        if ev is not None:
+            ev[1].record()
+        ne.ne_attn_bwd_dq_ex(q, k, v, o, lse, dO, dq, delta, causal=c, rope_base=rb)
+        if ev is not None:
+            ev[2].record()
+        ne.ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, delta, dk, dv, causal=c, rope_base=rb)
+        if ev is not None:
+            ev[3].record()
+
+    if a.copy_mib > 0:
+        src = torch.ones(a.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    graph = None
+    if a.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+
+    for _ in range(a.warmup):
+        graph.replay() if graph is not None else step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        if graph is not None:
+            events[i][0].record()
+            graph.replay()
+            events[i][3].record()
+        else:
+            step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / a.steps
+    tflops = w.flops_fwd_bwd() / (ms_per_step * 1e-3) / 1e12
+    fl = kernel_flops(w)
+    by = kernel_bytes(w)
+    kern = {}
+    if graph is None:
+        for j, n in enumerate(names):
+            ms = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events]))
+            kern[n] = {"avg_ms": ms, "tflops": fl[n] / (ms * 1e-3) / 1e12,
+                       "gbs": by[n] / (ms * 1e-3) / 1e9}
+        dom = max(kern, key=lambda n: kern[n]["avg_ms"])
+        ach = kern[dom]["tflops"]
+        traffic = measured_traffic(dom, w.name)
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 3),
+                "peak": MFMA_PEAK[w.dtype], "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK[w.dtype], 4), "traffic": traffic,
+                "algorithmic_flops_per_launch": fl[dom],
+                "algorithmic_bytes_per_launch": by[dom]}
+    else:
+        roof = None
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D,
+                   "causal": w.causal, "rope_base": w.rope_base, "seed": a.seed,
+                   "launch": "hip_graph" if graph is not None else "eager"},
+        "pct_mfma_peak": round(100 * tflops / MFMA_PEAK[w.dtype], 2),
+        "kernels": {n: {kk: round(vv, 4) for kk, vv in d.items()} for n, d in kern.items()},
+        "roofline": roof,
+        "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline(w, x, a.cpu_seconds),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,6 +20,7 @@ import os
 __all__ = [
     "NeAttnError", "library_path", "load", "lib",
     "ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
+    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex",
     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror",
     "forward", "backward",
     "NE_OK", "NE_ERR_NULL", "NE_ERR_SHAPE", "NE_ERR_UNSUPPORTED", "NE_ERR_ALIGN", "NE_ERR_HIP",
@@ -30,6 +31,7 @@ NE_OK, NE_ERR_NULL, NE_ERR_SHAPE, NE_ERR_UNSUPPORTED, NE_ERR_ALIGN, NE_ERR_HIP =
 NE_F32, NE_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
+                    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex",
                     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -61,7 +63,10 @@ def load():
     L.ne_attn_bwd.argtypes = [vp] * 10 + [i] * 6 + [vp]
     L.ne_attn_fwd_ex.argtypes = [vp] * 5 + [i] * 7 + [f, vp]
     L.ne_attn_bwd_ex.argtypes = [vp] * 10 + [i] * 7 + [f, vp]
-    for name in ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex"):
+    L.ne_attn_bwd_dq_ex.argtypes = [vp] * 8 + [i] * 7 + [f, vp]
+    L.ne_attn_bwd_dkdv_ex.argtypes = [vp] * 8 + [i] * 7 + [f, vp]
+    for name in ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
+                 "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex"):
         getattr(L, name).restype = i
     L.ne_attn_bwd_workspace_bytes.argtypes = [i, i, i]
     L.ne_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -207,6 +212,31 @@ def ne_attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal: bool = True, 
                                 _p(dv), _p(delta_ws), B, Hq, Hkv, T, D, int(bool(causal)),
                                 _stream(stream, q.device))
     _raise(rc, "ne_attn_bwd")
+
+
+def ne_attn_bwd_dq_ex(q, k, v, o, lse, dO, dq, delta_ws, causal: bool = True,
+                      rope_base: float = 0.0, stream=None):
+    """First backward pass: writes dq and delta_ws."""
+    torch = _torch()
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, k, v, delta_ws)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_bwd_dq_ex(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
+                                      _p(delta_ws), B, Hq, Hkv, T, D, int(bool(causal)),
+                                      _dtype_code(q), float(rope_base), _stream(stream, q.device))
+    _raise(rc, "ne_attn_bwd_dq_ex")
+
+
+def ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, delta_ws, dk, dv, causal: bool = True,
+                        rope_base: float = 0.0, stream=None):
+    """Second backward pass: reads delta_ws (from the dq pass), writes dk and dv."""
+    torch = _torch()
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, dO, lse, dO, dO, dk, dv, delta_ws)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_bwd_dkdv_ex(_p(q), _p(k), _p(v), _p(lse), _p(dO), _p(delta_ws),
+                                        _p(dk), _p(dv), B, Hq, Hkv, T, D, int(bool(causal)),
+                                        _dtype_code(q), float(rope_base),
+                                        _stream(stream, q.device))
+    _raise(rc, "ne_attn_bwd_dkdv_ex")
 
 
 # ----------------------------------------------------------------------------- conveniences

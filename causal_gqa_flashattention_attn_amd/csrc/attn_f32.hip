@@ -590,9 +590,9 @@ hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const 
     return launch(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
 }
 
-hipError_t launch_bwd_f32(const Shape &s, const float *q, const float *k, const float *v,
-                          const float *o, const float *lse, const float *dO, float *dq, float *dk,
-                          float *dv, float *delta, hipStream_t st) {
+hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const float *v,
+                         const float *o, const float *lse, const float *dO, float *dq,
+                         float *delta, hipStream_t st) {
     Args a = make_args(s);
     a.q = q;
     a.k = k;
@@ -601,22 +601,35 @@ hipError_t launch_bwd_f32(const Shape &s, const float *q, const float *k, const 
     a.lse = lse;
     a.dO = dO;
     a.dq = dq;
+    a.delta = delta;
+    const QTileGeom g = qtile_geometry(s);
+    a.hpw = g.hpw;
+    a.rb = g.rb;
+    a.nqt = g.nqt;
+    const bool causal = s.causal != 0, rope = a.rope.on != 0;
+    const void *fn = s.D == 64 ? pick_dq_f32<64>(causal, rope) : pick_dq_f32<32>(causal, rope);
+    return launch(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
+}
+
+hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const float *v,
+                           const float *lse, const float *dO, const float *delta, float *dk,
+                           float *dv, hipStream_t st) {
+    Args a = make_args(s);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.lse = lse;
+    a.dO = dO;
     a.dk = dk;
     a.dv = dv;
-    a.delta = delta;
-    const QTileGeom gq = qtile_geometry(s);
-    a.hpw = gq.hpw;
-    a.rb = gq.rb;
-    a.nqt = gq.nqt;
+    a.delta = const_cast<float *>(delta);  // read only in this pass
+    const KBlockGeom g = kblock_geometry(s);
+    a.kw = g.nwaves;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
-    const void *fq = s.D == 64 ? pick_dq_f32<64>(causal, rope) : pick_dq_f32<32>(causal, rope);
-    hipError_t e = launch(fq, gq.nblocks, 64 * gq.nwaves, 0, st, a);
-    if (e != hipSuccess) return e;
-    const KBlockGeom gk = kblock_geometry(s);
-    a.kw = gk.nwaves;
-    const size_t lds = (size_t)gk.nwaves * (s.D == 64 ? dkdv_wave_floats<64>() : dkdv_wave_floats<32>()) * sizeof(float);
-    const void *fk = s.D == 64 ? pick_dkdv_f32<64>(causal, rope) : pick_dkdv_f32<32>(causal, rope);
-    return launch(fk, gk.nblocks, 64 * gk.nwaves, lds, st, a);
+    const size_t lds = (size_t)g.nwaves *
+                       (s.D == 64 ? dkdv_wave_floats<64>() : dkdv_wave_floats<32>()) * sizeof(float);
+    const void *fn = s.D == 64 ? pick_dkdv_f32<64>(causal, rope) : pick_dkdv_f32<32>(causal, rope);
+    return launch(fn, g.nblocks, 64 * g.nwaves, lds, st, a);
 }
 
 }  // namespace ne

@@ -35,8 +35,13 @@ KBlockGeom kblock_geometry(const Shape &s);
 
 hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const float *v,
                           float *o, float *lse, hipStream_t st);
-hipError_t launch_bwd_f32(const Shape &s, const float *q, const float *k, const float *v,
-                          const float *o, const float *lse, const float *dO, float *dq,
-                          float *dk, float *dv, float *delta, hipStream_t st);
+// dQ pass: writes dq and delta (= rowsum(dO * o)).
+hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const float *v,
+                         const float *o, const float *lse, const float *dO, float *dq,
+                         float *delta, hipStream_t st);
+// dK/dV pass: reads delta written by the dQ pass.
+hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const float *v,
+                           const float *lse, const float *dO, const float *delta, float *dk,
+                           float *dv, hipStream_t st);
 
 }  // namespace ne

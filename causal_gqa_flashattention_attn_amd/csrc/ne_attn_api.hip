@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/ne_attn.h"
 #include "attn_kernels.hpp"
 
@@ -52,23 +54,58 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
+bool any_misaligned(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (misaligned(p)) return true;
+    return false;
+}
+
+int dq_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
+            const void *dO, void *dq, float *delta_ws, int B, int Hq, int Hkv, int T, int D,
+            int causal, int dtype, float rope_base, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !delta_ws) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (any_misaligned({q, k, v, o, lse, dO, dq, delta_ws})) return NE_ERR_ALIGN;
+    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
+    const hipError_t e = ne::launch_dq_f32(
+        s, static_cast<const float *>(q), static_cast<const float *>(k),
+        static_cast<const float *>(v), static_cast<const float *>(o), lse,
+        static_cast<const float *>(dO), static_cast<float *>(dq), delta_ws, stream);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+int dkdv_impl(const void *q, const void *k, const void *v, const float *lse, const void *dO,
+              const float *delta_ws, void *dk, void *dv, int B, int Hq, int Hkv, int T, int D,
+              int causal, int dtype, float rope_base, hipStream_t stream) {
+    if (!q || !k || !v || !lse || !dO || !delta_ws || !dk || !dv) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (any_misaligned({q, k, v, lse, dO, delta_ws, dk, dv})) return NE_ERR_ALIGN;
+    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
+    const hipError_t e = ne::launch_dkdv_f32(
+        s, static_cast<const float *>(q), static_cast<const float *>(k),
+        static_cast<const float *>(v), lse, static_cast<const float *>(dO), delta_ws,
+        static_cast<float *>(dk), static_cast<float *>(dv), stream);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
 int bwd_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
              const void *dO, void *dq, void *dk, void *dv, float *delta_ws, int B, int Hq,
              int Hkv, int T, int D, int causal, int dtype, float rope_base, hipStream_t stream) {
+    // Check everything (including dk, dv) before the first pass is enqueued.
     if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !delta_ws) return NE_ERR_NULL;
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
-    const void *ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv, delta_ws};
-    for (const void *p : ptrs)
-        if (misaligned(p)) return NE_ERR_ALIGN;
-    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
-    const hipError_t e = ne::launch_bwd_f32(
-        s, static_cast<const float *>(q), static_cast<const float *>(k),
-        static_cast<const float *>(v), static_cast<const float *>(o), lse,
-        static_cast<const float *>(dO), static_cast<float *>(dq), static_cast<float *>(dk),
-        static_cast<float *>(dv), delta_ws, stream);
-    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+    if (any_misaligned({q, k, v, o, lse, dO, dq, dk, dv, delta_ws})) return NE_ERR_ALIGN;
+    const int r1 = dq_impl(q, k, v, o, lse, dO, dq, delta_ws, B, Hq, Hkv, T, D, causal, dtype,
+                           rope_base, stream);
+    if (r1 != NE_OK) return r1;
+    return dkdv_impl(q, k, v, lse, dO, delta_ws, dk, dv, B, Hq, Hkv, T, D, causal, dtype,
+                     rope_base, stream);
 }
 
 }  // namespace
@@ -99,6 +136,22 @@ int ne_attn_bwd_ex(const void *q, const void *k, const void *v, const void *o, c
                    hipStream_t stream) {
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, B, Hq, Hkv, T, D, causal, dtype,
                     rope_base, stream);
+}
+
+int ne_attn_bwd_dq_ex(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dO, void *dq, float *delta_ws, int B, int Hq,
+                      int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                      hipStream_t stream) {
+    return dq_impl(q, k, v, o, lse, dO, dq, delta_ws, B, Hq, Hkv, T, D, causal, dtype, rope_base,
+                   stream);
+}
+
+int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float *lse,
+                        const void *dO, const float *delta_ws, void *dk, void *dv, int B, int Hq,
+                        int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                        hipStream_t stream) {
+    return dkdv_impl(q, k, v, lse, dO, delta_ws, dk, dv, B, Hq, Hkv, T, D, causal, dtype,
+                     rope_base, stream);
 }
 
 size_t ne_attn_bwd_workspace_bytes(int B, int Hq, int T) {

@@ -102,6 +102,22 @@ int ne_attn_bwd_ex(const void *q, const void *k, const void *v, const void *o,
                    float *delta_ws, int B, int Hq, int Hkv, int T, int D, int causal,
                    int dtype, float rope_base, hipStream_t stream);
 
+/*
+ * The two passes that ne_attn_bwd_ex runs back to back, as separate calls for callers that
+ * schedule them themselves or need only dq.  ne_attn_bwd_dq_ex writes dq and delta_ws
+ * (delta_i = sum_d dO_id o_id); ne_attn_bwd_dkdv_ex reads delta_ws and writes dk, dv, and must
+ * be ordered after the dq pass that filled delta_ws (same stream, or an event).  Arguments
+ * mean what they mean for ne_attn_bwd_ex.
+ */
+int ne_attn_bwd_dq_ex(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dO, void *dq, float *delta_ws, int B,
+                      int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                      hipStream_t stream);
+int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float *lse,
+                        const void *dO, const float *delta_ws, void *dk, void *dv, int B,
+                        int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                        hipStream_t stream);
+
 /* Bytes of the backward workspace: 4 * B * Hq * T (0 if an argument is below 1). */
 size_t ne_attn_bwd_workspace_bytes(int B, int Hq, int T);
 

@@ -97,6 +97,37 @@ def test_unsupported(ne, kw):
     assert bwd(ne, **kw) == ne.NE_ERR_UNSUPPORTED
 
 
+def dq_pass(ne, ptrs=None, **kw):
+    L = ne.load()
+    p = ptrs or [A] * 8
+    a = dict(B=1, Hq=4, Hkv=2, T=64, D=32, causal=1, dtype=0, rope=0.0)
+    a.update(kw)
+    return L.ne_attn_bwd_dq_ex(*[VP(x) for x in p], a["B"], a["Hq"], a["Hkv"], a["T"], a["D"],
+                               a["causal"], a["dtype"], a["rope"], VP(0))
+
+
+def dkdv_pass(ne, ptrs=None, **kw):
+    L = ne.load()
+    p = ptrs or [A] * 8
+    a = dict(B=1, Hq=4, Hkv=2, T=64, D=32, causal=1, dtype=0, rope=0.0)
+    a.update(kw)
+    return L.ne_attn_bwd_dkdv_ex(*[VP(x) for x in p], a["B"], a["Hq"], a["Hkv"], a["T"],
+                                 a["D"], a["causal"], a["dtype"], a["rope"], VP(0))
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_backward_passes_validate(ne, which):
+    p = [A] * 8
+    p[which] = 0
+    assert dq_pass(ne, p) == ne.NE_ERR_NULL
+    assert dkdv_pass(ne, p) == ne.NE_ERR_NULL
+    p[which] = A + 8
+    assert dq_pass(ne, p) == ne.NE_ERR_ALIGN
+    assert dkdv_pass(ne, p) == ne.NE_ERR_ALIGN
+    assert dq_pass(ne, Hkv=3) == ne.NE_ERR_SHAPE
+    assert dkdv_pass(ne, D=128) == ne.NE_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("which", range(10))
 def test_misaligned(ne, which):
     p = [A] * 10
