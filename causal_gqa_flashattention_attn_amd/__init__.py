@@ -57,6 +57,10 @@ def load():
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           "`python -m causal_gqa_flashattention_attn_amd._build`")
+    # torch ships its own HIP runtime with the same soname (libamdhip64.so.7).  Loading torch
+    # first makes the library bind to that runtime; loading the library first would bring in a
+    # second HIP runtime, whose launches cannot use torch's memory and streams.
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.ne_attn_fwd.argtypes = [vp] * 5 + [i] * 6 + [vp]

@@ -29,6 +29,17 @@
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
 
+// Minimum resident waves per SIMD each kernel is compiled for (caps its registers).
+#ifndef NE_FWD_WAVES_PER_EU
+#define NE_FWD_WAVES_PER_EU 2
+#endif
+#ifndef NE_DQ_WAVES_PER_EU
+#define NE_DQ_WAVES_PER_EU 2
+#endif
+#ifndef NE_DKDV_WAVES_PER_EU
+#define NE_DKDV_WAVES_PER_EU 2
+#endif
+
 namespace ne {
 
 namespace {
@@ -109,6 +120,8 @@ __device__ __forceinline__ QTile decode_qtile(const Args &a, bool causal, int wa
 }
 
 // K and V tiles of 32 rows, staged global -> registers -> LDS (padded rows), double buffered.
+// Rows past the end are loaded from the last row (so every load is unconditional and can stay in
+// flight while the current tile is computed) and replaced by zeros when written to LDS.
 template <int D, bool ROPE>
 struct KVStager {
     using C = Cfg<D>;
@@ -121,27 +134,26 @@ struct KVStager {
         for (int i = 0; i < C::MAXC; ++i) {
             const int c = wave + i * nw;
             if (c < C::CH) {
-                const int row = tile * 32 + c * C::RPC + lane / C::C4;
-                if (row < T) {
-                    k[i] = ld4(kg + (size_t)row * D + c4);
-                    v[i] = ld4(vg + (size_t)row * D + c4);
-                    if (ROPE) k[i] = rope4<D>(k[i], row, c4, rp, false);
-                } else {
-                    k[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    v[i] = k[i];
-                }
+                const int row = min(tile * 32 + c * C::RPC + lane / C::C4, T - 1);
+                k[i] = ld4(kg + (size_t)row * D + c4);
+                v[i] = ld4(vg + (size_t)row * D + c4);
             }
         }
     }
-    __device__ __forceinline__ void store(float *sK, float *sV, int wave, int nw, int lane) {
+    __device__ __forceinline__ void store(float *sK, float *sV, int tile, int T, int wave, int nw,
+                                          int lane, const RopeArgs &rp) {
         const int c4 = 4 * (lane % C::C4);
+        const f32x4 zero{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < C::MAXC; ++i) {
             const int c = wave + i * nw;
             if (c < C::CH) {
                 const int r = c * C::RPC + lane / C::C4;
-                st4(sK + r * C::LD + c4, k[i]);
-                st4(sV + r * C::LD + c4, v[i]);
+                const int row = tile * 32 + r;
+                f32x4 kk = k[i];
+                if (ROPE) kk = rope4<D>(kk, row, c4, rp, false);
+                st4(sK + r * C::LD + c4, row < T ? kk : zero);
+                st4(sV + r * C::LD + c4, row < T ? v[i] : zero);
             }
         }
     }
@@ -194,7 +206,8 @@ __device__ __forceinline__ void accum_t(f32x16 (&acc)[Cfg<D>::ND], const float *
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(512) fwd_f32(Args a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_FWD_WAVES_PER_EU)))
+fwd_f32(Args a) {
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(16))) float sK[2][32 * C::LD];
     __shared__ __attribute__((aligned(16))) float sV[2][32 * C::LD];
@@ -222,7 +235,7 @@ __global__ void __launch_bounds__(512) fwd_f32(Args a) {
 
     KVStager<D, ROPE> stg;
     stg.load(kg, vg, 0, T, wave, nw, lane, a.rope);
-    stg.store(sK[0], sV[0], wave, nw, lane);
+    stg.store(sK[0], sV[0], 0, T, wave, nw, lane, a.rope);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
@@ -256,7 +269,7 @@ __global__ void __launch_bounds__(512) fwd_f32(Args a) {
             for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
             accum_t<D>(acc, sV[buf], s, col, half);
         }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], wave, nw, lane);
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw, lane, a.rope);
         __syncthreads();
     }
 
@@ -276,7 +289,8 @@ __global__ void __launch_bounds__(512) fwd_f32(Args a) {
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(512) dq_f32(Args a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_DQ_WAVES_PER_EU)))
+dq_f32(Args a) {
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(16))) float sK[2][32 * C::LD];
     __shared__ __attribute__((aligned(16))) float sV[2][32 * C::LD];
@@ -323,7 +337,7 @@ __global__ void __launch_bounds__(512) dq_f32(Args a) {
 
     KVStager<D, ROPE> stg;
     stg.load(kg, vg, 0, T, wave, nw, lane, a.rope);
-    stg.store(sK[0], sV[0], wave, nw, lane);
+    stg.store(sK[0], sV[0], 0, T, wave, nw, lane, a.rope);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
@@ -344,7 +358,7 @@ __global__ void __launch_bounds__(512) dq_f32(Args a) {
             for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
             accum_t<D>(acc, sK[buf], ds, col, half);  // dQ^T += K^T dS^T
         }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], wave, nw, lane);
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw, lane, a.rope);
         __syncthreads();
     }
 
@@ -368,7 +382,8 @@ template <int D>
 constexpr int dkdv_wave_floats() { return 2 * 32 * Cfg<D>::LD + 64; }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(256) dkdv_f32(Args a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_DKDV_WAVES_PER_EU)))
+dkdv_f32(Args a) {
     using C = Cfg<D>;
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int nw = blockDim.x >> 6;
@@ -401,79 +416,103 @@ __global__ void __launch_bounds__(256) dkdv_f32(Args a) {
     const int i0 = CAUSAL ? kb : 0;
     const int c4 = 4 * (lane % C::C4);
 
-    for (int hh = wave; hh < a.G; hh += nw) {
+    // The group's (query head, query block) items are dealt round-robin to the waves; each
+    // wave stages its own query block and keeps private dK, dV partial sums.
+    const int per_head = nqb - i0;
+    const int nitems = a.G * per_head;
+    for (int it = wave; it < nitems; it += nw) {
+        const int hh = it / per_head;
+        const int i = i0 + it % per_head;
         const size_t bh = (size_t)b * a.Hq + (size_t)g * a.G + hh;
         const float *qh = a.q + bh * T * D;
         const float *doh = a.dO + bh * T * D;
-        for (int i = i0; i < nqb; ++i) {
-            // Stage this wave's query block; only this wave reads it, so ordering within the
-            // wave is all that is needed.
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        // Only this wave reads its staging area, so ordering within the wave is all that is
+        // needed between the previous item's reads and these writes.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        {
+            f32x4 tq[C::CH], td[C::CH];
+#pragma unroll
+            for (int ch = 0; ch < C::CH; ++ch) {
+                const int row = min(i * 32 + ch * C::RPC + lane / C::C4, T - 1);
+                tq[ch] = ld4(qh + (size_t)row * D + c4);
+                td[ch] = ld4(doh + (size_t)row * D + c4);
+            }
+            float lsev = 0.f, dlv = 0.f;
+            const int lrow = i * 32 + (lane & 31);
+            if (lrow < T) {
+                lsev = a.lse[bh * T + lrow];
+                dlv = a.delta[bh * T + lrow];
+            }
+            const f32x4 zero{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ch = 0; ch < C::CH; ++ch) {
                 const int r = ch * C::RPC + lane / C::C4;
                 const int row = i * 32 + r;
-                f32x4 tq{0.f, 0.f, 0.f, 0.f}, td{0.f, 0.f, 0.f, 0.f};
-                if (row < T) {
-                    tq = ld4(qh + (size_t)row * D + c4);
-                    td = ld4(doh + (size_t)row * D + c4);
-                    if (ROPE) tq = rope4<D>(tq, row, c4, a.rope, false);
-                }
-                st4(sQ + r * C::LD + c4, tq);
-                st4(sO + r * C::LD + c4, td);
+                f32x4 q4 = tq[ch];
+                if (ROPE) q4 = rope4<D>(q4, row, c4, a.rope, false);
+                st4(sQ + r * C::LD + c4, row < T ? q4 : zero);
+                st4(sO + r * C::LD + c4, row < T ? td[ch] : zero);
             }
             if (lane < 32) {
-                const int row = i * 32 + lane;
-                sL[lane] = row < T ? a.lse[bh * T + row] * kLog2e : INFINITY;
-                sDl[lane] = row < T ? a.delta[bh * T + row] : 0.f;
+                sL[lane] = lrow < T ? lsev * kLog2e : INFINITY;  // padding rows get P = 0
+                sDl[lane] = dlv;
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 
-            // S = Q K'^T (rows: queries acc_row(v, half), column: this lane's key)
-            f32x16 p = zero16();
+        // S = Q K'^T (rows: queries acc_row(v, half) of the block; column: this lane's key)
+        f32x16 p = zero16();
 #pragma unroll
-            for (int st = 0; st < C::NS; st += 4) {
-                const f32x4 qq = ld4(sQ + col * C::LD + C::NS * half + st);
-                p = mfma32(qq[0], kr[st + 0], p);
-                p = mfma32(qq[1], kr[st + 1], p);
-                p = mfma32(qq[2], kr[st + 2], p);
-                p = mfma32(qq[3], kr[st + 3], p);
+        for (int st = 0; st < C::NS; st += 4) {
+            const f32x4 qq = ld4(sQ + col * C::LD + C::NS * half + st);
+            p = mfma32(qq[0], kr[st + 0], p);
+            p = mfma32(qq[1], kr[st + 1], p);
+            p = mfma32(qq[2], kr[st + 2], p);
+            p = mfma32(qq[3], kr[st + 3], p);
+        }
+        // P = exp2(S - lse2): independent of the dP chain below, so the two can overlap.
+        const bool diag = CAUSAL && i == kb;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 L = ld4(sL + 8 * u + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = 4 * u + e;
+                const bool masked = diag && krow > i * 32 + acc_row(v, half);
+                p[v] = masked ? 0.f : fast_exp2(p[v] - L[e]);
             }
-            f32x16 ds = zero16();
+        }
+        // dP = dO V^T
+        f32x16 ds = zero16();
 #pragma unroll
-            for (int st = 0; st < C::NS; st += 4) {
-                const f32x4 oo = ld4(sO + col * C::LD + C::NS * half + st);
-                ds = mfma32(oo[0], vr[st + 0], ds);
-                ds = mfma32(oo[1], vr[st + 1], ds);
-                ds = mfma32(oo[2], vr[st + 2], ds);
-                ds = mfma32(oo[3], vr[st + 3], ds);
-            }
-            const bool diag = CAUSAL && i == kb;
+        for (int st = 0; st < C::NS; st += 4) {
+            const f32x4 oo = ld4(sO + col * C::LD + C::NS * half + st);
+            ds = mfma32(oo[0], vr[st + 0], ds);
+            ds = mfma32(oo[1], vr[st + 1], ds);
+            ds = mfma32(oo[2], vr[st + 2], ds);
+            ds = mfma32(oo[3], vr[st + 3], ds);
+        }
+        // dV^T += dO^T P  (needs only P, so it can run while dS is formed)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const f32x4 L = ld4(sL + 8 * u + 4 * half);
-                const f32x4 Dl = ld4(sDl + 8 * u + 4 * half);
+        for (int st = 0; st < 16; ++st) {
+            const int r = acc_row(st, half);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int v = 4 * u + e;
-                    const int qrow = i * 32 + acc_row(v, half);
-                    const bool masked = diag && krow > qrow;
-                    const float pv = masked ? 0.f : fast_exp2(p[v] - L[e]);
-                    p[v] = pv;
-                    ds[v] = pv * (ds[v] - Dl[e]);
-                }
-            }
-            // dV^T += dO^T P ; dK^T += Q^T dS
+            for (int dd = 0; dd < C::ND; ++dd) dv[dd] = mfma32(sO[r * C::LD + dd * 32 + col], p[st], dv[dd]);
+        }
+        // dS = P (dP - delta)
 #pragma unroll
-            for (int st = 0; st < 16; ++st) {
-                const int r = acc_row(st, half);
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 Dl = ld4(sDl + 8 * u + 4 * half);
 #pragma unroll
-                for (int dd = 0; dd < C::ND; ++dd) {
-                    dv[dd] = mfma32(sO[r * C::LD + dd * 32 + col], p[st], dv[dd]);
-                    dk[dd] = mfma32(sQ[r * C::LD + dd * 32 + col], ds[st], dk[dd]);
-                }
-            }
+            for (int e = 0; e < 4; ++e) ds[4 * u + e] = p[4 * u + e] * (ds[4 * u + e] - Dl[e]);
+        }
+        // dK^T += Q^T dS
+#pragma unroll
+        for (int st = 0; st < 16; ++st) {
+            const int r = acc_row(st, half);
+#pragma unroll
+            for (int dd = 0; dd < C::ND; ++dd) dk[dd] = mfma32(sQ[r * C::LD + dd * 32 + col], ds[st], dk[dd]);
         }
     }
 
@@ -562,12 +601,7 @@ QTileGeom qtile_geometry(const Shape &s) {
 
 KBlockGeom kblock_geometry(const Shape &s) {
     KBlockGeom g{};
-    g.nwaves = 1;
-    for (int d = 4; d >= 1; --d)
-        if (s.G % d == 0) {
-            g.nwaves = d;
-            break;
-        }
+    g.nwaves = 4;
     g.nkb = (s.T + 31) / 32;
     g.nblocks = (long long)s.B * s.Hkv * g.nkb;
     return g;

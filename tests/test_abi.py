@@ -143,3 +143,15 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(m, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         m.load()
+
+
+def test_single_hip_runtime_in_process():
+    """The library must share the HIP runtime torch loaded, not bring a second one."""
+    import subprocess
+    import sys
+    code = ("import re, causal_gqa_flashattention_attn_amd as ne; ne.load(); import torch; "
+            "m = open('/proc/self/maps').read(); "
+            "print(len(set(re.findall(r'/\\S*libamdhip64\\S*', m))))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout.strip().splitlines()[-1]
+    assert out == "1"
