@@ -1,0 +1,691 @@
+// attn_bf16.hip -- bfloat16 causal grouped-query FlashAttention for gfx950 with an optional fused
+// RoPE prologue, forward and backward.  Inputs and outputs are bf16; lse and delta are fp32; all
+// accumulation is fp32 (v_mfma_f32_32x32x16_bf16).
+//
+// Same method and decomposition as the fp32 kernels (exact softmax attention, online softmax,
+// no T x T matrix: "nanoeuler: un LLM estilo GPT-2 construido desde cero en C y CUDA", second
+// paragraph; causal upper triangle skipped: "NanoEuler: a GPT-2 hand-built in pure C/CUDA"
+// (openai-hub), implementation details; grouped-query heads and RoPE on queries and keys:
+// README translations, section "Architecture").
+//
+// RoPE: the pair (x[2i], x[2i+1]) at position t is rotated by t * base^(-2i/D) in fp32 when q
+// and k are loaded; the rotated values are rounded to bf16 before they enter the matrix cores.
+// dq and dk are rotated back (transpose) in fp32 before rounding, so they are gradients with
+// respect to the caller's un-rotated q and k.
+//
+// Layout in LDS: K, V, Q and dO tiles stay row-major as in HBM (16-byte chunks XOR-swizzled per
+// row).  Products that contract over the tile's rows (P V, dS K, dO^T P, Q^T dS) read their
+// operand with the transposing LDS load, so no tile is ever transposed in memory.
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_device.hpp"
+#include "attn_kernels.hpp"
+
+#ifndef NE_BF16_FWD_WAVES_PER_EU
+#define NE_BF16_FWD_WAVES_PER_EU 2
+#endif
+#ifndef NE_BF16_DQ_WAVES_PER_EU
+#define NE_BF16_DQ_WAVES_PER_EU 2
+#endif
+#ifndef NE_BF16_DKDV_WAVES_PER_EU
+#define NE_BF16_DKDV_WAVES_PER_EU 2
+#endif
+
+namespace ne {
+
+namespace {
+
+template <int D>
+struct CfgB {
+    static constexpr int KS = D / 16;   // MFMA k-steps of a contraction over D
+    static constexpr int ND = D / 32;   // 32-wide blocks of D
+    static constexpr int NCH = D / 8;   // 16-byte chunks per row
+    static constexpr int RB = 2 * D;    // bytes per tile row
+    static constexpr int BN = 64;       // keys per staged K/V tile (two 32-key sub-blocks)
+};
+
+struct ArgsB {
+    const __bf16 *q, *k, *v, *o, *dO;
+    const float *lse;
+    __bf16 *out_o, *dq, *dk, *dv;
+    float *out_lse, *delta;
+    int B, Hq, Hkv, T, G;
+    int hpw, rb, nqt;
+    float qscale;   // scale * log2(e)
+    float scale;    // 1 / sqrt(D)
+    float rope_lb;  // log2(rope base)
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+
+// Turns per position of pair i: base^(-2i/D) / (2 pi).
+template <int D>
+__device__ __forceinline__ float rope_rate(int i, float lb) {
+    return exp2f(-(2.0f * (float)i / (float)D) * lb) * 0.15915494309189535f;
+}
+
+// Rotates the pairs (x[2p], x[2p+1]), p < N/2, of a row at position t; rates[p] is the turn
+// rate of pair p.  The fractional turn goes to the hardware sine/cosine (input in turns).
+template <int N>
+__device__ __forceinline__ void rope_rotate(float (&x)[N], int t, const float *rates, bool inv) {
+#pragma unroll
+    for (int p = 0; p < N / 2; ++p) {
+        const float fr = __builtin_amdgcn_fractf((float)t * rates[p]);
+        const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
+        const float a = x[2 * p], b = x[2 * p + 1];
+        if (!inv) {
+            x[2 * p] = a * cs - b * sn;
+            x[2 * p + 1] = a * sn + b * cs;
+        } else {
+            x[2 * p] = a * cs + b * sn;
+            x[2 * p + 1] = b * cs - a * sn;
+        }
+    }
+}
+
+__device__ __forceinline__ void unpack8(const bf16x8 &v, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = bf2f(v[i]);
+}
+__device__ __forceinline__ bf16x8 round8(const float (&x)[8]) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+    return r;
+}
+
+// 8 elements (row, c0 .. c0+7) from HBM, rotated when ROPE (rates of the 4 pairs given).
+template <int D, bool ROPE>
+__device__ __forceinline__ bf16x8 load_row8(const __bf16 *base, int row, int T, int c0,
+                                            const float *rates) {
+    const int r = min(row, T - 1);
+    bf16x8 v = *reinterpret_cast<const bf16x8 *>(base + (size_t)r * D + c0);
+    if (ROPE) {
+        float x[8];
+        unpack8(v, x);
+        rope_rotate<8>(x, row, rates, false);
+        v = round8(x);
+    }
+    return v;
+}
+
+// Stores four fp32 values (row, c0 .. c0+3) as bf16, optionally rotating them back first.
+template <int D, bool ROPE_INV>
+__device__ __forceinline__ void store_row4(__bf16 *base, int row, int c0, float (&x)[4],
+                                           float lb) {
+    if (ROPE_INV) {
+        const float rates[2] = {rope_rate<D>(c0 / 2, lb), rope_rate<D>(c0 / 2 + 1, lb)};
+        rope_rotate<4>(x, row, rates, true);
+    }
+    bf16x4 r{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+    *reinterpret_cast<bf16x4 *>(base + (size_t)row * D + c0) = r;
+}
+
+struct QTileB {
+    int b, g, h, qt, r0;
+};
+
+__device__ __forceinline__ QTileB decode_qtile_b(const ArgsB &a, bool causal, int wave) {
+    const int nhc = a.G / a.hpw;
+    const int per = a.B * a.Hkv * nhc;
+    const int t = blockIdx.x / per;
+    int r = blockIdx.x % per;
+    QTileB c;
+    c.qt = causal ? a.nqt - 1 - t : t;
+    const int hc = r % nhc;
+    r /= nhc;
+    c.g = r % a.Hkv;
+    c.b = r / a.Hkv;
+    c.h = c.g * a.G + hc * a.hpw + wave / a.rb;
+    c.r0 = c.qt * 32 * a.rb + (wave % a.rb) * 32;
+    return c;
+}
+
+// Staging of BN-row K and V tiles: HBM -> registers (issued one tile ahead) -> swizzled LDS.
+// The thread count is a multiple of D/8, so each thread always handles the same 16-byte column
+// chunk and its RoPE rates are computed once.
+template <int D, bool ROPE>
+struct KVStagerB {
+    using C = CfgB<D>;
+    static constexpr int CH = C::BN * C::NCH;
+    static constexpr int MAXC = (CH + 127) / 128;  // query-tile work-groups have >= 2 waves
+    bf16x8 k[MAXC], v[MAXC];
+    float rates[4];
+    int ch;
+
+    __device__ __forceinline__ void init(int tid, float lb) {
+        ch = tid % C::NCH;
+        if (ROPE)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) rates[p] = rope_rate<D>(4 * ch + p, lb);
+    }
+    __device__ __forceinline__ void load(const __bf16 *kg, const __bf16 *vg, int tile, int T,
+                                         int tid, int nt) {
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+            const int c = tid + i * nt;
+            if (c < CH) {
+                const int row = min(tile * C::BN + c / C::NCH, T - 1);
+                k[i] = *reinterpret_cast<const bf16x8 *>(kg + (size_t)row * D + 8 * ch);
+                v[i] = *reinterpret_cast<const bf16x8 *>(vg + (size_t)row * D + 8 * ch);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(unsigned char *sK, unsigned char *sV, int tile, int T,
+                                          int tid, int nt) {
+        const bf16x8 zero = {};
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+            const int c = tid + i * nt;
+            if (c < CH) {
+                const int r = c / C::NCH;
+                const int row = tile * C::BN + r;
+                bf16x8 kk = k[i];
+                if (ROPE) {
+                    float x[8];
+                    unpack8(kk, x);
+                    rope_rotate<8>(x, row, rates, false);
+                    kk = round8(x);
+                }
+                *reinterpret_cast<bf16x8 *>(sK + tile_off<D>(r, 8 * ch)) = row < T ? kk : zero;
+                *reinterpret_cast<bf16x8 *>(sV + tile_off<D>(r, 8 * ch)) = row < T ? v[i] : zero;
+            }
+        }
+    }
+};
+
+// This lane's query (or key) row as KS operand chunks: chunk s holds columns 16 s + 8 half ..+7.
+template <int D, bool ROPE>
+__device__ __forceinline__ void load_operand_row(bf16x8 (&dst)[CfgB<D>::KS], const __bf16 *base,
+                                                 int row, int T, int half, float lb) {
+#pragma unroll
+    for (int s = 0; s < CfgB<D>::KS; ++s) {
+        const int c0 = 16 * s + 8 * half;
+        float rates[4];
+        if (ROPE)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) rates[p] = rope_rate<D>(c0 / 2 + p, lb);
+        dst[s] = load_row8<D, ROPE>(base, row, T, c0, rates);
+    }
+}
+
+// S^T block (32 keys of the tile from row r0 x this wave's 32 rows) = M_tile x X^T.
+template <int D>
+__device__ __forceinline__ f32x16 block_scores(const unsigned char *tile, int r0,
+                                               const bf16x8 (&x)[CfgB<D>::KS], int col, int half) {
+    f32x16 s = zero16();
+#pragma unroll
+    for (int st = 0; st < CfgB<D>::KS; ++st)
+        s = mfma32_bf16(tile_read8<D>(tile, r0 + col, 16 * st + 8 * half), x[st], s);
+    return s;
+}
+
+// acc (D x 32, transposed) += M_tile[r0 .. r0+31]^T x X, X = the accumulator tile in registers.
+template <int D>
+__device__ __forceinline__ void block_accum(f32x16 (&acc)[CfgB<D>::ND], const unsigned char *tile,
+                                            int r0, const f32x16 &x, int lane) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 b = pack8(x, s2);
+#pragma unroll
+        for (int dd = 0; dd < CfgB<D>::ND; ++dd)
+            acc[dd] = mfma32_bf16(tile_read_tr8<D>(tile, r0 + 16 * s2, 32 * dd, lane), b, acc[dd]);
+    }
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_FWD_WAVES_PER_EU)))
+fwd_bf16(ArgsB a) {
+    using C = CfgB<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char sK[2][C::BN * C::RB];
+    __shared__ __attribute__((aligned(16))) unsigned char sV[2][C::BN * C::RB];
+    const int nt = blockDim.x, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const QTileB c = decode_qtile_b(a, CAUSAL, wave);
+    const int T = a.T;
+    const int qrow = c.r0 + col;
+    const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
+    const __bf16 *kg = a.k + bg * T * D;
+    const __bf16 *vg = a.v + bg * T * D;
+
+    bf16x8 qv[C::KS];
+    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
+
+    f32x16 acc[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
+    float m = kNegBig, l = 0.f;
+
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
+
+    KVStagerB<D, ROPE> stg;
+    stg.init(tid, a.rope_lb);
+    stg.load(kg, vg, 0, T, tid, nt);
+    stg.store(sK[0], sV[0], 0, T, tid, nt);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        const bool more = j + 1 < ntiles;
+        if (more) stg.load(kg, vg, j + 1, T, tid, nt);
+        f32x16 s[2];
+        bool act[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int kb0 = j * C::BN + 32 * sb;
+            act[sb] = c.r0 < T && kb0 < T && (!CAUSAL || kb0 <= c.r0 + 31);
+            if (act[sb]) s[sb] = block_scores<D>(sK[buf], 32 * sb, qv, col, half);
+        }
+        if (act[0] || act[1]) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                if (!act[sb]) continue;
+                const int kb0 = j * C::BN + 32 * sb;
+                if ((CAUSAL && kb0 + 31 > c.r0) || kb0 + 32 > T) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = kb0 + acc_row(v, half);
+                        if ((CAUSAL && key > qrow) || key >= T) s[sb][v] = -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sb][v]);
+            }
+            mx = fmaxf(mx, swap_halves(mx));
+            const float mnew = fmaxf(m, mx * a.qscale);
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            float ps = 0.f;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                if (!act[sb]) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    s[sb][v] = fast_exp2(fmaf(s[sb][v], a.qscale, -mnew));
+                    ps += s[sb][v];
+                }
+            }
+            l = l * alpha + ps;
+#pragma unroll
+            for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+                if (act[sb]) block_accum<D>(acc, sV[buf], 32 * sb, s[sb], lane);
+        }
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, tid, nt);
+        __syncthreads();
+    }
+
+    l += swap_halves(l);
+    if (qrow < T) {
+        const float inv = 1.0f / l;
+        __bf16 *orow = a.out_o + bh * T * D;
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float x[4] = {acc[dd][4 * u] * inv, acc[dd][4 * u + 1] * inv,
+                              acc[dd][4 * u + 2] * inv, acc[dd][4 * u + 3] * inv};
+                store_row4<D, false>(orow, qrow, 32 * dd + 8 * u + 4 * half, x, 0.f);
+            }
+        if (half == 0) a.out_lse[bh * T + qrow] = m * kLn2 + logf(l);
+    }
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_DQ_WAVES_PER_EU)))
+dq_bf16(ArgsB a) {
+    using C = CfgB<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char sK[2][C::BN * C::RB];
+    __shared__ __attribute__((aligned(16))) unsigned char sV[2][C::BN * C::RB];
+    const int nt = blockDim.x, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const QTileB c = decode_qtile_b(a, CAUSAL, wave);
+    const int T = a.T;
+    const int qrow = c.r0 + col;
+    const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
+    const __bf16 *kg = a.k + bg * T * D;
+    const __bf16 *vg = a.v + bg * T * D;
+
+    bf16x8 qv[C::KS], dov[C::KS];
+    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
+    load_operand_row<D, false>(dov, a.dO + bh * T * D, qrow, T, half, 0.f);
+
+    // delta_i = sum_d dO_id o_id over this row (fp32), written once for the dK/dV pass.
+    float delta;
+    {
+        bf16x8 ov[C::KS];
+        load_operand_row<D, false>(ov, a.o + bh * T * D, qrow, T, half, 0.f);
+        float part = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) part += bf2f(dov[s][i]) * bf2f(ov[s][i]);
+        delta = part + swap_halves(part);
+    }
+    float lse2;
+    if (qrow < T) {
+        lse2 = a.lse[bh * T + qrow] * kLog2e;
+        if (half == 0) a.delta[bh * T + qrow] = delta;
+    } else {
+        lse2 = INFINITY;
+        delta = 0.f;
+    }
+
+    f32x16 acc[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
+
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
+
+    KVStagerB<D, ROPE> stg;
+    stg.init(tid, a.rope_lb);
+    stg.load(kg, vg, 0, T, tid, nt);
+    stg.store(sK[0], sV[0], 0, T, tid, nt);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        const bool more = j + 1 < ntiles;
+        if (more) stg.load(kg, vg, j + 1, T, tid, nt);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int kb0 = j * C::BN + 32 * sb;
+            if (!(c.r0 < T && kb0 < T && (!CAUSAL || kb0 <= c.r0 + 31))) continue;
+            f32x16 p = block_scores<D>(sK[buf], 32 * sb, qv, col, half);
+            const bool edge = (CAUSAL && kb0 + 31 > c.r0) || kb0 + 32 > T;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = kb0 + acc_row(v, half);
+                const bool masked = edge && ((CAUSAL && key > qrow) || key >= T);
+                p[v] = masked ? 0.f : fast_exp2(fmaf(p[v], a.qscale, -lse2));
+            }
+            f32x16 ds = block_scores<D>(sV[buf], 32 * sb, dov, col, half);  // dP^T = V dO^T
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
+            block_accum<D>(acc, sK[buf], 32 * sb, ds, lane);  // dQ^T += K^T dS^T
+        }
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, tid, nt);
+        __syncthreads();
+    }
+
+    if (qrow < T) {
+        __bf16 *drow = a.dq + bh * T * D;
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float x[4] = {acc[dd][4 * u] * a.scale, acc[dd][4 * u + 1] * a.scale,
+                              acc[dd][4 * u + 2] * a.scale, acc[dd][4 * u + 3] * a.scale};
+                store_row4<D, ROPE>(drow, qrow, 32 * dd + 8 * u + 4 * half, x, a.rope_lb);
+            }
+    }
+}
+
+// LDS bytes per dK/dV wave: the larger of the staged query/dO tiles (+ lse2, delta) and the
+// fp32 partial dK, dV it contributes to the final reduction.
+template <int D>
+constexpr int dkdv_wave_bytes_b() {
+    constexpr int stage = 2 * 32 * CfgB<D>::RB + 2 * 32 * 4;
+    constexpr int red = 2 * 32 * D * 4;
+    return stage > red ? stage : red;
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_BF16_DKDV_WAVES_PER_EU)))
+dkdv_bf16(ArgsB a) {
+    using C = CfgB<D>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_b[];
+    const int nw = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const int T = a.T;
+    const int per = a.B * a.Hkv;
+    const int kb = blockIdx.x / per;
+    const int g = (blockIdx.x % per) % a.Hkv;
+    const int b = (blockIdx.x % per) / a.Hkv;
+    const size_t bg = (size_t)b * a.Hkv + g;
+    const int krow = kb * 32 + col;
+
+    bf16x8 kv[C::KS], vv[C::KS];
+    load_operand_row<D, ROPE>(kv, a.k + bg * T * D, krow, T, half, a.rope_lb);
+    load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, 0.f);
+
+    f32x16 dk[C::ND], dv[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) {
+        dk[dd] = zero16();
+        dv[dd] = zero16();
+    }
+
+    unsigned char *wbuf = smem_b + wave * dkdv_wave_bytes_b<D>();
+    unsigned char *sQ = wbuf;
+    unsigned char *sO = wbuf + 32 * C::RB;
+    float *sL = reinterpret_cast<float *>(wbuf + 2 * 32 * C::RB);
+    float *sDl = sL + 32;
+
+    const int nqb = (T + 31) / 32;
+    const int i0 = CAUSAL ? kb : 0;
+    const int per_head = nqb - i0;
+    const int nitems = a.G * per_head;
+
+    // Staging of one item (query head hh, query block i): each lane moves 32*NCH/64 chunks of
+    // the query tile and of the dO tile, held in registers one item ahead.
+    constexpr int PC = 32 * C::NCH / 64;
+    const int sch = lane % C::NCH;  // fixed column chunk of this lane
+    float rates[4];
+    if (ROPE)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) rates[p] = rope_rate<D>(4 * sch + p, a.rope_lb);
+    bf16x8 pq[PC], pd[PC];
+    float plse = 0.f, pdl = 0.f;
+    auto prefetch = [&](int it) {
+        const int hh = it / per_head, i = i0 + it % per_head;
+        const size_t bh = (size_t)b * a.Hq + (size_t)g * a.G + hh;
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) {
+            const int row = min(i * 32 + (lane + 64 * pc) / C::NCH, T - 1);
+            pq[pc] = *reinterpret_cast<const bf16x8 *>(a.q + (bh * T + row) * D + 8 * sch);
+            pd[pc] = *reinterpret_cast<const bf16x8 *>(a.dO + (bh * T + row) * D + 8 * sch);
+        }
+        const int lrow = min(i * 32 + col, T - 1);
+        plse = a.lse[bh * T + lrow];
+        pdl = a.delta[bh * T + lrow];
+    };
+
+    if (wave < nitems) prefetch(wave);
+    for (int it = wave; it < nitems; it += nw) {
+        const int i = i0 + it % per_head;
+        // Only this wave reads its staging area: ordering within the wave suffices.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        {
+            const bf16x8 zero = {};
+#pragma unroll
+            for (int pc = 0; pc < PC; ++pc) {
+                const int r = (lane + 64 * pc) / C::NCH;
+                const int row = i * 32 + r;
+                bf16x8 qq = pq[pc];
+                if (ROPE) {
+                    float x[8];
+                    unpack8(qq, x);
+                    rope_rotate<8>(x, row, rates, false);
+                    qq = round8(x);
+                }
+                *reinterpret_cast<bf16x8 *>(sQ + tile_off<D>(r, 8 * sch)) = row < T ? qq : zero;
+                *reinterpret_cast<bf16x8 *>(sO + tile_off<D>(r, 8 * sch)) = row < T ? pd[pc] : zero;
+            }
+            if (lane < 32) {
+                const bool valid = i * 32 + lane < T;
+                sL[lane] = valid ? plse * kLog2e : INFINITY;  // padding rows get P = 0
+                sDl[lane] = valid ? pdl : 0.f;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (it + nw < nitems) prefetch(it + nw);
+
+        // S = Q K'^T (rows: queries acc_row(v, half) of the block; column: this lane's key)
+        f32x16 p = zero16();
+#pragma unroll
+        for (int st = 0; st < C::KS; ++st)
+            p = mfma32_bf16(tile_read8<D>(sQ, col, 16 * st + 8 * half), kv[st], p);
+        const bool diag = CAUSAL && i == kb;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 L = ld4(sL + 8 * u + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = 4 * u + e;
+                const bool masked = diag && krow > i * 32 + acc_row(v, half);
+                p[v] = masked ? 0.f : fast_exp2(fmaf(p[v], a.qscale, -L[e]));
+            }
+        }
+        // dP = dO V^T
+        f32x16 ds = zero16();
+#pragma unroll
+        for (int st = 0; st < C::KS; ++st)
+            ds = mfma32_bf16(tile_read8<D>(sO, col, 16 * st + 8 * half), vv[st], ds);
+        // dV^T += dO^T P
+        block_accum<D>(dv, sO, 0, p, lane);
+        // dS = P (dP - delta)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 Dl = ld4(sDl + 8 * u + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds[4 * u + e] = p[4 * u + e] * (ds[4 * u + e] - Dl[e]);
+        }
+        // dK^T += Q^T dS
+        block_accum<D>(dk, sQ, 0, ds, lane);
+    }
+
+    // Add the waves' partial sums in LDS (fixed wave order), rotate dK back, round, store.
+    __syncthreads();
+    {
+        float *R = reinterpret_cast<float *>(wbuf);
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int d = 32 * dd + 8 * u + 4 * half;
+                st4(R + col * D + d, f32x4{dk[dd][4 * u] * a.scale, dk[dd][4 * u + 1] * a.scale,
+                                           dk[dd][4 * u + 2] * a.scale, dk[dd][4 * u + 3] * a.scale});
+                st4(R + 32 * D + col * D + d,
+                    f32x4{dv[dd][4 * u], dv[dd][4 * u + 1], dv[dd][4 * u + 2], dv[dd][4 * u + 3]});
+            }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 2 * 32 * (D / 4); idx += blockDim.x) {
+        const int t = idx / (32 * (D / 4));
+        const int r = (idx / (D / 4)) % 32;
+        const int cc = 4 * (idx % (D / 4));
+        f32x4 sum{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < nw; ++w)
+            sum += ld4(reinterpret_cast<const float *>(smem_b + w * dkdv_wave_bytes_b<D>()) +
+                       t * 32 * D + r * D + cc);
+        const int row = kb * 32 + r;
+        if (row < T) {
+            float x[4] = {sum[0], sum[1], sum[2], sum[3]};
+            if (t == 0)
+                store_row4<D, ROPE>(a.dk + bg * T * D, row, cc, x, a.rope_lb);
+            else
+                store_row4<D, false>(a.dv + bg * T * D, row, cc, x, 0.f);
+        }
+    }
+}
+
+ArgsB make_args_b(const Shape &s) {
+    ArgsB a{};
+    a.B = s.B;
+    a.Hq = s.Hq;
+    a.Hkv = s.Hkv;
+    a.T = s.T;
+    a.G = s.G;
+    a.scale = (float)(1.0 / sqrt((double)s.D));
+    a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));
+    a.rope_lb = s.rope_base > 0.f ? (float)log2((double)s.rope_base) : 0.f;
+    const QTileGeom g = qtile_geometry(s);
+    a.hpw = g.hpw;
+    a.rb = g.rb;
+    a.nqt = g.nqt;
+    return a;
+}
+
+#define NE_PICK_B(KERNEL)                                                                    \
+    template <int D>                                                                         \
+    const void *pick_##KERNEL(bool causal, bool rope) {                                      \
+        if (causal) return rope ? (const void *)KERNEL<D, true, true> : (const void *)KERNEL<D, true, false>; \
+        return rope ? (const void *)KERNEL<D, false, true> : (const void *)KERNEL<D, false, false>; \
+    }
+NE_PICK_B(fwd_bf16)
+NE_PICK_B(dq_bf16)
+NE_PICK_B(dkdv_bf16)
+#undef NE_PICK_B
+
+hipError_t launch_b(const void *fn, long long blocks, int threads, size_t lds, hipStream_t st,
+                    ArgsB &a) {
+    void *params[] = {&a};
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), params, lds, st);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const void *v, void *o,
+                           float *lse, hipStream_t st) {
+    ArgsB a = make_args_b(s);
+    a.q = static_cast<const __bf16 *>(q);
+    a.k = static_cast<const __bf16 *>(k);
+    a.v = static_cast<const __bf16 *>(v);
+    a.out_o = static_cast<__bf16 *>(o);
+    a.out_lse = lse;
+    const QTileGeom g = qtile_geometry(s);
+    const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
+    const void *fn = s.D == 64 ? pick_fwd_bf16<64>(causal, rope) : pick_fwd_bf16<32>(causal, rope);
+    return launch_b(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
+}
+
+hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const void *v,
+                          const void *o, const float *lse, const void *dO, void *dq, float *delta,
+                          hipStream_t st) {
+    ArgsB a = make_args_b(s);
+    a.q = static_cast<const __bf16 *>(q);
+    a.k = static_cast<const __bf16 *>(k);
+    a.v = static_cast<const __bf16 *>(v);
+    a.o = static_cast<const __bf16 *>(o);
+    a.lse = lse;
+    a.dO = static_cast<const __bf16 *>(dO);
+    a.dq = static_cast<__bf16 *>(dq);
+    a.delta = delta;
+    const QTileGeom g = qtile_geometry(s);
+    const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
+    const void *fn = s.D == 64 ? pick_dq_bf16<64>(causal, rope) : pick_dq_bf16<32>(causal, rope);
+    return launch_b(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
+}
+
+hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const void *v,
+                            const float *lse, const void *dO, const float *delta, void *dk,
+                            void *dv, hipStream_t st) {
+    ArgsB a = make_args_b(s);
+    a.q = static_cast<const __bf16 *>(q);
+    a.k = static_cast<const __bf16 *>(k);
+    a.v = static_cast<const __bf16 *>(v);
+    a.lse = lse;
+    a.dO = static_cast<const __bf16 *>(dO);
+    a.delta = const_cast<float *>(delta);  // read only in this pass
+    a.dk = static_cast<__bf16 *>(dk);
+    a.dv = static_cast<__bf16 *>(dv);
+    const KBlockGeom g = kblock_geometry(s);
+    const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
+    const size_t lds = (size_t)g.nwaves * (s.D == 64 ? dkdv_wave_bytes_b<64>() : dkdv_wave_bytes_b<32>());
+    const void *fn = s.D == 64 ? pick_dkdv_bf16<64>(causal, rope) : pick_dkdv_bf16<32>(causal, rope);
+    return launch_b(fn, g.nblocks, 64 * g.nwaves, lds, st, a);
+}
+
+}  // namespace ne

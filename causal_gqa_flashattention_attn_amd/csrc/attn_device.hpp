@@ -49,3 +49,69 @@ __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<
 __device__ __forceinline__ void st4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
 
 }  // namespace ne
+
+// ---------------------------------------------------------------------------------------------
+// bfloat16 building blocks (v_mfma_f32_32x32x16_bf16).  A operand of lane l: A[row = l % 32]
+// [k = 8 * (l / 32) .. + 7]; B operand: B[k = 8 * (l / 32) .. + 7][column = l % 32]; the f32
+// accumulator has the same layout as the fp32 32x32 family above.
+namespace ne {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row-major bf16 tiles in LDS, rows of D elements, with 16-byte chunks permuted within each row
+// by an XOR of the row index.  The permutation makes both access patterns conflict-free:
+// 16-byte reads of one chunk from 8 consecutive rows, and the 8-byte pieces of the transposed
+// read below (4 consecutive rows x 32 contiguous bytes per 16 lanes).
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row, int ch) {
+    if constexpr (D == 64) return ch ^ (((row & 3) << 1) | ((row >> 2) & 1));
+    else return ch ^ ((((row >> 1) & 1) << 1) | ((row >> 2) & 1));
+}
+
+// Byte offset of element (row, col) in a swizzled tile; col must be a multiple of 4.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+    return row * (2 * D) + 16 * chunk_swizzle<D>(row, col >> 3) + 2 * (col & 7);
+}
+
+// The 8 consecutive elements (row, col .. col+7) of a swizzled tile; col a multiple of 8.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_read8(const unsigned char *t, int row, int col) {
+    return *reinterpret_cast<const bf16x8 *>(t + tile_off<D>(row, col));
+}
+
+// Transposed read of a swizzled tile: lane l receives M[k0 + 4 * (l / 32) + j][c0 + l % 32] for
+// j = 0..3 (ds_read_b64_tr_b16: within each group of 16 lanes, lane i takes element i % 4 of the
+// 8-byte pieces addressed by lanes i / 4 + 4 j).
+template <int D>
+__device__ __forceinline__ bf16x4 tile_read_tr4(const unsigned char *t, int k0, int c0, int lane) {
+    const int row = k0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(uintptr_t)(t + tile_off<D>(row, col)));
+}
+
+// 8 keys of the transposed operand: (k0 .. +3) from the first read, (k0 + 8 .. +11) from the
+// second, matching the rows held in accumulator registers 8 s .. 8 s + 7 of a lane half.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_read_tr8(const unsigned char *t, int k0, int c0, int lane) {
+    const bf16x4 lo = tile_read_tr4<D>(t, k0, c0, lane);
+    const bf16x4 hi = tile_read_tr4<D>(t, k0 + 8, c0, lane);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Registers 8 s .. 8 s + 7 of an accumulator tile, rounded to bf16, as an MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16 &x, int s) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[8 * s + i];
+    return r;
+}
+
+}  // namespace ne

@@ -44,4 +44,14 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
                            const float *lse, const float *dO, const float *delta, float *dk,
                            float *dv, hipStream_t st);
 
+// bfloat16 variants: tensors are bf16 (passed untyped), lse and delta fp32.
+hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const void *v, void *o,
+                           float *lse, hipStream_t st);
+hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const void *v,
+                          const void *o, const float *lse, const void *dO, void *dq, float *delta,
+                          hipStream_t st);
+hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const void *v,
+                            const float *lse, const void *dO, const float *delta, void *dk,
+                            void *dv, hipStream_t st);
+
 }  // namespace ne

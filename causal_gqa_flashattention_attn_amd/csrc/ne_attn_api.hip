@@ -46,11 +46,12 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
     if (rc != NE_OK) return rc;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
         return NE_ERR_ALIGN;
-    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
-    const hipError_t e = ne::launch_fwd_f32(s, static_cast<const float *>(q),
-                                            static_cast<const float *>(k),
-                                            static_cast<const float *>(v), static_cast<float *>(o),
-                                            lse, stream);
+    const hipError_t e =
+        dtype == NE_BF16
+            ? ne::launch_fwd_bf16(s, q, k, v, o, lse, stream)
+            : ne::launch_fwd_f32(s, static_cast<const float *>(q), static_cast<const float *>(k),
+                                 static_cast<const float *>(v), static_cast<float *>(o), lse,
+                                 stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
@@ -68,11 +69,13 @@ int dq_impl(const void *q, const void *k, const void *v, const void *o, const fl
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
     if (any_misaligned({q, k, v, o, lse, dO, dq, delta_ws})) return NE_ERR_ALIGN;
-    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
-    const hipError_t e = ne::launch_dq_f32(
-        s, static_cast<const float *>(q), static_cast<const float *>(k),
-        static_cast<const float *>(v), static_cast<const float *>(o), lse,
-        static_cast<const float *>(dO), static_cast<float *>(dq), delta_ws, stream);
+    const hipError_t e =
+        dtype == NE_BF16
+            ? ne::launch_dq_bf16(s, q, k, v, o, lse, dO, dq, delta_ws, stream)
+            : ne::launch_dq_f32(s, static_cast<const float *>(q), static_cast<const float *>(k),
+                                static_cast<const float *>(v), static_cast<const float *>(o), lse,
+                                static_cast<const float *>(dO), static_cast<float *>(dq),
+                                delta_ws, stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
@@ -84,11 +87,13 @@ int dkdv_impl(const void *q, const void *k, const void *v, const float *lse, con
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
     if (any_misaligned({q, k, v, lse, dO, delta_ws, dk, dv})) return NE_ERR_ALIGN;
-    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
-    const hipError_t e = ne::launch_dkdv_f32(
-        s, static_cast<const float *>(q), static_cast<const float *>(k),
-        static_cast<const float *>(v), lse, static_cast<const float *>(dO), delta_ws,
-        static_cast<float *>(dk), static_cast<float *>(dv), stream);
+    const hipError_t e =
+        dtype == NE_BF16
+            ? ne::launch_dkdv_bf16(s, q, k, v, lse, dO, delta_ws, dk, dv, stream)
+            : ne::launch_dkdv_f32(s, static_cast<const float *>(q), static_cast<const float *>(k),
+                                  static_cast<const float *>(v), lse,
+                                  static_cast<const float *>(dO), delta_ws,
+                                  static_cast<float *>(dk), static_cast<float *>(dv), stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 

@@ -1,0 +1,157 @@
+"""Properties of the HIP path that hold at any size, checked without the oracle."""
+import math
+
+import numpy as np
+import pytest
+
+from helpers import gpu_fwd_bwd, normwise
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+
+
+def qkvd(B, Hq, Hkv, T, D, seed):
+    return {"q": rnd((B, Hq, T, D), seed), "k": rnd((B, Hkv, T, D), seed + 1),
+            "v": rnd((B, Hkv, T, D), seed + 2), "dO": rnd((B, Hq, T, D), seed + 3)}
+
+
+@pytest.mark.parametrize("name", ["gpu_model", "cpu_model"])
+def test_bitwise_determinism(ne, name):
+    """No atomics anywhere: two runs give identical bits."""
+    x = make_inputs(WORKLOADS[name], 0)
+    print(f"\n[case] determinism {name}", flush=True)
+    a = gpu_fwd_bwd(ne, x)
+    b = gpu_fwd_bwd(ne, x)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("t", [63, 200, 255])
+def test_causality_is_bitwise(ne, t):
+    """Changing q, k, v, dO at positions > t leaves o and lse at positions <= t bit-identical
+    (masked probabilities are exactly 0); changing queries and dO at positions < 32*floor(t/32)
+    leaves dk, dv at keys >= 32*floor(t/32) bit-identical."""
+    B, Hq, Hkv, T, D = 2, 6, 2, 300, 64
+    x = qkvd(B, Hq, Hkv, T, D, 40)
+    y = {n: a.copy() for n, a in x.items()}
+    r = np.random.default_rng(41)
+    for n in y:
+        y[n][:, :, t + 1:] = r.standard_normal(y[n][:, :, t + 1:].shape)
+    print(f"\n[case] causality t={t}", flush=True)
+    a = gpu_fwd_bwd(ne, x, with_bwd=False)
+    b = gpu_fwd_bwd(ne, y, with_bwd=False)
+    assert np.array_equal(a["o"][:, :, :t + 1], b["o"][:, :, :t + 1])
+    assert np.array_equal(a["lse"][:, :, :t + 1], b["lse"][:, :, :t + 1])
+    assert not np.array_equal(a["o"][:, :, t + 1:], b["o"][:, :, t + 1:])
+    tb = 32 * (t // 32)
+    z = {n: a_.copy() for n, a_ in x.items()}
+    z["q"][:, :, :tb] = r.standard_normal(z["q"][:, :, :tb].shape)
+    z["dO"][:, :, :tb] = r.standard_normal(z["dO"][:, :, :tb].shape)
+    ga = gpu_fwd_bwd(ne, x)
+    gz = gpu_fwd_bwd(ne, z)
+    assert np.array_equal(ga["dk"][:, :, tb:], gz["dk"][:, :, tb:])
+    assert np.array_equal(ga["dv"][:, :, tb:], gz["dv"][:, :, tb:])
+
+
+def test_zero_queries_give_prefix_means(ne):
+    B, Hq, Hkv, T, D = 1, 8, 2, 257, 64
+    x = qkvd(B, Hq, Hkv, T, D, 50)
+    x["q"][:] = 0
+    print("\n[case] q=0", flush=True)
+    res = gpu_fwd_bwd(ne, x, with_bwd=False)
+    G = Hq // Hkv
+    n = np.arange(1, T + 1)
+    for h in range(Hq):
+        pm = np.cumsum(x["v"][:, h // G].astype(np.float64), axis=1) / n[None, :, None]
+        assert np.abs(res["o"][:, h] - pm).max() < 2e-5
+        assert np.abs(res["lse"][:, h] - np.log(n)[None]).max() < 2e-5
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_single_position(ne, causal):
+    """T = 1: o = v_0 exactly, lse = q.k/sqrt(D), dq = dk = 0, dv = sum of dO over the group."""
+    B, Hq, Hkv, D = 3, 12, 4, 64
+    x = qkvd(B, Hq, Hkv, 1, D, 60)
+    print("\n[case] T=1", flush=True)
+    res = gpu_fwd_bwd(ne, x, causal=causal)
+    G = Hq // Hkv
+    for h in range(Hq):
+        g = h // G
+        assert np.array_equal(res["o"][:, h, 0], x["v"][:, g, 0].astype(np.float64))
+        s = (x["q"][:, h, 0].astype(np.float64) * x["k"][:, g, 0]).sum(-1) / math.sqrt(D)
+        assert np.abs(res["lse"][:, h, 0] - s).max() < 2e-5
+    assert np.abs(res["dq"]).max() < 1e-5 and np.abs(res["dk"]).max() < 1e-5
+    ref = x["dO"].astype(np.float64).reshape(B, Hkv, G, 1, D).sum(2)
+    assert np.abs(res["dv"] - ref).max() < 1e-5
+
+
+def test_constant_values(ne):
+    """v_j = c: o_i = c and dq = dk = 0 up to rounding."""
+    B, Hq, Hkv, T, D = 2, 6, 3, 190, 64
+    x = qkvd(B, Hq, Hkv, T, D, 70)
+    c = rnd((D,), 71)
+    x["v"][:] = c
+    print("\n[case] constant v", flush=True)
+    res = gpu_fwd_bwd(ne, x)
+    assert np.abs(res["o"] - c).max() < 1e-5
+    scale = np.abs(x["dO"]).max() * np.abs(x["k"]).max()
+    assert np.abs(res["dq"]).max() < 1e-5 * scale
+    assert np.abs(res["dk"]).max() < 1e-5 * scale * T
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_gradient_sum_identities(ne, causal):
+    """Without RoPE: sum_j dk_j = 0 and sum_j dv_j = sum over the group and all i of dO_i."""
+    B, Hq, Hkv, T, D = 2, 12, 4, 200, 64
+    x = qkvd(B, Hq, Hkv, T, D, 80)
+    print(f"\n[case] gradient sums causal={causal}", flush=True)
+    res = gpu_fwd_bwd(ne, x, causal=causal)
+    G = Hq // Hkv
+    dk_scale = np.abs(res["dk"]).max()
+    assert np.abs(res["dk"].sum(2)).max() < 1e-4 * dk_scale * math.sqrt(T)
+    ref = x["dO"].astype(np.float64).reshape(B, Hkv, G, T, D).sum((2, 3))
+    assert normwise(res["dv"].sum(2), ref) < 1e-5
+
+
+def test_gqa_matches_mha_on_repeated_kv(ne):
+    B, Hq, Hkv, T, D = 2, 12, 4, 160, 64
+    x = qkvd(B, Hq, Hkv, T, D, 90)
+    G = Hq // Hkv
+    y = dict(x, k=np.repeat(x["k"], G, axis=1), v=np.repeat(x["v"], G, axis=1))
+    print("\n[case] gqa vs mha", flush=True)
+    a = gpu_fwd_bwd(ne, x)
+    b = gpu_fwd_bwd(ne, y)
+    assert np.abs(a["o"] - b["o"]).max() < 1e-5
+    assert np.abs(a["lse"] - b["lse"]).max() < 1e-5
+    assert normwise(a["dq"], b["dq"]) < 1e-5
+    assert normwise(a["dk"], b["dk"].reshape(B, Hkv, G, T, D).sum(2)) < 1e-5
+    assert normwise(a["dv"], b["dv"].reshape(B, Hkv, G, T, D).sum(2)) < 1e-5
+
+
+def test_key_shift_invariance(ne):
+    """k_j -> k_j + u: o unchanged, lse_i increases by q_i.u/sqrt(D); large u stresses the
+    running maximum."""
+    B, Hq, Hkv, T, D = 1, 8, 2, 300, 64
+    x = qkvd(B, Hq, Hkv, T, D, 100)
+    u = 3.0 * rnd((D,), 101)
+    y = dict(x, k=(x["k"] + u).astype(np.float32))
+    print("\n[case] key shift", flush=True)
+    a = gpu_fwd_bwd(ne, x, with_bwd=False)
+    b = gpu_fwd_bwd(ne, y, with_bwd=False)
+    assert np.abs(a["o"] - b["o"]).max() < 1e-4
+    shift = (x["q"].astype(np.float64) @ u.astype(np.float64)) / math.sqrt(D)
+    assert np.abs(b["lse"] - a["lse"] - shift).max() < 1e-3
+
+
+def test_rope_single_position_is_identity(ne):
+    """Position 0 is not rotated, so with T = 1 RoPE changes nothing."""
+    x = qkvd(2, 8, 2, 1, 64, 110)
+    print("\n[case] rope T=1", flush=True)
+    a = gpu_fwd_bwd(ne, x, rope_base=10000.0)
+    b = gpu_fwd_bwd(ne, x)
+    for n in a:
+        assert np.abs(a[n] - b[n]).max() < 1e-6, n

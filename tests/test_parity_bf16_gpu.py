@@ -1,0 +1,67 @@
+"""bf16 path (optional fused RoPE) against the fp64 oracle on the same bf16-rounded inputs.
+
+Bar: normwise relative error max |x - x_ref| / max |x_ref| <= 2e-2 on o, lse, dq, dk, dv.
+"""
+import numpy as np
+import pytest
+
+from helpers import assert_bf16, gpu_fwd_bwd, oracle_fwd_bwd
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bf16(ne, oracle_mod, w, seed=0, causal=True, rope_base=None):
+    import torch
+    rope_base = w.rope_base if rope_base is None else rope_base
+    x = make_inputs(w.with_(dtype="bf16"), seed)
+    print(f"\n[case] bf16 {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} T{w.T} D{w.D} causal={causal} "
+          f"rope={rope_base} seed={seed}", flush=True)
+    res = gpu_fwd_bwd(ne, x, causal=causal, rope_base=rope_base, dtype=torch.bfloat16)
+    ref = oracle_fwd_bwd(oracle_mod, x, causal=causal, rope_base=rope_base)
+    e = assert_bf16(res, ref, w.name)
+    print("  " + " ".join(f"{k}={v:.2e}" for k, v in e.items() if k.endswith("_rel")))
+    return res, ref
+
+
+def test_bf16_rope_workload(ne, oracle_mod):
+    """The full bf16 + RoPE workload (B16 Hq16 Hkv4 T1024 D64, base 10000)."""
+    run_bf16(ne, oracle_mod, WORKLOADS["bf16_rope"])
+
+
+BF16_CASES = [
+    (1, 4, 2, 64, 32), (2, 12, 4, 130, 64), (1, 6, 3, 517, 64), (1, 16, 4, 256, 64),
+    (1, 2, 1, 100, 64), (1, 8, 2, 33, 32), (2, 5, 5, 1, 64),
+]
+
+
+@pytest.mark.parametrize("rope", [0.0, 10000.0])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", BF16_CASES)
+def test_bf16_shapes(ne, oracle_mod, shape, causal, rope):
+    B, Hq, Hkv, T, D = shape
+    run_bf16(ne, oracle_mod, Workload("bf16", B, Hq, Hkv, T, D, dtype="bf16"), seed=5,
+             causal=causal, rope_base=rope)
+
+
+def test_bf16_gpu_model_shape(ne, oracle_mod):
+    """The GPU-model layer shape (boosted query rows) in bf16 without RoPE."""
+    run_bf16(ne, oracle_mod, WORKLOADS["gpu_model"].with_(dtype="bf16"))
+
+
+def test_bf16_determinism_and_causality(ne):
+    import torch
+    w = Workload("bf16", 2, 8, 2, 300, 64, dtype="bf16", rope_base=10000.0)
+    x = make_inputs(w, 9)
+    a = gpu_fwd_bwd(ne, x, rope_base=w.rope_base, dtype=torch.bfloat16)
+    b = gpu_fwd_bwd(ne, x, rope_base=w.rope_base, dtype=torch.bfloat16)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+    t = 150
+    y = {n: v.copy() for n, v in x.items()}
+    r = np.random.default_rng(3)
+    for n in y:
+        y[n][:, :, t + 1:] = r.standard_normal(y[n][:, :, t + 1:].shape).astype(np.float32)
+    c = gpu_fwd_bwd(ne, y, rope_base=w.rope_base, dtype=torch.bfloat16, with_bwd=False)
+    assert np.array_equal(a["o"][:, :, :t + 1], c["o"][:, :, :t + 1])
+    assert np.array_equal(a["lse"][:, :, :t + 1], c["lse"][:, :, :t + 1])

@@ -52,3 +52,33 @@ def test_ragged_and_odd_shapes(ne, oracle_mod, shape, causal):
 @pytest.mark.parametrize("name", ["tiny", "cpu_model"])
 def test_non_causal_workloads(ne, oracle_mod, name):
     run_case(ne, oracle_mod, WORKLOADS[name], causal=False)
+
+
+ROPE_CASES = [
+    (1, 4, 2, 64, 32, 10000.0), (2, 12, 4, 130, 64, 10000.0), (1, 6, 3, 517, 64, 10000.0),
+    (1, 16, 4, 1024, 64, 10000.0), (1, 4, 4, 33, 32, 500.0),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("case", ROPE_CASES)
+def test_fp32_fused_rope(ne, oracle_mod, case, causal):
+    """fp32 with RoPE applied in-kernel against the oracle's fp64 rotation; dq, dk are gradients
+    with respect to the un-rotated q, k."""
+    B, Hq, Hkv, T, D, base = case
+    w = Workload("rope_f32", B, Hq, Hkv, T, D, rope_base=base)
+    x = make_inputs(w, 11)
+    print(f"\n[case] rope fp32 {case} causal={causal}", flush=True)
+    res = gpu_fwd_bwd(ne, x, causal=causal, rope_base=base)
+    ref = oracle_fwd_bwd(oracle_mod, x, causal=causal, rope_base=base)
+    assert_f32(res, ref, f"rope {case}")
+
+
+def test_fp32_rope_long_positions(ne, oracle_mod):
+    """Positions up to 4095: the angle must be reduced accurately at large t."""
+    w = Workload("rope_long", 1, 4, 1, 4096, 64, rope_base=10000.0)
+    x = make_inputs(w, 12)
+    print("\n[case] rope fp32 T4096", flush=True)
+    res = gpu_fwd_bwd(ne, x, causal=True, rope_base=w.rope_base)
+    ref = oracle_fwd_bwd(oracle_mod, x, causal=True, rope_base=w.rope_base)
+    assert_f32(res, ref, "rope long")
