@@ -216,8 +216,11 @@ def main():
     else:
         roof = None
 
+    metric = METRIC if w.name == "gpu_model" else (
+        f"attn fwd+bwd TFLOP/s & % MFMA peak, B{w.B} Hq{w.Hq}/Hkv{w.Hkv} T{w.T} D{w.D} "
+        f"{'causal' if w.causal else 'non-causal'} {w.dtype}" + (" RoPE" if w.rope_base else ""))
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -145,43 +145,46 @@ __device__ __forceinline__ QTileB decode_qtile_b(const ArgsB &a, bool causal, in
 }
 
 // Staging of BN-row K and V tiles: HBM -> registers (issued one tile ahead) -> swizzled LDS.
-// The thread count is a multiple of D/8, so each thread always handles the same 16-byte column
-// chunk and its RoPE rates are computed once.
+// A tile is moved in 1 KB pieces, one wave-wide 16-byte load per piece; piece c goes to wave
+// c % nw, so every branch on the piece index is uniform across the wave, and each lane always
+// moves the same column chunk (its RoPE rates are computed once).
 template <int D, bool ROPE>
 struct KVStagerB {
     using C = CfgB<D>;
-    static constexpr int CH = C::BN * C::NCH;
-    static constexpr int MAXC = (CH + 127) / 128;  // query-tile work-groups have >= 2 waves
-    bf16x8 k[MAXC], v[MAXC];
+    static constexpr int RPP = 64 / C::NCH;            // rows per 1 KB piece
+    static constexpr int NP = C::BN / RPP;             // pieces per tile
+    static constexpr int MAXP = (NP + 1) / 2;          // per wave (query-tile groups have >= 2 waves)
+    bf16x8 k[MAXP], v[MAXP];
     float rates[4];
-    int ch;
+    int ch, rsub;
 
-    __device__ __forceinline__ void init(int tid, float lb) {
-        ch = tid % C::NCH;
+    __device__ __forceinline__ void init(int lane, float lb) {
+        ch = lane % C::NCH;
+        rsub = lane / C::NCH;
         if (ROPE)
 #pragma unroll
             for (int p = 0; p < 4; ++p) rates[p] = rope_rate<D>(4 * ch + p, lb);
     }
     __device__ __forceinline__ void load(const __bf16 *kg, const __bf16 *vg, int tile, int T,
-                                         int tid, int nt) {
+                                         int wave, int nw) {
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            const int c = tid + i * nt;
-            if (c < CH) {
-                const int row = min(tile * C::BN + c / C::NCH, T - 1);
+        for (int i = 0; i < MAXP; ++i) {
+            const int pc = wave + i * nw;
+            if (pc < NP) {
+                const int row = min(tile * C::BN + pc * RPP + rsub, T - 1);
                 k[i] = *reinterpret_cast<const bf16x8 *>(kg + (size_t)row * D + 8 * ch);
                 v[i] = *reinterpret_cast<const bf16x8 *>(vg + (size_t)row * D + 8 * ch);
             }
         }
     }
     __device__ __forceinline__ void store(unsigned char *sK, unsigned char *sV, int tile, int T,
-                                          int tid, int nt) {
+                                          int wave, int nw) {
         const bf16x8 zero = {};
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            const int c = tid + i * nt;
-            if (c < CH) {
-                const int r = c / C::NCH;
+        for (int i = 0; i < MAXP; ++i) {
+            const int pc = wave + i * nw;
+            if (pc < NP) {
+                const int r = pc * RPP + rsub;
                 const int row = tile * C::BN + r;
                 bf16x8 kk = k[i];
                 if (ROPE) {
@@ -242,8 +245,8 @@ fwd_bf16(ArgsB a) {
     using C = CfgB<D>;
     __shared__ __attribute__((aligned(16))) unsigned char sK[2][C::BN * C::RB];
     __shared__ __attribute__((aligned(16))) unsigned char sV[2][C::BN * C::RB];
-    const int nt = blockDim.x, tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int nw = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const QTileB c = decode_qtile_b(a, CAUSAL, wave);
     const int T = a.T;
@@ -265,14 +268,14 @@ fwd_bf16(ArgsB a) {
     const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
 
     KVStagerB<D, ROPE> stg;
-    stg.init(tid, a.rope_lb);
-    stg.load(kg, vg, 0, T, tid, nt);
-    stg.store(sK[0], sV[0], 0, T, tid, nt);
+    stg.init(lane, a.rope_lb);
+    stg.load(kg, vg, 0, T, wave, nw);
+    stg.store(sK[0], sV[0], 0, T, wave, nw);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
         const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, T, tid, nt);
+        if (more) stg.load(kg, vg, j + 1, T, wave, nw);
         f32x16 s[2];
         bool act[2];
 #pragma unroll
@@ -297,28 +300,34 @@ fwd_bf16(ArgsB a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sb][v]);
             }
-            mx = fmaxf(mx, swap_halves(mx));
-            const float mnew = fmaxf(m, mx * a.qscale);
-            const float alpha = fast_exp2(m - mnew);
-            m = mnew;
+            mx = fmaxf(mx, swap_halves(mx)) * a.qscale;
+            // The reference maximum m only moves when some row's maximum exceeds it by more
+            // than 2^8: probabilities up to 256 are exact enough in fp32 sums and bf16 operands,
+            // and most tiles then skip the rescale of l and O entirely.
+            if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
+                const float mnew = fmaxf(m, mx);
+                const float alpha = fast_exp2(m - mnew);
+                m = mnew;
+                l *= alpha;
+#pragma unroll
+                for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
+            }
             float ps = 0.f;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
                 if (!act[sb]) continue;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    s[sb][v] = fast_exp2(fmaf(s[sb][v], a.qscale, -mnew));
+                    s[sb][v] = fast_exp2(fmaf(s[sb][v], a.qscale, -m));
                     ps += s[sb][v];
                 }
             }
-            l = l * alpha + ps;
-#pragma unroll
-            for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
+            l += ps;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
                 if (act[sb]) block_accum<D>(acc, sV[buf], 32 * sb, s[sb], lane);
         }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, tid, nt);
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw);
         __syncthreads();
     }
 
@@ -344,8 +353,8 @@ dq_bf16(ArgsB a) {
     using C = CfgB<D>;
     __shared__ __attribute__((aligned(16))) unsigned char sK[2][C::BN * C::RB];
     __shared__ __attribute__((aligned(16))) unsigned char sV[2][C::BN * C::RB];
-    const int nt = blockDim.x, tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int nw = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const QTileB c = decode_qtile_b(a, CAUSAL, wave);
     const int T = a.T;
@@ -388,14 +397,14 @@ dq_bf16(ArgsB a) {
     const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
 
     KVStagerB<D, ROPE> stg;
-    stg.init(tid, a.rope_lb);
-    stg.load(kg, vg, 0, T, tid, nt);
-    stg.store(sK[0], sV[0], 0, T, tid, nt);
+    stg.init(lane, a.rope_lb);
+    stg.load(kg, vg, 0, T, wave, nw);
+    stg.store(sK[0], sV[0], 0, T, wave, nw);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
         const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, T, tid, nt);
+        if (more) stg.load(kg, vg, j + 1, T, wave, nw);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int kb0 = j * C::BN + 32 * sb;
@@ -413,7 +422,7 @@ dq_bf16(ArgsB a) {
             for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
             block_accum<D>(acc, sK[buf], 32 * sb, ds, lane);  // dQ^T += K^T dS^T
         }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, tid, nt);
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw);
         __syncthreads();
     }
 
@@ -530,7 +539,7 @@ dkdv_bf16(ArgsB a) {
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        if (it + nw < nitems) prefetch(it + nw);
+        prefetch(min(it + nw, nitems - 1));  // unconditional: the last item is fetched again
 
         // S = Q K'^T (rows: queries acc_row(v, half) of the block; column: this lane's key)
         f32x16 p = zero16();

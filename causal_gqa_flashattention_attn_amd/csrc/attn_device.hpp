@@ -63,14 +63,20 @@ __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Row-major bf16 tiles in LDS, rows of D elements, with 16-byte chunks permuted within each row
-// by an XOR of the row index.  The permutation makes both access patterns conflict-free:
-// 16-byte reads of one chunk from 8 consecutive rows, and the 8-byte pieces of the transposed
-// read below (4 consecutive rows x 32 contiguous bytes per 16 lanes).
+// Row-major bf16 tiles in LDS, rows of D elements, 16-byte chunks permuted within each row.
+// The LDS serves 256 bytes (64 banks) per cycle and a 16-byte read 16 lanes per cycle, so a
+// pattern is conflict-free when the 16 lanes of each group hit 16 distinct 16-byte slots modulo
+// 256 bytes.  The permutations below make three patterns conflict-free (measured with the LDS
+// bank-conflict counter): 16-byte reads of one chunk from 16 consecutive rows, the transposed
+// read below (32 lanes: 4 consecutive rows x 64 contiguous bytes), and staging writes where 16
+// lanes fill two (D = 64) or four (D = 32) whole rows.
+//   D = 64 (128-byte rows): chunk c of row r is stored at c ^ f(r),
+//          f(r) = 2 * (((r & 3) + ((r >> 2) & 3)) & 3) + ((r >> 3) & 1).
+//   D = 32 (64-byte rows):  chunk c of row r is stored at c ^ ((r >> 2) & 3).
 template <int D>
 __device__ __forceinline__ int chunk_swizzle(int row, int ch) {
-    if constexpr (D == 64) return ch ^ (((row & 3) << 1) | ((row >> 2) & 1));
-    else return ch ^ ((((row >> 1) & 1) << 1) | ((row >> 2) & 1));
+    if constexpr (D == 64) return ch ^ (2 * (((row & 3) + ((row >> 2) & 3)) & 3) + ((row >> 3) & 1));
+    else return ch ^ ((row >> 2) & 3);
 }
 
 // Byte offset of element (row, col) in a swizzled tile; col must be a multiple of 4.
