@@ -52,6 +52,8 @@ struct ArgsB {
     float *out_lse, *delta;
     int B, Hq, Hkv, T, G;
     int hpw, rb, nqt;
+    int paired;     // work-groups take mirrored pairs of tiles or key blocks
+    int nkb;        // key blocks per head (dK/dV)
     float qscale;   // scale * log2(e)
     float scale;    // 1 / sqrt(D)
     float rope_lb;  // log2(rope base)
@@ -128,19 +130,34 @@ struct QTileB {
     int b, g, h, qt, r0;
 };
 
-__device__ __forceinline__ QTileB decode_qtile_b(const ArgsB &a, bool causal, int wave) {
+// Work-group -> (batch, kv head, head chunk) and its query tiles (mirrored pairs when causal).
+struct QWorkB {
+    int b, g, hc, qt0, qt1;  // qt1 < 0: a single tile
+};
+
+__device__ __forceinline__ QWorkB decode_qwork_b(const ArgsB &a) {
     const int nhc = a.G / a.hpw;
     const int per = a.B * a.Hkv * nhc;
     const int t = blockIdx.x / per;
     int r = blockIdx.x % per;
-    QTileB c;
-    c.qt = causal ? a.nqt - 1 - t : t;
-    const int hc = r % nhc;
+    QWorkB w;
+    w.hc = r % nhc;
     r /= nhc;
-    c.g = r % a.Hkv;
-    c.b = r / a.Hkv;
-    c.h = c.g * a.G + hc * a.hpw + wave / a.rb;
-    c.r0 = c.qt * 32 * a.rb + (wave % a.rb) * 32;
+    w.g = r % a.Hkv;
+    w.b = r / a.Hkv;
+    // Longest tile first under a causal mask (the order is immaterial otherwise).
+    w.qt0 = a.nqt - 1 - t;
+    w.qt1 = a.paired && t < w.qt0 ? t : -1;
+    return w;
+}
+
+__device__ __forceinline__ QTileB qtile_of_b(const ArgsB &a, const QWorkB &w, int qt, int wave) {
+    QTileB c;
+    c.b = w.b;
+    c.g = w.g;
+    c.qt = qt;
+    c.h = w.g * a.G + w.hc * a.hpw + wave / a.rb;
+    c.r0 = qt * 32 * a.rb + (wave % a.rb) * 32;
     return c;
 }
 
@@ -240,15 +257,13 @@ __device__ __forceinline__ void block_accum(f32x16 (&acc)[CfgB<D>::ND], const un
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_FWD_WAVES_PER_EU)))
-fwd_bf16(ArgsB a) {
+__device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c,
+                                           unsigned char (&sK)[2][CfgB<D>::BN * CfgB<D>::RB],
+                                           unsigned char (&sV)[2][CfgB<D>::BN * CfgB<D>::RB]) {
     using C = CfgB<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char sK[2][C::BN * C::RB];
-    __shared__ __attribute__((aligned(16))) unsigned char sV[2][C::BN * C::RB];
     const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
-    const QTileB c = decode_qtile_b(a, CAUSAL, wave);
     const int T = a.T;
     const int qrow = c.r0 + col;
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
@@ -348,15 +363,27 @@ fwd_bf16(ArgsB a) {
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_DQ_WAVES_PER_EU)))
-dq_bf16(ArgsB a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_FWD_WAVES_PER_EU)))
+fwd_bf16(ArgsB a) {
+    __shared__ __attribute__((aligned(16))) unsigned char sK[2][CfgB<D>::BN * CfgB<D>::RB];
+    __shared__ __attribute__((aligned(16))) unsigned char sV[2][CfgB<D>::BN * CfgB<D>::RB];
+    const int wave = threadIdx.x >> 6;
+    const QWorkB w = decode_qwork_b(a);
+    fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), sK, sV);
+    if (w.qt1 >= 0) {
+        __syncthreads();
+        fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt1, wave), sK, sV);
+    }
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c,
+                                          unsigned char (&sK)[2][CfgB<D>::BN * CfgB<D>::RB],
+                                          unsigned char (&sV)[2][CfgB<D>::BN * CfgB<D>::RB]) {
     using C = CfgB<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char sK[2][C::BN * C::RB];
-    __shared__ __attribute__((aligned(16))) unsigned char sV[2][C::BN * C::RB];
     const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
-    const QTileB c = decode_qtile_b(a, CAUSAL, wave);
     const int T = a.T;
     const int qrow = c.r0 + col;
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
@@ -439,6 +466,20 @@ dq_bf16(ArgsB a) {
     }
 }
 
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_DQ_WAVES_PER_EU)))
+dq_bf16(ArgsB a) {
+    __shared__ __attribute__((aligned(16))) unsigned char sK[2][CfgB<D>::BN * CfgB<D>::RB];
+    __shared__ __attribute__((aligned(16))) unsigned char sV[2][CfgB<D>::BN * CfgB<D>::RB];
+    const int wave = threadIdx.x >> 6;
+    const QWorkB w = decode_qwork_b(a);
+    dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), sK, sV);
+    if (w.qt1 >= 0) {
+        __syncthreads();
+        dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt1, wave), sK, sV);
+    }
+}
+
 // LDS bytes per dK/dV wave: the larger of the staged query/dO tiles (+ lse2, delta) and the
 // fp32 partial dK, dV it contributes to the final reduction.
 template <int D>
@@ -449,18 +490,13 @@ constexpr int dkdv_wave_bytes_b() {
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_BF16_DKDV_WAVES_PER_EU)))
-dkdv_bf16(ArgsB a) {
+__device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int kb,
+                                             unsigned char *smem_b) {
     using C = CfgB<D>;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_b[];
     const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
-    const int per = a.B * a.Hkv;
-    const int kb = blockIdx.x / per;
-    const int g = (blockIdx.x % per) % a.Hkv;
-    const int b = (blockIdx.x % per) / a.Hkv;
     const size_t bg = (size_t)b * a.Hkv + g;
     const int krow = kb * 32 + col;
 
@@ -610,6 +646,21 @@ dkdv_bf16(ArgsB a) {
     }
 }
 
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_BF16_DKDV_WAVES_PER_EU)))
+dkdv_bf16(ArgsB a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_b[];
+    const int per = a.B * a.Hkv;
+    const int p = blockIdx.x / per;
+    const int g = (blockIdx.x % per) % a.Hkv;
+    const int b = (blockIdx.x % per) / a.Hkv;
+    dkdv_block_b<D, CAUSAL, ROPE>(a, b, g, p, smem_b);
+    if (a.paired && a.nkb - 1 - p > p) {
+        __syncthreads();
+        dkdv_block_b<D, CAUSAL, ROPE>(a, b, g, a.nkb - 1 - p, smem_b);
+    }
+}
+
 ArgsB make_args_b(const Shape &s) {
     ArgsB a{};
     a.B = s.B;
@@ -620,10 +671,11 @@ ArgsB make_args_b(const Shape &s) {
     a.scale = (float)(1.0 / sqrt((double)s.D));
     a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));
     a.rope_lb = s.rope_base > 0.f ? (float)log2((double)s.rope_base) : 0.f;
-    const QTileGeom g = qtile_geometry(s);
+    const QTileGeom g = qtile_geometry(s, false);
     a.hpw = g.hpw;
     a.rb = g.rb;
     a.nqt = g.nqt;
+    a.nkb = kblock_geometry(s, false).nkb;
     return a;
 }
 
@@ -654,7 +706,8 @@ hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const v
     a.v = static_cast<const __bf16 *>(v);
     a.out_o = static_cast<__bf16 *>(o);
     a.out_lse = lse;
-    const QTileGeom g = qtile_geometry(s);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.fwd);
+    a.paired = g.paired;
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
     const void *fn = s.D == 64 ? pick_fwd_bf16<64>(causal, rope) : pick_fwd_bf16<32>(causal, rope);
     return launch_b(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
@@ -672,7 +725,8 @@ hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const vo
     a.dO = static_cast<const __bf16 *>(dO);
     a.dq = static_cast<__bf16 *>(dq);
     a.delta = delta;
-    const QTileGeom g = qtile_geometry(s);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.dq);
+    a.paired = g.paired;
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
     const void *fn = s.D == 64 ? pick_dq_bf16<64>(causal, rope) : pick_dq_bf16<32>(causal, rope);
     return launch_b(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
@@ -690,7 +744,8 @@ hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const 
     a.delta = const_cast<float *>(delta);  // read only in this pass
     a.dk = static_cast<__bf16 *>(dk);
     a.dv = static_cast<__bf16 *>(dv);
-    const KBlockGeom g = kblock_geometry(s);
+    const KBlockGeom g = kblock_geometry(s, s.causal && kPairBf16.dkdv);
+    a.paired = g.paired;
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
     const size_t lds = (size_t)g.nwaves * (s.D == 64 ? dkdv_wave_bytes_b<64>() : dkdv_wave_bytes_b<32>());
     const void *fn = s.D == 64 ? pick_dkdv_bf16<64>(causal, rope) : pick_dkdv_bf16<32>(causal, rope);

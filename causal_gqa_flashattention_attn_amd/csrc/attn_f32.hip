@@ -92,7 +92,8 @@ struct Args {
     float *out_o, *out_lse, *dq, *dk, *dv, *delta;
     int B, Hq, Hkv, T, G;
     int hpw, rb, nqt;  // query-tile kernels
-    int kw;            // waves of a dK/dV work-group
+    int paired;        // work-groups take mirrored pairs of tiles or key blocks
+    int nkb;           // key blocks per head (dK/dV)
     float qscale;      // scale * log2(e)
     float scale;       // 1 / sqrt(D)
     RopeArgs rope;
@@ -102,20 +103,36 @@ struct QTile {
     int b, g, h, qt, r0;  // r0: first query row of this wave
 };
 
-// Longest work first: causal query tiles are issued from the last (most key tiles) down.
-__device__ __forceinline__ QTile decode_qtile(const Args &a, bool causal, int wave) {
+// Work-group -> (batch, kv head, head chunk) and its query tiles.  Work-group row t takes tile
+// nqt-1-t (under a causal mask the longest tiles go first) and, in paired launches, also tile t
+// after it.
+struct QTileWork {
+    int b, g, hc, qt0, qt1;  // qt1 < 0: a single tile
+};
+
+__device__ __forceinline__ QTileWork decode_qwork(const Args &a) {
     const int nhc = a.G / a.hpw;
     const int per = a.B * a.Hkv * nhc;
     const int t = blockIdx.x / per;
     int r = blockIdx.x % per;
-    QTile c;
-    c.qt = causal ? a.nqt - 1 - t : t;
-    const int hc = r % nhc;
+    QTileWork w;
+    w.hc = r % nhc;
     r /= nhc;
-    c.g = r % a.Hkv;
-    c.b = r / a.Hkv;
-    c.h = c.g * a.G + hc * a.hpw + wave / a.rb;
-    c.r0 = c.qt * 32 * a.rb + (wave % a.rb) * 32;
+    w.g = r % a.Hkv;
+    w.b = r / a.Hkv;
+    // Longest tile first under a causal mask (the order is immaterial otherwise).
+    w.qt0 = a.nqt - 1 - t;
+    w.qt1 = a.paired && t < w.qt0 ? t : -1;
+    return w;
+}
+
+__device__ __forceinline__ QTile qtile_of(const Args &a, const QTileWork &w, int qt, int wave) {
+    QTile c;
+    c.b = w.b;
+    c.g = w.g;
+    c.qt = qt;
+    c.h = w.g * a.G + w.hc * a.hpw + wave / a.rb;
+    c.r0 = qt * 32 * a.rb + (wave % a.rb) * 32;
     return c;
 }
 
@@ -174,47 +191,65 @@ __device__ __forceinline__ void load_row_half(float (&dst)[Cfg<D>::NS], const fl
     }
 }
 
+// acc += sum_st A[st] * x[st], with A[st] = a[st] read from LDS in 16-byte groups: a chain of NS
+// dependent MFMAs over one row of a tile.  The reads are software-pipelined: group g+1 is
+// requested before the four MFMAs of group g are issued, and sched_barrier keeps the compiler
+// from sinking the read back next to its use, so LDS latency hides behind the matrix core.
+template <int NS>
+__device__ __forceinline__ f32x16 chain_lds4(const float *a, const float (&x)[NS], f32x16 acc) {
+    f32x4 cur = ld4(a);
+#pragma unroll
+    for (int g = 0; g < NS / 4; ++g) {
+        f32x4 nxt = cur;
+        if (g + 1 < NS / 4) nxt = ld4(a + 4 * (g + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32(cur[0], x[4 * g + 0], acc);
+        acc = mfma32(cur[1], x[4 * g + 1], acc);
+        acc = mfma32(cur[2], x[4 * g + 2], acc);
+        acc = mfma32(cur[3], x[4 * g + 3], acc);
+        cur = nxt;
+    }
+    return acc;
+}
+
 // S^T tile (32 keys x 32 queries) = K_tile (LDS, padded rows) x this wave's query rows (regs).
 template <int D>
 __device__ __forceinline__ f32x16 scores_t(const float *K, const float (&x)[Cfg<D>::NS], int col,
                                            int half) {
     using C = Cfg<D>;
-    f32x16 s = zero16();
-#pragma unroll
-    for (int st = 0; st < C::NS; st += 4) {
-        const f32x4 kk = ld4(K + col * C::LD + C::NS * half + st);
-        s = mfma32(kk[0], x[st + 0], s);
-        s = mfma32(kk[1], x[st + 1], s);
-        s = mfma32(kk[2], x[st + 2], s);
-        s = mfma32(kk[3], x[st + 3], s);
-    }
-    return s;
+    return chain_lds4<C::NS>(K + col * C::LD + C::NS * half, x, zero16());
 }
 
 // acc (D x 32 queries, transposed) += M_tile^T (D x 32 keys) * X (32 keys x 32 queries), with
-// X the accumulator-layout tile in registers and M_tile the LDS tile [key][d].
+// X the accumulator-layout tile in registers and M_tile the LDS tile [key][d].  Step st reads
+// row acc_row(st, half); the reads of step st+1 are issued ahead of the MFMAs of step st.
 template <int D>
 __device__ __forceinline__ void accum_t(f32x16 (&acc)[Cfg<D>::ND], const float *M, const f32x16 &x,
                                         int col, int half) {
     using C = Cfg<D>;
+    float cur[C::ND], nxt[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) cur[dd] = M[acc_row(0, half) * C::LD + dd * 32 + col];
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
-        const int key = acc_row(st, half);
 #pragma unroll
-        for (int dd = 0; dd < C::ND; ++dd) acc[dd] = mfma32(M[key * C::LD + dd * 32 + col], x[st], acc[dd]);
+        for (int dd = 0; dd < C::ND; ++dd)
+            nxt[dd] = st + 1 < 16 ? M[acc_row(st + 1, half) * C::LD + dd * 32 + col] : cur[dd];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd) acc[dd] = mfma32(cur[dd], x[st], acc[dd]);
+#pragma unroll
+        for (int dd = 0; dd < C::ND; ++dd) cur[dd] = nxt[dd];
     }
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_FWD_WAVES_PER_EU)))
-fwd_f32(Args a) {
+__device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&sK)[2][32 * Cfg<D>::LD],
+                                         float (&sV)[2][32 * Cfg<D>::LD]) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) float sK[2][32 * C::LD];
-    __shared__ __attribute__((aligned(16))) float sV[2][32 * C::LD];
     const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
-    const QTile c = decode_qtile(a, CAUSAL, wave);
     const int T = a.T;
     const int qrow = c.r0 + col;
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
@@ -289,15 +324,26 @@ fwd_f32(Args a) {
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_DQ_WAVES_PER_EU)))
-dq_f32(Args a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_FWD_WAVES_PER_EU)))
+fwd_f32(Args a) {
+    __shared__ __attribute__((aligned(16))) float sK[2][32 * Cfg<D>::LD];
+    __shared__ __attribute__((aligned(16))) float sV[2][32 * Cfg<D>::LD];
+    const int wave = threadIdx.x >> 6;
+    const QTileWork w = decode_qwork(a);
+    fwd_tile<D, CAUSAL, ROPE>(a, qtile_of(a, w, w.qt0, wave), sK, sV);
+    if (w.qt1 >= 0) {
+        __syncthreads();
+        fwd_tile<D, CAUSAL, ROPE>(a, qtile_of(a, w, w.qt1, wave), sK, sV);
+    }
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&sK)[2][32 * Cfg<D>::LD],
+                                        float (&sV)[2][32 * Cfg<D>::LD]) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) float sK[2][32 * C::LD];
-    __shared__ __attribute__((aligned(16))) float sV[2][32 * C::LD];
     const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
-    const QTile c = decode_qtile(a, CAUSAL, wave);
     const int T = a.T;
     const int qrow = c.r0 + col;
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
@@ -377,23 +423,31 @@ dq_f32(Args a) {
     }
 }
 
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_DQ_WAVES_PER_EU)))
+dq_f32(Args a) {
+    __shared__ __attribute__((aligned(16))) float sK[2][32 * Cfg<D>::LD];
+    __shared__ __attribute__((aligned(16))) float sV[2][32 * Cfg<D>::LD];
+    const int wave = threadIdx.x >> 6;
+    const QTileWork w = decode_qwork(a);
+    dq_tile<D, CAUSAL, ROPE>(a, qtile_of(a, w, w.qt0, wave), sK, sV);
+    if (w.qt1 >= 0) {
+        __syncthreads();
+        dq_tile<D, CAUSAL, ROPE>(a, qtile_of(a, w, w.qt1, wave), sK, sV);
+    }
+}
+
 // Floats of LDS per dK/dV wave: a query tile and a dO tile (32 padded rows each), lse2, delta.
 template <int D>
 constexpr int dkdv_wave_floats() { return 2 * 32 * Cfg<D>::LD + 64; }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_DKDV_WAVES_PER_EU)))
-dkdv_f32(Args a) {
+__device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, float *smem) {
     using C = Cfg<D>;
-    extern __shared__ __attribute__((aligned(16))) float smem[];
     const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
-    const int per = a.B * a.Hkv;
-    const int kb = blockIdx.x / per;  // ascending: the first key blocks see the most queries
-    const int g = (blockIdx.x % per) % a.Hkv;
-    const int b = (blockIdx.x % per) / a.Hkv;
     const size_t bg = (size_t)b * a.Hkv + g;
     const int krow = kb * 32 + col;
 
@@ -462,15 +516,7 @@ dkdv_f32(Args a) {
         __builtin_amdgcn_wave_barrier();
 
         // S = Q K'^T (rows: queries acc_row(v, half) of the block; column: this lane's key)
-        f32x16 p = zero16();
-#pragma unroll
-        for (int st = 0; st < C::NS; st += 4) {
-            const f32x4 qq = ld4(sQ + col * C::LD + C::NS * half + st);
-            p = mfma32(qq[0], kr[st + 0], p);
-            p = mfma32(qq[1], kr[st + 1], p);
-            p = mfma32(qq[2], kr[st + 2], p);
-            p = mfma32(qq[3], kr[st + 3], p);
-        }
+        f32x16 p = chain_lds4<C::NS>(sQ + col * C::LD + C::NS * half, kr, zero16());
         // P = exp2(S - lse2): independent of the dP chain below, so the two can overlap.
         const bool diag = CAUSAL && i == kb;
 #pragma unroll
@@ -484,22 +530,9 @@ dkdv_f32(Args a) {
             }
         }
         // dP = dO V^T
-        f32x16 ds = zero16();
-#pragma unroll
-        for (int st = 0; st < C::NS; st += 4) {
-            const f32x4 oo = ld4(sO + col * C::LD + C::NS * half + st);
-            ds = mfma32(oo[0], vr[st + 0], ds);
-            ds = mfma32(oo[1], vr[st + 1], ds);
-            ds = mfma32(oo[2], vr[st + 2], ds);
-            ds = mfma32(oo[3], vr[st + 3], ds);
-        }
+        f32x16 ds = chain_lds4<C::NS>(sO + col * C::LD + C::NS * half, vr, zero16());
         // dV^T += dO^T P  (needs only P, so it can run while dS is formed)
-#pragma unroll
-        for (int st = 0; st < 16; ++st) {
-            const int r = acc_row(st, half);
-#pragma unroll
-            for (int dd = 0; dd < C::ND; ++dd) dv[dd] = mfma32(sO[r * C::LD + dd * 32 + col], p[st], dv[dd]);
-        }
+        accum_t<D>(dv, sO, p, col, half);
         // dS = P (dP - delta)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -508,12 +541,7 @@ dkdv_f32(Args a) {
             for (int e = 0; e < 4; ++e) ds[4 * u + e] = p[4 * u + e] * (ds[4 * u + e] - Dl[e]);
         }
         // dK^T += Q^T dS
-#pragma unroll
-        for (int st = 0; st < 16; ++st) {
-            const int r = acc_row(st, half);
-#pragma unroll
-            for (int dd = 0; dd < C::ND; ++dd) dk[dd] = mfma32(sQ[r * C::LD + dd * 32 + col], ds[st], dk[dd]);
-        }
+        accum_t<D>(dk, sQ, ds, col, half);
     }
 
     // Add the waves' partial dK, dV in LDS (wave order fixed) and write them out.
@@ -551,6 +579,22 @@ dkdv_f32(Args a) {
     }
 }
 
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_DKDV_WAVES_PER_EU)))
+dkdv_f32(Args a) {
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int per = a.B * a.Hkv;
+    const int p = blockIdx.x / per;
+    const int g = (blockIdx.x % per) % a.Hkv;
+    const int b = (blockIdx.x % per) / a.Hkv;
+    // Causal: key blocks p and nkb-1-p (the first sees the most queries, the second the fewest).
+    dkdv_block<D, CAUSAL, ROPE>(a, b, g, p, smem);
+    if (a.paired && a.nkb - 1 - p > p) {
+        __syncthreads();
+        dkdv_block<D, CAUSAL, ROPE>(a, b, g, a.nkb - 1 - p, smem);
+    }
+}
+
 Args make_args(const Shape &s) {
     Args a{};
     a.B = s.B;
@@ -583,7 +627,7 @@ hipError_t launch(const void *fn, long long blocks, int threads, size_t lds, hip
 
 }  // namespace
 
-QTileGeom qtile_geometry(const Shape &s) {
+QTileGeom qtile_geometry(const Shape &s, bool pair) {
     QTileGeom g{};
     g.hpw = 1;
     for (int d = 8; d >= 1; --d)
@@ -595,15 +639,17 @@ QTileGeom qtile_geometry(const Shape &s) {
     g.nwaves = g.hpw * g.rb;
     g.rows = 32 * g.rb;
     g.nqt = (s.T + g.rows - 1) / g.rows;
-    g.nblocks = (long long)s.B * s.Hkv * (s.G / g.hpw) * g.nqt;
+    g.paired = pair ? 1 : 0;
+    g.nblocks = (long long)s.B * s.Hkv * (s.G / g.hpw) * (g.paired ? (g.nqt + 1) / 2 : g.nqt);
     return g;
 }
 
-KBlockGeom kblock_geometry(const Shape &s) {
+KBlockGeom kblock_geometry(const Shape &s, bool pair) {
     KBlockGeom g{};
     g.nwaves = 4;
     g.nkb = (s.T + 31) / 32;
-    g.nblocks = (long long)s.B * s.Hkv * g.nkb;
+    g.paired = pair ? 1 : 0;
+    g.nblocks = (long long)s.B * s.Hkv * (g.paired ? (g.nkb + 1) / 2 : g.nkb);
     return g;
 }
 
@@ -615,10 +661,11 @@ hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const 
     a.v = v;
     a.out_o = o;
     a.out_lse = lse;
-    const QTileGeom g = qtile_geometry(s);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.fwd);
     a.hpw = g.hpw;
     a.rb = g.rb;
     a.nqt = g.nqt;
+    a.paired = g.paired;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
     const void *fn = s.D == 64 ? pick_fwd_f32<64>(causal, rope) : pick_fwd_f32<32>(causal, rope);
     return launch(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
@@ -636,10 +683,11 @@ hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const f
     a.dO = dO;
     a.dq = dq;
     a.delta = delta;
-    const QTileGeom g = qtile_geometry(s);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.dq);
     a.hpw = g.hpw;
     a.rb = g.rb;
     a.nqt = g.nqt;
+    a.paired = g.paired;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
     const void *fn = s.D == 64 ? pick_dq_f32<64>(causal, rope) : pick_dq_f32<32>(causal, rope);
     return launch(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
@@ -657,8 +705,9 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
     a.dk = dk;
     a.dv = dv;
     a.delta = const_cast<float *>(delta);  // read only in this pass
-    const KBlockGeom g = kblock_geometry(s);
-    a.kw = g.nwaves;
+    const KBlockGeom g = kblock_geometry(s, s.causal && kPairF32.dkdv);
+    a.paired = g.paired;
+    a.nkb = g.nkb;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
     const size_t lds = (size_t)g.nwaves *
                        (s.D == 64 ? dkdv_wave_floats<64>() : dkdv_wave_floats<32>()) * sizeof(float);

@@ -16,22 +16,47 @@ struct Shape {
 // Work-group composition of the query-tile kernels (forward and dQ): each work-group serves
 // `hpw` query heads of one key/value head and `rb` 32-row blocks per head, i.e. hpw * rb waves,
 // all sharing each K/V tile staged in LDS.
+//
+// With a causal mask the work of a query tile grows with its position.  With `pair` set,
+// work-groups take a mirrored pair of tiles (qt and nqt-1-qt, one after the other), so every
+// work-group does the same work and a single round of work-groups fills the GPU evenly.
 struct QTileGeom {
     int hpw, rb, nwaves, rows;  // rows = 32 * rb query rows per head
     int nqt;                    // query tiles per head
+    int paired;                 // work-groups take mirrored tile pairs
     long long nblocks;
 };
 
-QTileGeom qtile_geometry(const Shape &s);
+QTileGeom qtile_geometry(const Shape &s, bool pair);
 
-// Key-block kernel (dK/dV): one work-group per (b, kv head, 32-key block), `nwaves` waves that
-// split the group's query heads between them and reduce their partial sums in LDS.
+// Key-block kernel (dK/dV): one work-group per (b, kv head, 32-key block) -- per mirrored pair
+// of key blocks with `pair` set -- with `nwaves` waves that split the group's (query head, query
+// block) items between them and add their partial sums in LDS.
 struct KBlockGeom {
     int nwaves, nkb;
+    int paired;
     long long nblocks;
 };
 
-KBlockGeom kblock_geometry(const Shape &s);
+KBlockGeom kblock_geometry(const Shape &s, bool pair);
+
+// Which passes take mirrored pairs under a causal mask (measured per pass and dtype).  Pairing
+// evens out the work per work-group, but a compute unit favours its oldest waves, so equal
+// work-groups still finish at staggered times; once none is left to dispatch the unit drains
+// at low occupancy.  Unpaired launches, longest tile first, keep more work-groups in flight and
+// win where the grid is several times the resident capacity (the fp32 forward at long
+// sequences, and the bf16 passes); pairing wins for the fp32 backward passes.
+#ifndef NE_PAIR_F32
+#define NE_PAIR_F32 0, 1, 1  // forward, dQ, dK/dV
+#endif
+#ifndef NE_PAIR_BF16
+#define NE_PAIR_BF16 0, 0, 0
+#endif
+struct PairPolicy {
+    int fwd, dq, dkdv;
+};
+constexpr PairPolicy kPairF32{NE_PAIR_F32};
+constexpr PairPolicy kPairBf16{NE_PAIR_BF16};
 
 hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const float *v,
                           float *o, float *lse, hipStream_t st);

@@ -32,8 +32,9 @@ int check_shape(int B, int Hq, int Hkv, int T, int D, int causal, int dtype, flo
     s.G = Hq / Hkv;
     s.causal = causal != 0;
     s.rope_base = rope_base;
-    const ne::QTileGeom gq = ne::qtile_geometry(s);
-    const ne::KBlockGeom gk = ne::kblock_geometry(s);
+    // Unpaired launches have the most work-groups.
+    const ne::QTileGeom gq = ne::qtile_geometry(s, false);
+    const ne::KBlockGeom gk = ne::kblock_geometry(s, false);
     if (gq.nblocks > 0x7fffffffLL || gk.nblocks > 0x7fffffffLL) return NE_ERR_SHAPE;
     return NE_OK;
 }
