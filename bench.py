@@ -142,20 +142,20 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev)
     c, rb = w.causal, w.rope_base
+    ws = ne.workspace(q, k, rb)
     names = ("fwd", "bwd_dq", "bwd_dkdv")
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        ne.ne_attn_fwd_ex(q, k, v, o, lse, causal=c, rope_base=rb)
+        ne.ne_attn_fwd_ex(q, k, v, o, lse, ws, causal=c, rope_base=rb)
         if ev is not None:
             ev[1].record()
-        ne.ne_attn_bwd_dq_ex(q, k, v, o, lse, dO, dq, delta, causal=c, rope_base=rb)
+        ne.ne_attn_bwd_dq_ex(q, k, v, o, lse, dO, dq, ws, causal=c, rope_base=rb)
         if ev is not None:
             ev[2].record()
-        ne.ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, delta, dk, dv, causal=c, rope_base=rb)
+        ne.ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, ws, dk, dv, causal=c, rope_base=rb)
         if ev is not None:
             ev[3].record()
 

@@ -1,13 +1,14 @@
 """Python binding of ``libne_attn.so``: causal grouped-query FlashAttention for MI355X (gfx950).
 
 The functions named like the C entry points (``ne_attn_fwd``, ``ne_attn_bwd``,
-``ne_attn_fwd_ex``, ``ne_attn_bwd_ex``, ``ne_attn_bwd_workspace_bytes``, ``ne_attn_strerror``)
-only marshal arguments: they read sizes from tensor shapes, pass ``data_ptr()`` and the current
+``ne_attn_fwd_ex``, ``ne_attn_bwd_ex``, ``ne_attn_bwd_dq_ex``, ``ne_attn_bwd_dkdv_ex``,
+``ne_attn_workspace_bytes``, ``ne_attn_bwd_workspace_bytes``, ``ne_attn_strerror``) only
+marshal arguments: they read sizes from tensor shapes, pass ``data_ptr()`` and the current
 HIP stream, and raise ``NeAttnError`` on a non-zero status.  All arithmetic happens in the HIP
 kernels.  PyTorch provides device memory and streams.
 
-``forward`` and ``backward`` are conveniences that allocate the outputs with torch and call the
-entry points.
+``forward`` and ``backward`` are conveniences that allocate the outputs and the workspace with
+torch and call the entry points.
 
 Tensor layout: q, o, dO, dq: [B, Hq, T, D]; k, v, dk, dv: [B, Hkv, T, D]; lse: [B, Hq, T]
 float32; all contiguous on one GPU; float32, or bfloat16 through the ``_ex`` entry points.
@@ -21,8 +22,8 @@ __all__ = [
     "NeAttnError", "library_path", "load", "lib",
     "ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
     "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex",
-    "ne_attn_bwd_workspace_bytes", "ne_attn_strerror",
-    "forward", "backward",
+    "ne_attn_workspace_bytes", "ne_attn_bwd_workspace_bytes", "ne_attn_strerror",
+    "forward", "backward", "workspace",
     "NE_OK", "NE_ERR_NULL", "NE_ERR_SHAPE", "NE_ERR_UNSUPPORTED", "NE_ERR_ALIGN", "NE_ERR_HIP",
     "NE_F32", "NE_BF16", "EXPORTED_SYMBOLS",
 ]
@@ -31,7 +32,7 @@ NE_OK, NE_ERR_NULL, NE_ERR_SHAPE, NE_ERR_UNSUPPORTED, NE_ERR_ALIGN, NE_ERR_HIP =
 NE_F32, NE_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-                    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex",
+                    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_workspace_bytes",
                     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -65,13 +66,15 @@ def load():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.ne_attn_fwd.argtypes = [vp] * 5 + [i] * 6 + [vp]
     L.ne_attn_bwd.argtypes = [vp] * 10 + [i] * 6 + [vp]
-    L.ne_attn_fwd_ex.argtypes = [vp] * 5 + [i] * 7 + [f, vp]
+    L.ne_attn_fwd_ex.argtypes = [vp] * 6 + [i] * 7 + [f, vp]
     L.ne_attn_bwd_ex.argtypes = [vp] * 10 + [i] * 7 + [f, vp]
     L.ne_attn_bwd_dq_ex.argtypes = [vp] * 8 + [i] * 7 + [f, vp]
     L.ne_attn_bwd_dkdv_ex.argtypes = [vp] * 8 + [i] * 7 + [f, vp]
     for name in ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
                  "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex"):
         getattr(L, name).restype = i
+    L.ne_attn_workspace_bytes.argtypes = [i] * 6 + [f]
+    L.ne_attn_workspace_bytes.restype = ctypes.c_size_t
     L.ne_attn_bwd_workspace_bytes.argtypes = [i, i, i]
     L.ne_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.ne_attn_strerror.argtypes = [i]
@@ -90,6 +93,12 @@ def ne_attn_strerror(status: int) -> str:
 
 def ne_attn_bwd_workspace_bytes(B: int, Hq: int, T: int) -> int:
     return int(load().ne_attn_bwd_workspace_bytes(int(B), int(Hq), int(T)))
+
+
+def ne_attn_workspace_bytes(B: int, Hq: int, Hkv: int, T: int, D: int, dtype: int,
+                            rope_base: float = 0.0) -> int:
+    return int(load().ne_attn_workspace_bytes(int(B), int(Hq), int(Hkv), int(T), int(D),
+                                              int(dtype), float(rope_base)))
 
 
 # ----------------------------------------------------------------------------- marshalling
@@ -143,7 +152,16 @@ def _raise(rc, where):
         raise NeAttnError(rc, where)
 
 
-def ne_attn_fwd_ex(q, k, v, o, lse, causal: bool = True, rope_base: float = 0.0, stream=None):
+def _ws_check(ws, need, dev, name="workspace"):
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"{name} must hold at least {need} bytes")
+    _check_tensors({name: ws}, dev)
+
+
+def ne_attn_fwd_ex(q, k, v, o, lse, workspace=None, causal: bool = True, rope_base: float = 0.0,
+                   stream=None):
+    """workspace: a device tensor of at least ne_attn_workspace_bytes(...) bytes; may be None
+    without RoPE."""
     torch = _torch()
     B, Hq, Hkv, T, D = _dims(q, k, v)
     dt = _dtype_code(q)
@@ -153,8 +171,13 @@ def ne_attn_fwd_ex(q, k, v, o, lse, causal: bool = True, rope_base: float = 0.0,
     if o.shape != q.shape or tuple(lse.shape) != (B, Hq, T) or lse.dtype != torch.float32:
         raise ValueError("o must match q; lse must be float32 [B, Hq, T]")
     _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse), q.device)
+    if workspace is not None:
+        _ws_check(workspace, ne_attn_workspace_bytes(B, Hq, Hkv, T, D, dt, rope_base), q.device)
+    elif rope_base > 0:
+        raise ValueError("the forward with RoPE needs a workspace")
+    ws = _p(workspace) if workspace is not None else None
     with torch.cuda.device(q.device):
-        rc = load().ne_attn_fwd_ex(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, T, D,
+        rc = load().ne_attn_fwd_ex(_p(q), _p(k), _p(v), _p(o), _p(lse), ws, B, Hq, Hkv, T, D,
                                    int(bool(causal)), dt, float(rope_base),
                                    _stream(stream, q.device))
     _raise(rc, "ne_attn_fwd_ex")
@@ -175,7 +198,9 @@ def ne_attn_fwd(q, k, v, o, lse, causal: bool = True, stream=None):
     _raise(rc, "ne_attn_fwd")
 
 
-def _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, delta_ws):
+def _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, ws, rope_base=None):
+    """rope_base None: ws is the float32 delta workspace of ne_attn_bwd; otherwise the
+    workspace of the _ex entry points for that RoPE setting."""
     torch = _torch()
     B, Hq, Hkv, T, D = _dims(q, k, v)
     for name, t in (("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk),
@@ -188,20 +213,24 @@ def _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, delta_ws):
         raise ValueError("dk, dv must match k")
     if tuple(lse.shape) != (B, Hq, T) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [B, Hq, T]")
-    if delta_ws.dtype != torch.float32 or delta_ws.numel() * 4 < ne_attn_bwd_workspace_bytes(B, Hq, T):
-        raise ValueError("delta_ws must be float32 with at least B*Hq*T elements")
-    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv,
-                        delta_ws=delta_ws), q.device)
+    if rope_base is None:
+        if ws.dtype != torch.float32 or ws.numel() * 4 < ne_attn_bwd_workspace_bytes(B, Hq, T):
+            raise ValueError("delta_ws must be float32 with at least B*Hq*T elements")
+    else:
+        _ws_check(ws, ne_attn_workspace_bytes(B, Hq, Hkv, T, D, _dtype_code(q), rope_base),
+                  q.device)
+    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv, ws=ws),
+                   q.device)
     return B, Hq, Hkv, T, D
 
 
-def ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal: bool = True,
+def ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal: bool = True,
                    rope_base: float = 0.0, stream=None):
     torch = _torch()
-    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, delta_ws)
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, workspace, rope_base)
     with torch.cuda.device(q.device):
         rc = load().ne_attn_bwd_ex(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq), _p(dk),
-                                   _p(dv), _p(delta_ws), B, Hq, Hkv, T, D, int(bool(causal)),
+                                   _p(dv), _p(workspace), B, Hq, Hkv, T, D, int(bool(causal)),
                                    _dtype_code(q), float(rope_base), _stream(stream, q.device))
     _raise(rc, "ne_attn_bwd_ex")
 
@@ -218,25 +247,25 @@ def ne_attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal: bool = True, 
     _raise(rc, "ne_attn_bwd")
 
 
-def ne_attn_bwd_dq_ex(q, k, v, o, lse, dO, dq, delta_ws, causal: bool = True,
+def ne_attn_bwd_dq_ex(q, k, v, o, lse, dO, dq, workspace, causal: bool = True,
                       rope_base: float = 0.0, stream=None):
-    """First backward pass: writes dq and delta_ws."""
+    """First backward pass: writes dq and fills the workspace."""
     torch = _torch()
-    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, k, v, delta_ws)
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, k, v, workspace, rope_base)
     with torch.cuda.device(q.device):
         rc = load().ne_attn_bwd_dq_ex(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
-                                      _p(delta_ws), B, Hq, Hkv, T, D, int(bool(causal)),
+                                      _p(workspace), B, Hq, Hkv, T, D, int(bool(causal)),
                                       _dtype_code(q), float(rope_base), _stream(stream, q.device))
     _raise(rc, "ne_attn_bwd_dq_ex")
 
 
-def ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, delta_ws, dk, dv, causal: bool = True,
+def ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, workspace, dk, dv, causal: bool = True,
                         rope_base: float = 0.0, stream=None):
-    """Second backward pass: reads delta_ws (from the dq pass), writes dk and dv."""
+    """Second backward pass: reads the workspace filled by the dq pass, writes dk and dv."""
     torch = _torch()
-    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, dO, lse, dO, dO, dk, dv, delta_ws)
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, dO, lse, dO, dO, dk, dv, workspace, rope_base)
     with torch.cuda.device(q.device):
-        rc = load().ne_attn_bwd_dkdv_ex(_p(q), _p(k), _p(v), _p(lse), _p(dO), _p(delta_ws),
+        rc = load().ne_attn_bwd_dkdv_ex(_p(q), _p(k), _p(v), _p(lse), _p(dO), _p(workspace),
                                         _p(dk), _p(dv), B, Hq, Hkv, T, D, int(bool(causal)),
                                         _dtype_code(q), float(rope_base),
                                         _stream(stream, q.device))
@@ -245,22 +274,33 @@ def ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, delta_ws, dk, dv, causal: bool = True,
 
 # ----------------------------------------------------------------------------- conveniences
 
+def workspace(q, k, rope_base: float = 0.0):
+    """Allocates a workspace for the _ex entry points on the tensors' device."""
+    torch = _torch()
+    B, Hq, T, D = q.shape
+    n = ne_attn_workspace_bytes(B, Hq, k.shape[1], T, D, _dtype_code(q), rope_base)
+    if n == 0:
+        raise ValueError("invalid shape for a workspace")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
 def forward(q, k, v, causal: bool = True, rope_base: float = 0.0, stream=None):
-    """Allocates o and lse and runs the forward pass; returns (o, lse)."""
+    """Allocates o, lse (and with RoPE the workspace) and runs the forward pass; returns
+    (o, lse)."""
     torch = _torch()
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    ne_attn_fwd_ex(q, k, v, o, lse, causal=causal, rope_base=rope_base, stream=stream)
+    ws = workspace(q, k, rope_base) if rope_base > 0 else None
+    ne_attn_fwd_ex(q, k, v, o, lse, ws, causal=causal, rope_base=rope_base, stream=stream)
     return o, lse
 
 
 def backward(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0, stream=None):
-    """Allocates dq, dk, dv and the delta workspace and runs the backward pass."""
+    """Allocates dq, dk, dv and the workspace and runs the backward pass."""
     torch = _torch()
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, delta, causal=causal, rope_base=rope_base,
-                   stream=stream)
+    ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, rope_base), causal=causal,
+                   rope_base=rope_base, stream=stream)
     return dq, dk, dv

@@ -19,6 +19,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
 
@@ -163,24 +165,20 @@ __device__ __forceinline__ QTileB qtile_of_b(const ArgsB &a, const QWorkB &w, in
 
 // Staging of BN-row K and V tiles: HBM -> registers (issued one tile ahead) -> swizzled LDS.
 // A tile is moved in 1 KB pieces, one wave-wide 16-byte load per piece; piece c goes to wave
-// c % nw, so every branch on the piece index is uniform across the wave, and each lane always
-// moves the same column chunk (its RoPE rates are computed once).
-template <int D, bool ROPE>
+// c % nw, so every branch on the piece index is uniform across the wave.  With RoPE the keys
+// arrive already rotated.
+template <int D>
 struct KVStagerB {
     using C = CfgB<D>;
     static constexpr int RPP = 64 / C::NCH;            // rows per 1 KB piece
     static constexpr int NP = C::BN / RPP;             // pieces per tile
     static constexpr int MAXP = (NP + 1) / 2;          // per wave (query-tile groups have >= 2 waves)
     bf16x8 k[MAXP], v[MAXP];
-    float rates[4];
     int ch, rsub;
 
-    __device__ __forceinline__ void init(int lane, float lb) {
+    __device__ __forceinline__ void init(int lane) {
         ch = lane % C::NCH;
         rsub = lane / C::NCH;
-        if (ROPE)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) rates[p] = rope_rate<D>(4 * ch + p, lb);
     }
     __device__ __forceinline__ void load(const __bf16 *kg, const __bf16 *vg, int tile, int T,
                                          int wave, int nw) {
@@ -203,14 +201,7 @@ struct KVStagerB {
             if (pc < NP) {
                 const int r = pc * RPP + rsub;
                 const int row = tile * C::BN + r;
-                bf16x8 kk = k[i];
-                if (ROPE) {
-                    float x[8];
-                    unpack8(kk, x);
-                    rope_rotate<8>(x, row, rates, false);
-                    kk = round8(x);
-                }
-                *reinterpret_cast<bf16x8 *>(sK + tile_off<D>(r, 8 * ch)) = row < T ? kk : zero;
+                *reinterpret_cast<bf16x8 *>(sK + tile_off<D>(r, 8 * ch)) = row < T ? k[i] : zero;
                 *reinterpret_cast<bf16x8 *>(sV + tile_off<D>(r, 8 * ch)) = row < T ? v[i] : zero;
             }
         }
@@ -282,8 +273,8 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c,
     const int wg_end = min(c.qt * wg_rows + wg_rows, T);
     const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
 
-    KVStagerB<D, ROPE> stg;
-    stg.init(lane, a.rope_lb);
+    KVStagerB<D> stg;
+    stg.init(lane);
     stg.load(kg, vg, 0, T, wave, nw);
     stg.store(sK[0], sV[0], 0, T, wave, nw);
     __syncthreads();
@@ -391,7 +382,7 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c,
     const __bf16 *vg = a.v + bg * T * D;
 
     bf16x8 qv[C::KS], dov[C::KS];
-    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
+    load_operand_row<D, false>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
     load_operand_row<D, false>(dov, a.dO + bh * T * D, qrow, T, half, 0.f);
 
     // delta_i = sum_d dO_id o_id over this row (fp32), written once for the dK/dV pass.
@@ -423,8 +414,8 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c,
     const int wg_end = min(c.qt * wg_rows + wg_rows, T);
     const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
 
-    KVStagerB<D, ROPE> stg;
-    stg.init(lane, a.rope_lb);
+    KVStagerB<D> stg;
+    stg.init(lane);
     stg.load(kg, vg, 0, T, wave, nw);
     stg.store(sK[0], sV[0], 0, T, wave, nw);
     __syncthreads();
@@ -501,7 +492,7 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     const int krow = kb * 32 + col;
 
     bf16x8 kv[C::KS], vv[C::KS];
-    load_operand_row<D, ROPE>(kv, a.k + bg * T * D, krow, T, half, a.rope_lb);
+    load_operand_row<D, false>(kv, a.k + bg * T * D, krow, T, half, a.rope_lb);
     load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, 0.f);
 
     f32x16 dk[C::ND], dv[C::ND];
@@ -526,10 +517,6 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     // the query tile and of the dO tile, held in registers one item ahead.
     constexpr int PC = 32 * C::NCH / 64;
     const int sch = lane % C::NCH;  // fixed column chunk of this lane
-    float rates[4];
-    if (ROPE)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) rates[p] = rope_rate<D>(4 * sch + p, a.rope_lb);
     bf16x8 pq[PC], pd[PC];
     float plse = 0.f, pdl = 0.f;
     auto prefetch = [&](int it) {
@@ -557,14 +544,7 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
             for (int pc = 0; pc < PC; ++pc) {
                 const int r = (lane + 64 * pc) / C::NCH;
                 const int row = i * 32 + r;
-                bf16x8 qq = pq[pc];
-                if (ROPE) {
-                    float x[8];
-                    unpack8(qq, x);
-                    rope_rotate<8>(x, row, rates, false);
-                    qq = round8(x);
-                }
-                *reinterpret_cast<bf16x8 *>(sQ + tile_off<D>(r, 8 * sch)) = row < T ? qq : zero;
+                *reinterpret_cast<bf16x8 *>(sQ + tile_off<D>(r, 8 * sch)) = row < T ? pq[pc] : zero;
                 *reinterpret_cast<bf16x8 *>(sO + tile_off<D>(r, 8 * sch)) = row < T ? pd[pc] : zero;
             }
             if (lane < 32) {
@@ -661,6 +641,38 @@ dkdv_bf16(ArgsB a) {
     }
 }
 
+// RoPE applied once to a whole bf16 tensor [BH][T][D] (the position of a row is its t), in fp32
+// with the angle reduced modulo one turn in double precision, rounded once to bf16.  Each thread
+// owns one (position, 8-column chunk): it evaluates the four sines and cosines once and applies
+// them to the rows of every (batch, head) it visits.  The attention kernels that stream a tensor
+// through LDS many times read this rotated copy.
+template <int D>
+__global__ void __launch_bounds__(256) rope_rows_bf16(const __bf16 *x, __bf16 *y, long long nbh, int T,
+                                                      RopeTurns rt) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= T * (D / 8)) return;
+    const int t = idx / (D / 8);
+    const int c = 8 * (idx % (D / 8));
+    float sn[4], cs[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const double turns = (double)t * rt.per_pos[c / 2 + p];
+        sincospif(2.0f * (float)(turns - rint(turns)), &sn[p], &cs[p]);
+    }
+    for (long long bh = blockIdx.y; bh < nbh; bh += gridDim.y) {
+        const size_t off = ((size_t)bh * T + t) * D + c;
+        float f[8];
+        unpack8(*reinterpret_cast<const bf16x8 *>(x + off), f);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float u = f[2 * p], w = f[2 * p + 1];
+            f[2 * p] = u * cs[p] - w * sn[p];
+            f[2 * p + 1] = u * sn[p] + w * cs[p];
+        }
+        *reinterpret_cast<bf16x8 *>(y + off) = round8(f);
+    }
+}
+
 ArgsB make_args_b(const Shape &s) {
     ArgsB a{};
     a.B = s.B;
@@ -706,7 +718,7 @@ hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const v
     a.v = static_cast<const __bf16 *>(v);
     a.out_o = static_cast<__bf16 *>(o);
     a.out_lse = lse;
-    const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.fwd);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.fwd != 0);
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
     const void *fn = s.D == 64 ? pick_fwd_bf16<64>(causal, rope) : pick_fwd_bf16<32>(causal, rope);
@@ -725,7 +737,7 @@ hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const vo
     a.dO = static_cast<const __bf16 *>(dO);
     a.dq = static_cast<__bf16 *>(dq);
     a.delta = delta;
-    const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.dq);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.dq != 0);
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
     const void *fn = s.D == 64 ? pick_dq_bf16<64>(causal, rope) : pick_dq_bf16<32>(causal, rope);
@@ -744,12 +756,28 @@ hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const 
     a.delta = const_cast<float *>(delta);  // read only in this pass
     a.dk = static_cast<__bf16 *>(dk);
     a.dv = static_cast<__bf16 *>(dv);
-    const KBlockGeom g = kblock_geometry(s, s.causal && kPairBf16.dkdv);
+    const KBlockGeom g = kblock_geometry(s, s.causal && kPairBf16.dkdv != 0);
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
     const size_t lds = (size_t)g.nwaves * (s.D == 64 ? dkdv_wave_bytes_b<64>() : dkdv_wave_bytes_b<32>());
     const void *fn = s.D == 64 ? pick_dkdv_bf16<64>(causal, rope) : pick_dkdv_bf16<32>(causal, rope);
     return launch_b(fn, g.nblocks, 64 * g.nwaves, lds, st, a);
+}
+
+hipError_t launch_rope_bf16(const Shape &s, const void *x, void *y, long long rows,
+                            hipStream_t st) {
+    const __bf16 *xb = static_cast<const __bf16 *>(x);
+    __bf16 *yb = static_cast<__bf16 *>(y);
+    RopeTurns rt = rope_turns(s);
+    long long nbh = rows / s.T;
+    int T = s.T;
+    const long long per_pos = (long long)T * (s.D / 8);
+    const unsigned gx = (unsigned)((per_pos + 255) / 256);
+    // About 8 (batch, head) rows per thread when that still leaves enough threads.
+    const long long gy = std::max(1LL, std::min(nbh, std::max(nbh / 8, 2048LL / (long long)gx)));
+    const void *fn = s.D == 64 ? (const void *)rope_rows_bf16<64> : (const void *)rope_rows_bf16<32>;
+    void *params[] = {&xb, &yb, &nbh, &T, &rt};
+    return hipLaunchKernel(fn, dim3(gx, (unsigned)std::min(gy, 65535LL)), dim3(256), params, 0, st);
 }
 
 }  // namespace ne

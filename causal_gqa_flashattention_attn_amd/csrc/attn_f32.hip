@@ -26,6 +26,8 @@
 //             so results are reproducible bit for bit.
 #include <math.h>
 
+#include <algorithm>
+
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
 
@@ -138,14 +140,15 @@ __device__ __forceinline__ QTile qtile_of(const Args &a, const QTileWork &w, int
 
 // K and V tiles of 32 rows, staged global -> registers -> LDS (padded rows), double buffered.
 // Rows past the end are loaded from the last row (so every load is unconditional and can stay in
-// flight while the current tile is computed) and replaced by zeros when written to LDS.
-template <int D, bool ROPE>
+// flight while the current tile is computed) and replaced by zeros when written to LDS.  With
+// RoPE the keys arrive already rotated.
+template <int D>
 struct KVStager {
     using C = Cfg<D>;
     f32x4 k[C::MAXC], v[C::MAXC];
 
     __device__ __forceinline__ void load(const float *kg, const float *vg, int tile, int T,
-                                         int wave, int nw, int lane, const RopeArgs &rp) {
+                                         int wave, int nw, int lane) {
         const int c4 = 4 * (lane % C::C4);
 #pragma unroll
         for (int i = 0; i < C::MAXC; ++i) {
@@ -158,7 +161,7 @@ struct KVStager {
         }
     }
     __device__ __forceinline__ void store(float *sK, float *sV, int tile, int T, int wave, int nw,
-                                          int lane, const RopeArgs &rp) {
+                                          int lane) {
         const int c4 = 4 * (lane % C::C4);
         const f32x4 zero{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -167,9 +170,7 @@ struct KVStager {
             if (c < C::CH) {
                 const int r = c * C::RPC + lane / C::C4;
                 const int row = tile * 32 + r;
-                f32x4 kk = k[i];
-                if (ROPE) kk = rope4<D>(kk, row, c4, rp, false);
-                st4(sK + r * C::LD + c4, row < T ? kk : zero);
+                st4(sK + r * C::LD + c4, row < T ? k[i] : zero);
                 st4(sV + r * C::LD + c4, row < T ? v[i] : zero);
             }
         }
@@ -268,14 +269,14 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     const int wg_end = min(c.qt * wg_rows + wg_rows, T);
     const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
 
-    KVStager<D, ROPE> stg;
-    stg.load(kg, vg, 0, T, wave, nw, lane, a.rope);
-    stg.store(sK[0], sV[0], 0, T, wave, nw, lane, a.rope);
+    KVStager<D> stg;
+    stg.load(kg, vg, 0, T, wave, nw, lane);
+    stg.store(sK[0], sV[0], 0, T, wave, nw, lane);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
         const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, T, wave, nw, lane, a.rope);
+        if (more) stg.load(kg, vg, j + 1, T, wave, nw, lane);
         const int k0 = j * 32;
         if (c.r0 < T && (!CAUSAL || k0 <= c.r0 + 31)) {
             f32x16 s = scores_t<D>(sK[buf], qr, col, half);
@@ -304,7 +305,7 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
             for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
             accum_t<D>(acc, sV[buf], s, col, half);
         }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw, lane, a.rope);
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw, lane);
         __syncthreads();
     }
 
@@ -351,7 +352,7 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
     const float *vg = a.v + bg * T * D;
 
     float qr[C::NS], dor[C::NS];
-    load_row_half<D, ROPE>(qr, a.q + bh * T * D, qrow, T, half, a.qscale, a.rope);
+    load_row_half<D, false>(qr, a.q + bh * T * D, qrow, T, half, a.qscale, a.rope);
     load_row_half<D, false>(dor, a.dO + bh * T * D, qrow, T, half, 1.0f, a.rope);
 
     // delta_i = sum_d dO_id o_id over this row; written once per row for the dK/dV pass.
@@ -381,14 +382,14 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
     const int wg_end = min(c.qt * wg_rows + wg_rows, T);
     const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
 
-    KVStager<D, ROPE> stg;
-    stg.load(kg, vg, 0, T, wave, nw, lane, a.rope);
-    stg.store(sK[0], sV[0], 0, T, wave, nw, lane, a.rope);
+    KVStager<D> stg;
+    stg.load(kg, vg, 0, T, wave, nw, lane);
+    stg.store(sK[0], sV[0], 0, T, wave, nw, lane);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
         const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, T, wave, nw, lane, a.rope);
+        if (more) stg.load(kg, vg, j + 1, T, wave, nw, lane);
         const int k0 = j * 32;
         if (c.r0 < T && (!CAUSAL || k0 <= c.r0 + 31)) {
             f32x16 p = scores_t<D>(sK[buf], qr, col, half);
@@ -404,7 +405,7 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
             for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
             accum_t<D>(acc, sK[buf], ds, col, half);  // dQ^T += K^T dS^T
         }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw, lane, a.rope);
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw, lane);
         __syncthreads();
     }
 
@@ -452,7 +453,7 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
     const int krow = kb * 32 + col;
 
     float kr[C::NS], vr[C::NS];
-    load_row_half<D, ROPE>(kr, a.k + bg * T * D, krow, T, half, a.qscale, a.rope);
+    load_row_half<D, false>(kr, a.k + bg * T * D, krow, T, half, a.qscale, a.rope);
     load_row_half<D, false>(vr, a.v + bg * T * D, krow, T, half, 1.0f, a.rope);
 
     f32x16 dk[C::ND], dv[C::ND];
@@ -502,9 +503,7 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
             for (int ch = 0; ch < C::CH; ++ch) {
                 const int r = ch * C::RPC + lane / C::C4;
                 const int row = i * 32 + r;
-                f32x4 q4 = tq[ch];
-                if (ROPE) q4 = rope4<D>(q4, row, c4, a.rope, false);
-                st4(sQ + r * C::LD + c4, row < T ? q4 : zero);
+                st4(sQ + r * C::LD + c4, row < T ? tq[ch] : zero);
                 st4(sO + r * C::LD + c4, row < T ? td[ch] : zero);
             }
             if (lane < 32) {
@@ -595,6 +594,32 @@ dkdv_f32(Args a) {
     }
 }
 
+// RoPE applied once to a whole tensor [BH][T][D] (the position of a row is its t), the angle
+// reduced modulo one turn in double precision.  Each thread owns one (position, 4-column chunk):
+// it evaluates the two sines and cosines once and applies them to the rows of every (batch,
+// head) it visits.  The attention kernels that stream a tensor through LDS many times read this
+// rotated copy instead of rotating every staged tile again.
+template <int D>
+__global__ void __launch_bounds__(256) rope_rows_f32(const float *x, float *y, long long nbh, int T,
+                                                     RopeTurns rt) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= T * (D / 4)) return;
+    const int t = idx / (D / 4);
+    const int c = 4 * (idx % (D / 4));
+    float sn[2], cs[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const double turns = (double)t * rt.per_pos[c / 2 + p];
+        sincospif(2.0f * (float)(turns - rint(turns)), &sn[p], &cs[p]);
+    }
+    for (long long bh = blockIdx.y; bh < nbh; bh += gridDim.y) {
+        const size_t off = ((size_t)bh * T + t) * D + c;
+        const f32x4 v = ld4(x + off);
+        st4(y + off, f32x4{v[0] * cs[0] - v[1] * sn[0], v[0] * sn[0] + v[1] * cs[0],
+                           v[2] * cs[1] - v[3] * sn[1], v[2] * sn[1] + v[3] * cs[1]});
+    }
+}
+
 Args make_args(const Shape &s) {
     Args a{};
     a.B = s.B;
@@ -661,7 +686,7 @@ hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const 
     a.v = v;
     a.out_o = o;
     a.out_lse = lse;
-    const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.fwd);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.fwd != 0);
     a.hpw = g.hpw;
     a.rb = g.rb;
     a.nqt = g.nqt;
@@ -683,7 +708,7 @@ hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const f
     a.dO = dO;
     a.dq = dq;
     a.delta = delta;
-    const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.dq);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.dq != 0);
     a.hpw = g.hpw;
     a.rb = g.rb;
     a.nqt = g.nqt;
@@ -705,7 +730,7 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
     a.dk = dk;
     a.dv = dv;
     a.delta = const_cast<float *>(delta);  // read only in this pass
-    const KBlockGeom g = kblock_geometry(s, s.causal && kPairF32.dkdv);
+    const KBlockGeom g = kblock_geometry(s, s.causal && kPairF32.dkdv != 0);
     a.paired = g.paired;
     a.nkb = g.nkb;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
@@ -713,6 +738,19 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
                        (s.D == 64 ? dkdv_wave_floats<64>() : dkdv_wave_floats<32>()) * sizeof(float);
     const void *fn = s.D == 64 ? pick_dkdv_f32<64>(causal, rope) : pick_dkdv_f32<32>(causal, rope);
     return launch(fn, g.nblocks, 64 * g.nwaves, lds, st, a);
+}
+
+hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long rows,
+                           hipStream_t st) {
+    RopeTurns rt = rope_turns(s);
+    long long nbh = rows / s.T;
+    int T = s.T;
+    const long long per_pos = (long long)T * (s.D / 4);
+    const unsigned gx = (unsigned)((per_pos + 255) / 256);
+    const long long gy = std::max(1LL, std::min(nbh, std::max(nbh / 8, 2048LL / (long long)gx)));
+    const void *fn = s.D == 64 ? (const void *)rope_rows_f32<64> : (const void *)rope_rows_f32<32>;
+    void *params[] = {&x, &y, &nbh, &T, &rt};
+    return hipLaunchKernel(fn, dim3(gx, (unsigned)std::min(gy, 65535LL)), dim3(256), params, 0, st);
 }
 
 }  // namespace ne

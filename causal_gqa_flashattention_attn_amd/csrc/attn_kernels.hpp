@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 
 namespace ne {
@@ -58,6 +59,9 @@ struct PairPolicy {
 constexpr PairPolicy kPairF32{NE_PAIR_F32};
 constexpr PairPolicy kPairBf16{NE_PAIR_BF16};
 
+// With RoPE (s.rope_base > 0) the kernels expect rotated inputs where they stream a tensor
+// through LDS: the forward takes rotated k (and rotates each query row itself), the dQ and
+// dK/dV passes take rotated q and k, and rotate dq and dk back before storing them.
 hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const float *v,
                           float *o, float *lse, hipStream_t st);
 // dQ pass: writes dq and delta (= rowsum(dO * o)).
@@ -78,5 +82,24 @@ hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const vo
 hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const void *v,
                             const float *lse, const void *dO, const float *delta, void *dk,
                             void *dv, hipStream_t st);
+
+// Turns per position of each RoPE pair, base^(-2i/D) / (2 pi), evaluated on the host in double.
+struct RopeTurns {
+    double per_pos[32];
+};
+
+inline RopeTurns rope_turns(const Shape &s) {
+    RopeTurns r{};
+    const double lb = s.rope_base > 0.f ? log2((double)s.rope_base) : 0.0;
+    for (int i = 0; i < s.D / 2 && i < 32; ++i)
+        r.per_pos[i] = exp2(-(2.0 * i / s.D) * lb) * 0.15915494309189535;
+    return r;
+}
+
+// RoPE applied to a whole tensor [rows / T][T][D] (s.rope_base > 0), x -> y.
+hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long rows,
+                           hipStream_t st);
+hipError_t launch_rope_bf16(const Shape &s, const void *x, void *y, long long rows,
+                            hipStream_t st);
 
 }  // namespace ne

@@ -39,79 +39,140 @@ int check_shape(int B, int Hq, int Hkv, int T, int D, int causal, int dtype, flo
     return NE_OK;
 }
 
-int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
-             int Hkv, int T, int D, int causal, int dtype, float rope_base, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse) return NE_ERR_NULL;
-    ne::Shape s;
-    const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
-    if (rc != NE_OK) return rc;
-    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
-        return NE_ERR_ALIGN;
-    const hipError_t e =
-        dtype == NE_BF16
-            ? ne::launch_fwd_bf16(s, q, k, v, o, lse, stream)
-            : ne::launch_fwd_f32(s, static_cast<const float *>(q), static_cast<const float *>(k),
-                                 static_cast<const float *>(v), static_cast<float *>(o), lse,
-                                 stream);
-    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
-}
-
 bool any_misaligned(std::initializer_list<const void *> ptrs) {
     for (const void *p : ptrs)
         if (misaligned(p)) return true;
     return false;
 }
 
-int dq_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
-            const void *dO, void *dq, float *delta_ws, int B, int Hq, int Hkv, int T, int D,
-            int causal, int dtype, float rope_base, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse || !dO || !dq || !delta_ws) return NE_ERR_NULL;
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the _ex entry points: delta (fp32 [B][Hq][T]) first, then -- with RoPE -- the
+// rotated keys [B][Hkv][T][D] and the rotated queries [B][Hq][T][D] in the tensors' dtype, each
+// region starting on a 256-byte boundary.
+struct WsLayout {
+    size_t delta, kr, qr, total;
+};
+
+WsLayout ws_layout(const ne::Shape &s, int dtype) {
+    const size_t es = dtype == NE_BF16 ? 2 : 4;
+    const size_t bt = (size_t)s.B * (size_t)s.T;
+    WsLayout w{};
+    size_t off = up256(4 * bt * (size_t)s.Hq);
+    if (s.rope_base > 0.f) {
+        w.kr = off;
+        off += up256(es * bt * (size_t)s.Hkv * (size_t)s.D);
+        w.qr = off;
+        off += up256(es * bt * (size_t)s.Hq * (size_t)s.D);
+    }
+    w.total = off;
+    return w;
+}
+
+hipError_t launch_rope(const ne::Shape &s, int dtype, const void *x, void *y, long long rows,
+                       hipStream_t stream) {
+    return dtype == NE_BF16 ? ne::launch_rope_bf16(s, x, y, rows, stream)
+                            : ne::launch_rope_f32(s, static_cast<const float *>(x),
+                                                  static_cast<float *>(y), rows, stream);
+}
+
+int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, void *ws, int B,
+             int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
+             hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return NE_ERR_NULL;
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
-    if (any_misaligned({q, k, v, o, lse, dO, dq, delta_ws})) return NE_ERR_ALIGN;
+    const bool rope = s.rope_base > 0.f;
+    if (rope && !ws) return NE_ERR_NULL;
+    if (any_misaligned({q, k, v, o, lse}) || (rope && misaligned(ws))) return NE_ERR_ALIGN;
+    const void *kk = k;
+    if (rope) {
+        // Keys rotated once into the workspace; each query row is rotated as it is loaded.
+        void *kr = static_cast<char *>(ws) + ws_layout(s, dtype).kr;
+        if (launch_rope(s, dtype, k, kr, (long long)B * Hkv * T, stream) != hipSuccess)
+            return NE_ERR_HIP;
+        kk = kr;
+    }
     const hipError_t e =
         dtype == NE_BF16
-            ? ne::launch_dq_bf16(s, q, k, v, o, lse, dO, dq, delta_ws, stream)
-            : ne::launch_dq_f32(s, static_cast<const float *>(q), static_cast<const float *>(k),
+            ? ne::launch_fwd_bf16(s, q, kk, v, o, lse, stream)
+            : ne::launch_fwd_f32(s, static_cast<const float *>(q), static_cast<const float *>(kk),
+                                 static_cast<const float *>(v), static_cast<float *>(o), lse,
+                                 stream);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+int dq_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
+            const void *dO, void *dq, void *ws, int B, int Hq, int Hkv, int T, int D, int causal,
+            int dtype, float rope_base, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !ws) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (any_misaligned({q, k, v, o, lse, dO, dq, ws})) return NE_ERR_ALIGN;
+    const WsLayout L = ws_layout(s, dtype);
+    float *delta = static_cast<float *>(ws);
+    const void *qq = q, *kk = k;
+    if (s.rope_base > 0.f) {
+        // Queries and keys rotated once into the workspace, for this pass and the dK/dV pass.
+        void *qr = static_cast<char *>(ws) + L.qr;
+        void *kr = static_cast<char *>(ws) + L.kr;
+        if (launch_rope(s, dtype, q, qr, (long long)B * Hq * T, stream) != hipSuccess ||
+            launch_rope(s, dtype, k, kr, (long long)B * Hkv * T, stream) != hipSuccess)
+            return NE_ERR_HIP;
+        qq = qr;
+        kk = kr;
+    }
+    const hipError_t e =
+        dtype == NE_BF16
+            ? ne::launch_dq_bf16(s, qq, kk, v, o, lse, dO, dq, delta, stream)
+            : ne::launch_dq_f32(s, static_cast<const float *>(qq), static_cast<const float *>(kk),
                                 static_cast<const float *>(v), static_cast<const float *>(o), lse,
-                                static_cast<const float *>(dO), static_cast<float *>(dq),
-                                delta_ws, stream);
+                                static_cast<const float *>(dO), static_cast<float *>(dq), delta,
+                                stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
 int dkdv_impl(const void *q, const void *k, const void *v, const float *lse, const void *dO,
-              const float *delta_ws, void *dk, void *dv, int B, int Hq, int Hkv, int T, int D,
+              const void *ws, void *dk, void *dv, int B, int Hq, int Hkv, int T, int D,
               int causal, int dtype, float rope_base, hipStream_t stream) {
-    if (!q || !k || !v || !lse || !dO || !delta_ws || !dk || !dv) return NE_ERR_NULL;
+    if (!q || !k || !v || !lse || !dO || !ws || !dk || !dv) return NE_ERR_NULL;
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
-    if (any_misaligned({q, k, v, lse, dO, delta_ws, dk, dv})) return NE_ERR_ALIGN;
+    if (any_misaligned({q, k, v, lse, dO, ws, dk, dv})) return NE_ERR_ALIGN;
+    const WsLayout L = ws_layout(s, dtype);
+    const float *delta = static_cast<const float *>(ws);
+    const void *qq = q, *kk = k;
+    if (s.rope_base > 0.f) {  // rotated by the dQ pass
+        qq = static_cast<const char *>(ws) + L.qr;
+        kk = static_cast<const char *>(ws) + L.kr;
+    }
     const hipError_t e =
         dtype == NE_BF16
-            ? ne::launch_dkdv_bf16(s, q, k, v, lse, dO, delta_ws, dk, dv, stream)
-            : ne::launch_dkdv_f32(s, static_cast<const float *>(q), static_cast<const float *>(k),
+            ? ne::launch_dkdv_bf16(s, qq, kk, v, lse, dO, delta, dk, dv, stream)
+            : ne::launch_dkdv_f32(s, static_cast<const float *>(qq), static_cast<const float *>(kk),
                                   static_cast<const float *>(v), lse,
-                                  static_cast<const float *>(dO), delta_ws,
+                                  static_cast<const float *>(dO), delta,
                                   static_cast<float *>(dk), static_cast<float *>(dv), stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
 int bwd_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
-             const void *dO, void *dq, void *dk, void *dv, float *delta_ws, int B, int Hq,
-             int Hkv, int T, int D, int causal, int dtype, float rope_base, hipStream_t stream) {
+             const void *dO, void *dq, void *dk, void *dv, void *ws, int B, int Hq, int Hkv,
+             int T, int D, int causal, int dtype, float rope_base, hipStream_t stream) {
     // Check everything (including dk, dv) before the first pass is enqueued.
-    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !delta_ws) return NE_ERR_NULL;
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !ws) return NE_ERR_NULL;
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
-    if (any_misaligned({q, k, v, o, lse, dO, dq, dk, dv, delta_ws})) return NE_ERR_ALIGN;
-    const int r1 = dq_impl(q, k, v, o, lse, dO, dq, delta_ws, B, Hq, Hkv, T, D, causal, dtype,
+    if (any_misaligned({q, k, v, o, lse, dO, dq, dk, dv, ws})) return NE_ERR_ALIGN;
+    const int r1 = dq_impl(q, k, v, o, lse, dO, dq, ws, B, Hq, Hkv, T, D, causal, dtype,
                            rope_base, stream);
     if (r1 != NE_OK) return r1;
-    return dkdv_impl(q, k, v, lse, dO, delta_ws, dk, dv, B, Hq, Hkv, T, D, causal, dtype,
-                     rope_base, stream);
+    return dkdv_impl(q, k, v, lse, dO, ws, dk, dv, B, Hq, Hkv, T, D, causal, dtype, rope_base,
+                     stream);
 }
 
 }  // namespace
@@ -120,44 +181,53 @@ extern "C" {
 
 int ne_attn_fwd(const float *q, const float *k, const float *v, float *o, float *lse, int B,
                 int Hq, int Hkv, int T, int D, int causal, hipStream_t stream) {
-    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, T, D, causal, NE_F32, 0.f, stream);
+    return fwd_impl(q, k, v, o, lse, nullptr, B, Hq, Hkv, T, D, causal, NE_F32, 0.f, stream);
 }
 
 int ne_attn_bwd(const float *q, const float *k, const float *v, const float *o, const float *lse,
                 const float *dO, float *dq, float *dk, float *dv, float *delta_ws, int B, int Hq,
                 int Hkv, int T, int D, int causal, hipStream_t stream) {
+    // Without RoPE the workspace is the delta region alone.
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, B, Hq, Hkv, T, D, causal, NE_F32,
                     0.f, stream);
 }
 
-int ne_attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B,
-                   int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
-                   hipStream_t stream) {
-    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, T, D, causal, dtype, rope_base, stream);
+int ne_attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                   void *workspace, int B, int Hq, int Hkv, int T, int D, int causal, int dtype,
+                   float rope_base, hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, workspace, B, Hq, Hkv, T, D, causal, dtype, rope_base,
+                    stream);
 }
 
 int ne_attn_bwd_ex(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                   const void *dO, void *dq, void *dk, void *dv, float *delta_ws, int B, int Hq,
+                   const void *dO, void *dq, void *dk, void *dv, void *workspace, int B, int Hq,
                    int Hkv, int T, int D, int causal, int dtype, float rope_base,
                    hipStream_t stream) {
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, B, Hq, Hkv, T, D, causal, dtype,
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, workspace, B, Hq, Hkv, T, D, causal, dtype,
                     rope_base, stream);
 }
 
 int ne_attn_bwd_dq_ex(const void *q, const void *k, const void *v, const void *o,
-                      const float *lse, const void *dO, void *dq, float *delta_ws, int B, int Hq,
+                      const float *lse, const void *dO, void *dq, void *workspace, int B, int Hq,
                       int Hkv, int T, int D, int causal, int dtype, float rope_base,
                       hipStream_t stream) {
-    return dq_impl(q, k, v, o, lse, dO, dq, delta_ws, B, Hq, Hkv, T, D, causal, dtype, rope_base,
-                   stream);
+    return dq_impl(q, k, v, o, lse, dO, dq, workspace, B, Hq, Hkv, T, D, causal, dtype,
+                   rope_base, stream);
 }
 
 int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float *lse,
-                        const void *dO, const float *delta_ws, void *dk, void *dv, int B, int Hq,
+                        const void *dO, const void *workspace, void *dk, void *dv, int B, int Hq,
                         int Hkv, int T, int D, int causal, int dtype, float rope_base,
                         hipStream_t stream) {
-    return dkdv_impl(q, k, v, lse, dO, delta_ws, dk, dv, B, Hq, Hkv, T, D, causal, dtype,
+    return dkdv_impl(q, k, v, lse, dO, workspace, dk, dv, B, Hq, Hkv, T, D, causal, dtype,
                      rope_base, stream);
+}
+
+size_t ne_attn_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int dtype,
+                               float rope_base) {
+    ne::Shape s;
+    if (check_shape(B, Hq, Hkv, T, D, 1, dtype, rope_base, s) != NE_OK) return 0;
+    return ws_layout(s, dtype).total;
 }
 
 size_t ne_attn_bwd_workspace_bytes(int B, int Hq, int T) {

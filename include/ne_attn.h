@@ -25,7 +25,8 @@
  *   by the angle t * rope_base^(-2i/D).
  *
  * Ownership and memory.  Every pointer is a device pointer owned by the caller; the library
- * allocates and frees nothing, keeps no state and is thread-safe.  Outputs (o, lse, dq, dk, dv,
+ * allocates and frees nothing, keeps no state and is thread-safe (calls that share a workspace
+ * must be ordered).  Outputs (o, lse, dq, dk, dv,
  * delta) are fully overwritten; inputs are never written.  Inputs and outputs must not alias.
  * Pointers must be 16-byte aligned.
  *
@@ -85,40 +86,59 @@ int ne_attn_bwd(const float *q, const float *k, const float *v, const float *o,
                 hipStream_t stream);
 
 /*
- * Forward with a dtype (NE_F32 or NE_BF16) and an optional fused RoPE prologue on q and k
+ * Forward with a dtype (NE_F32 or NE_BF16) and an optional RoPE prologue on q and k
  * (rope_base > 0; 0 disables it).  Tensors are float* for NE_F32 and bfloat16 (uint16 bit
  * patterns) for NE_BF16; lse is float32 in both.
+ *
+ * workspace: caller-owned device memory of ne_attn_workspace_bytes(B, Hq, Hkv, T, D, dtype,
+ * rope_base) bytes, 16-byte aligned, not aliasing any tensor.  With RoPE the keys are rotated
+ * once into it (each query row is rotated as the kernel loads it); without RoPE it is not used
+ * and may be NULL.  Its contents on return are unspecified.
  */
 int ne_attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
-                   int B, int Hq, int Hkv, int T, int D, int causal, int dtype,
+                   void *workspace, int B, int Hq, int Hkv, int T, int D, int causal, int dtype,
                    float rope_base, hipStream_t stream);
 
 /*
  * Backward with a dtype and the same RoPE setting as the forward call.  With RoPE, dq and dk
  * are gradients with respect to the un-rotated q and k the caller passed.
+ *
+ * workspace: caller-owned device memory of ne_attn_workspace_bytes(...) bytes (never NULL),
+ * 16-byte aligned, not aliasing any tensor.  It receives delta_i = sum_d dO_id o_id (float32
+ * [B][Hq][T], at offset 0) and, with RoPE, the rotated q and k used by both passes.  No
+ * atomics: results are bitwise reproducible run to run.
  */
 int ne_attn_bwd_ex(const void *q, const void *k, const void *v, const void *o,
                    const float *lse, const void *dO, void *dq, void *dk, void *dv,
-                   float *delta_ws, int B, int Hq, int Hkv, int T, int D, int causal,
+                   void *workspace, int B, int Hq, int Hkv, int T, int D, int causal,
                    int dtype, float rope_base, hipStream_t stream);
 
 /*
  * The two passes that ne_attn_bwd_ex runs back to back, as separate calls for callers that
- * schedule them themselves or need only dq.  ne_attn_bwd_dq_ex writes dq and delta_ws
- * (delta_i = sum_d dO_id o_id); ne_attn_bwd_dkdv_ex reads delta_ws and writes dk, dv, and must
- * be ordered after the dq pass that filled delta_ws (same stream, or an event).  Arguments
- * mean what they mean for ne_attn_bwd_ex.
+ * schedule them themselves or need only dq.  ne_attn_bwd_dq_ex writes dq and fills the
+ * workspace (delta and, with RoPE, the rotated q and k); ne_attn_bwd_dkdv_ex reads the
+ * workspace and writes dk, dv, and must be ordered after the dq pass that filled it (same
+ * stream, or an event), with the same inputs and settings.  Arguments mean what they mean for
+ * ne_attn_bwd_ex.
  */
 int ne_attn_bwd_dq_ex(const void *q, const void *k, const void *v, const void *o,
-                      const float *lse, const void *dO, void *dq, float *delta_ws, int B,
+                      const float *lse, const void *dO, void *dq, void *workspace, int B,
                       int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
                       hipStream_t stream);
 int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float *lse,
-                        const void *dO, const float *delta_ws, void *dk, void *dv, int B,
+                        const void *dO, const void *workspace, void *dk, void *dv, int B,
                         int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
                         hipStream_t stream);
 
-/* Bytes of the backward workspace: 4 * B * Hq * T (0 if an argument is below 1). */
+/*
+ * Bytes of the workspace of the _ex entry points: the delta region (4 * B * Hq * T) and, when
+ * rope_base > 0, room for rotated copies of q and k in the given dtype, each region rounded up
+ * to 256 bytes.  0 if the arguments are invalid (the checks of the entry points).
+ */
+size_t ne_attn_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int dtype,
+                               float rope_base);
+
+/* Bytes of the workspace of ne_attn_bwd: 4 * B * Hq * T (0 if an argument is below 1). */
 size_t ne_attn_bwd_workspace_bytes(int B, int Hq, int T);
 
 /* Static, NUL-terminated description of a status code ("unknown status" otherwise). */

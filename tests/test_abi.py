@@ -47,12 +47,30 @@ def test_workspace_bytes(ne):
     assert ne.ne_attn_bwd_workspace_bytes(1, 1, 1) == 4
 
 
-def fwd(ne, ptrs=None, B=1, Hq=4, Hkv=2, T=64, D=32, causal=1, dtype=None, rope=0.0):
+def up256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("dtype,es", [(0, 4), (1, 2)])
+def test_ex_workspace_bytes(ne, dtype, es):
+    """delta region, then (with RoPE) rotated k and rotated q, each on a 256-byte boundary."""
+    B, Hq, Hkv, T, D = 3, 6, 2, 77, 64
+    assert ne.ne_attn_workspace_bytes(B, Hq, Hkv, T, D, dtype, 0.0) == up256(4 * B * Hq * T)
+    assert ne.ne_attn_workspace_bytes(B, Hq, Hkv, T, D, dtype, 10000.0) == (
+        up256(4 * B * Hq * T) + up256(es * B * Hkv * T * D) + up256(es * B * Hq * T * D))
+    assert ne.ne_attn_workspace_bytes(B, Hq, 4, T, D, dtype, 0.0) == 0    # Hq % Hkv != 0
+    assert ne.ne_attn_workspace_bytes(B, Hq, Hkv, T, 48, dtype, 0.0) == 0  # unsupported D
+    assert ne.ne_attn_workspace_bytes(B, Hq, Hkv, T, D, 7, 0.0) == 0       # unknown dtype
+    assert ne.ne_attn_workspace_bytes(B, Hq, Hkv, T, D, dtype, -1.0) == 0
+
+
+def fwd(ne, ptrs=None, B=1, Hq=4, Hkv=2, T=64, D=32, causal=1, dtype=None, rope=0.0, ws=A):
     L = ne.load()
     p = ptrs or [A] * 5
     if dtype is None:
         return L.ne_attn_fwd(*[VP(x) for x in p], B, Hq, Hkv, T, D, causal, VP(0))
-    return L.ne_attn_fwd_ex(*[VP(x) for x in p], B, Hq, Hkv, T, D, causal, dtype, rope, VP(0))
+    return L.ne_attn_fwd_ex(*[VP(x) for x in p], VP(ws), B, Hq, Hkv, T, D, causal, dtype, rope,
+                            VP(0))
 
 
 def bwd(ne, ptrs=None, B=1, Hq=4, Hkv=2, T=64, D=32, causal=1, dtype=None, rope=0.0):
@@ -69,6 +87,15 @@ def test_fwd_null_pointer(ne, which):
     p[which] = 0
     assert fwd(ne, p) == ne.NE_ERR_NULL
     assert fwd(ne, p, dtype=0) == ne.NE_ERR_NULL
+    assert fwd(ne, p, dtype=1, rope=10000.0) == ne.NE_ERR_NULL
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_fwd_rope_needs_workspace(ne, dtype):
+    """With RoPE the forward rotates the keys into the workspace: NULL or misaligned is refused
+    before anything is enqueued."""
+    assert fwd(ne, dtype=dtype, rope=10000.0, ws=0) == ne.NE_ERR_NULL
+    assert fwd(ne, dtype=dtype, rope=10000.0, ws=A + 4) == ne.NE_ERR_ALIGN
 
 
 @pytest.mark.parametrize("which", range(10))
