@@ -5,8 +5,10 @@
                     [--no-cpu-baseline] [--graph]
 
 One step is one pass of the whole path over one batch of synthetic inputs already resident in
-HBM: the forward kernel (o, lse), then the two backward passes (dq + delta, then dk, dv), i.e.
-exactly what ne_attn_fwd_ex followed by ne_attn_bwd_ex enqueue.  The K timed steps are
+HBM: the forward (o, lse), then the two backward passes (dq + delta, then dk, dv), i.e. exactly
+what ne_attn_fwd_ex followed by ne_attn_bwd_ex enqueue.  With RoPE the forward and the dq pass
+each start with the pre-pass that rotates k (forward) or q and k (dq pass) into the workspace;
+their per-call durations include it.  The K timed steps are
 bracketed by device synchronisations; `value` is algorithmic TFLOP/s (causal FLOPs counted as
 half of dense; forward 2 GEMMs, backward 5) over the wall-clock time per step.
 
@@ -18,6 +20,8 @@ sample of the same workload.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
+import gc
 import hashlib
 import json
 import os
@@ -146,16 +150,29 @@ def main():
     ws = ne.workspace(q, k, rb)
     names = ("fwd", "bwd_dq", "bwd_dkdv")
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        ne.ne_attn_fwd_ex(q, k, v, o, lse, ws, causal=c, rope_base=rb)
-        if ev is not None:
-            ev[1].record()
-        ne.ne_attn_bwd_dq_ex(q, k, v, o, lse, dO, dq, ws, causal=c, rope_base=rb)
-        if ev is not None:
-            ev[2].record()
-        ne.ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, ws, dk, dv, causal=c, rope_base=rb)
+    # Arguments are marshalled once: a step is three calls straight into the C entry points
+    # (which validate their arguments themselves), so the host stays well ahead of the GPU.
+    L = ne.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def bind(stream):
+        dims = (w.B, w.Hq, w.Hkv, w.T, w.D, int(c),
+                ne.NE_BF16 if w.dtype == "bf16" else ne.NE_F32, ctypes.c_float(rb),
+                ctypes.c_void_p(stream.cuda_stream))
+        return ((L.ne_attn_fwd_ex, (P(q), P(k), P(v), P(o), P(lse), P(ws)) + dims),
+                (L.ne_attn_bwd_dq_ex, (P(q), P(k), P(v), P(o), P(lse), P(dO), P(dq), P(ws)) + dims),
+                (L.ne_attn_bwd_dkdv_ex, (P(q), P(k), P(v), P(lse), P(dO), P(ws), P(dk), P(dv))
+                 + dims))
+
+    calls = bind(torch.cuda.current_stream(dev))
+
+    def step(ev=None, calls_=None):
+        for j, (fn, args) in enumerate(calls_ or calls):
+            if ev is not None:
+                ev[j].record()
+            rc = fn(*args)
+            if rc != ne.NE_OK:
+                raise ne.NeAttnError(rc, fn.__name__)
         if ev is not None:
             ev[3].record()
 
@@ -172,11 +189,11 @@ def main():
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            step()
+            step(calls_=bind(s))
         torch.cuda.current_stream().wait_stream(s)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
+            step(calls_=bind(torch.cuda.current_stream()))
 
     for _ in range(a.warmup):
         graph.replay() if graph is not None else step()
@@ -184,6 +201,7 @@ def main():
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
     torch.cuda.synchronize()
+    gc.disable()  # no collector pause while the host enqueues the timed steps
     t0 = time.perf_counter()
     for i in range(a.steps):
         if graph is not None:
@@ -194,6 +212,7 @@ def main():
             step(events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
 
     ms_per_step = (t1 - t0) * 1e3 / a.steps
     tflops = w.flops_fwd_bwd() / (ms_per_step * 1e-3) / 1e12
