@@ -28,7 +28,7 @@
 #define NE_BF16_FWD_WAVES_PER_EU 2
 #endif
 #ifndef NE_BF16_DQ_WAVES_PER_EU
-#define NE_BF16_DQ_WAVES_PER_EU 2
+#define NE_BF16_DQ_WAVES_PER_EU 3
 #endif
 #ifndef NE_BF16_DKDV_WAVES_PER_EU
 #define NE_BF16_DKDV_WAVES_PER_EU 2
@@ -163,48 +163,60 @@ __device__ __forceinline__ QTileB qtile_of_b(const ArgsB &a, const QWorkB &w, in
     return c;
 }
 
-// Staging of BN-row K and V tiles: HBM -> registers (issued one tile ahead) -> swizzled LDS.
-// A tile is moved in 1 KB pieces, one wave-wide 16-byte load per piece; piece c goes to wave
-// c % nw, so every branch on the piece index is uniform across the wave.  With RoPE the keys
-// arrive already rotated.
+// K and V tiles of BN rows staged by direct global -> LDS copies into a ring of NST stages
+// (stage = K tile then V tile, rows in the swizzled layout of tile_off).  A stage is NPC 1 KB
+// pieces; one wave-wide dma16 fills one piece, and lane l fills the 16-byte slot l of it, so a
+// lane loads the logical chunk that the swizzle places in its slot (the swizzle is an XOR, its
+// own inverse).  Within a tensor tile, piece q covers rows q * RPP .. + RPP - 1 and the lane's
+// row is q * RPP + lane / NCH; the swizzle depends on the row modulo 16, so one column offset
+// per parity of q covers every piece.  Wave w copies pieces w, w + nw, ...; a wave with a
+// shorter share copies its first piece again, so every wave issues lpw copies per tile and can
+// wait on a fixed count.  Rows past the end read row T - 1: those keys are masked, so only
+// finiteness matters.
 template <int D>
-struct KVStagerB {
+struct KVRingB {
     using C = CfgB<D>;
-    static constexpr int RPP = 64 / C::NCH;            // rows per 1 KB piece
-    static constexpr int NP = C::BN / RPP;             // pieces per tile
-    static constexpr int MAXP = (NP + 1) / 2;          // per wave (query-tile groups have >= 2 waves)
-    bf16x8 k[MAXP], v[MAXP];
-    int ch, rsub;
+    static constexpr int NST = 3;                 // stages
+    static constexpr int TB = C::BN * C::RB;      // bytes of one K (or V) tile
+    static constexpr int SB = 2 * TB;             // bytes of one stage
+    static constexpr int PPT = TB / 1024;         // pieces per tensor tile
+    static constexpr int NPC = 2 * PPT;           // pieces per stage
+    static constexpr int RPP = 1024 / C::RB;      // tile rows per piece
+    static constexpr int MAXL = NPC / 2;          // pieces per wave (query-tile groups: >= 2 waves)
+    int wave, nw, lpw;  // wave-uniform
+    int lrow;           // lane / NCH: the lane's row within a piece
+    int off0, off1;     // byte offset of the lane's 16 bytes within an even / odd piece's rows
 
-    __device__ __forceinline__ void init(int lane) {
-        ch = lane % C::NCH;
-        rsub = lane / C::NCH;
+    __device__ __forceinline__ void init(int wave_, int nw_, int lane) {
+        wave = wave_;
+        nw = nw_;
+        lpw = (NPC + nw - 1) / nw;
+        lrow = lane / C::NCH;
+        // Rows lrow and RPP + lrow have the swizzle of every row of even and odd pieces.
+        off0 = 2 * (lrow * D + 8 * chunk_swizzle<D>(lrow, lane % C::NCH));
+        off1 = 2 * (lrow * D + 8 * chunk_swizzle<D>(RPP + lrow, lane % C::NCH));
     }
-    __device__ __forceinline__ void load(const __bf16 *kg, const __bf16 *vg, int tile, int T,
-                                         int wave, int nw) {
+    // Starts the copies of tile `tile` into `stage`.
+    __device__ __forceinline__ void issue(const __bf16 *kg, const __bf16 *vg, int tile, int T,
+                                          unsigned char *stage) const {
+        const bool whole = (tile + 1) * C::BN <= T;  // no row past the end
 #pragma unroll
-        for (int i = 0; i < MAXP; ++i) {
-            const int pc = wave + i * nw;
-            if (pc < NP) {
-                const int row = min(tile * C::BN + pc * RPP + rsub, T - 1);
-                k[i] = *reinterpret_cast<const bf16x8 *>(kg + (size_t)row * D + 8 * ch);
-                v[i] = *reinterpret_cast<const bf16x8 *>(vg + (size_t)row * D + 8 * ch);
+        for (int i = 0; i < MAXL; ++i)
+            if (i < lpw) {
+                int pc = wave + i * nw;
+                if (pc >= NPC) pc = wave;
+                const bool isv = pc >= PPT;
+                const int q = isv ? pc - PPT : pc;
+                const int row0 = tile * C::BN + q * RPP;  // first row of the piece
+                const unsigned char *base = reinterpret_cast<const unsigned char *>(isv ? vg : kg);
+                const int off = (q & 1) ? off1 : off0;
+                if (whole) {
+                    dma16(base + (size_t)row0 * (2 * D) + off, stage + pc * 1024);
+                } else {
+                    const int r = min(row0 + lrow, T - 1);
+                    dma16(base + (size_t)r * (2 * D) + (off - 2 * lrow * D), stage + pc * 1024);
+                }
             }
-        }
-    }
-    __device__ __forceinline__ void store(unsigned char *sK, unsigned char *sV, int tile, int T,
-                                          int wave, int nw) {
-        const bf16x8 zero = {};
-#pragma unroll
-        for (int i = 0; i < MAXP; ++i) {
-            const int pc = wave + i * nw;
-            if (pc < NP) {
-                const int r = pc * RPP + rsub;
-                const int row = tile * C::BN + r;
-                *reinterpret_cast<bf16x8 *>(sK + tile_off<D>(r, 8 * ch)) = row < T ? k[i] : zero;
-                *reinterpret_cast<bf16x8 *>(sV + tile_off<D>(r, 8 * ch)) = row < T ? v[i] : zero;
-            }
-        }
     }
 };
 
@@ -247,97 +259,137 @@ __device__ __forceinline__ void block_accum(f32x16 (&acc)[CfgB<D>::ND], const un
     }
 }
 
+// acc (D x 32, transposed) += M_tile[r0 .. r0+31]^T x X, X given as its two bf16 operand halves.
+template <int D>
+__device__ __forceinline__ void block_accum_x(f32x16 (&acc)[CfgB<D>::ND], const unsigned char *tile,
+                                              int r0, const bf16x8 (&xb)[2], int lane) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dd = 0; dd < CfgB<D>::ND; ++dd)
+            acc[dd] = mfma32_bf16(tile_read_tr8<D>(tile, r0 + 16 * s2, 32 * dd, lane), xb[s2], acc[dd]);
+}
+
+// Online-softmax state of a wave's 32 query rows in the forward: O^T accumulator, reference
+// maximum m (base 2, scaled) and four partial sums of the bf16 probabilities.
+template <int D>
+struct FwdState {
+    f32x16 acc[CfgB<D>::ND];
+    float m;
+    float l4[4];
+};
+
+// One 32-key half of a tile in the forward (keys kb0 .. kb0 + 31, tile rows rt .. rt + 31).  The
+// halves are processed one after the other, each with its own online-softmax update, so only
+// one 32 x 32 score block is live: that keeps the kernel within the registers of two waves per
+// SIMD with room to spare, which measured faster than one wider update per 64 keys.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_half(const ArgsB &a, FwdState<D> &st, const unsigned char *sK,
+                                         const unsigned char *sV, int rt, int kb0, int r0, int T,
+                                         const bf16x8 (&qv)[CfgB<D>::KS], int lane, int li) {
+    const int half = lane >> 5, col = lane & 31;
+    const int qrow = r0 + col;
+    f32x16 s = block_scores<D>(sK, rt, qv, col, half);
+    if ((CAUSAL && kb0 + 31 > r0) || kb0 + 32 > T) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int key = kb0 + acc_row(v, half);
+            if ((CAUSAL && key > qrow) || key >= T) s[v] = -INFINITY;
+        }
+    }
+    // Maximum over the 32 keys of each row: four independent chains, then the two lane halves.
+    float mq[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mq[c] = fmaxf(fmaxf(s[4 * c], s[4 * c + 1]), fmaxf(s[4 * c + 2], s[4 * c + 3]));
+    const float mx = max_halves(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * a.qscale;
+    // The reference maximum m only moves when some row's maximum exceeds it by more than 2^8:
+    // probabilities up to 256 are exact enough in fp32 sums and bf16 operands, and most steps
+    // then skip the rescale of l and O entirely.
+    if (__builtin_amdgcn_ballot_w64(mx > st.m + 8.0f) != 0) {
+        const float mnew = fmaxf(st.m, mx);
+        const float alpha = fast_exp2(st.m - mnew);
+        st.m = mnew;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.l4[i] *= alpha;
+#pragma unroll
+        for (int dd = 0; dd < CfgB<D>::ND; ++dd) st.acc[dd] *= alpha;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = fast_exp2(fmaf(s[v], a.qscale, -st.m));
+    // P enters the matrix cores rounded to bf16; l sums exactly those values.
+    const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
+    st.l4[li] = sum8_bf16(pb[0], st.l4[li]);
+    st.l4[li + 1] = sum8_bf16(pb[1], st.l4[li + 1]);
+    block_accum_x<D>(st.acc, sV, rt, pb, lane);
+}
+
+// One 64-key tile of the forward: its two 32-key halves one after the other (a half entirely
+// above the diagonal or past the end is skipped, and then so is the second).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_step(const ArgsB &a, FwdState<D> &st, const unsigned char *sK,
+                                         const unsigned char *sV, int kt0, int r0, int T,
+                                         const bf16x8 (&qv)[CfgB<D>::KS], int lane) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        const int kb0 = kt0 + 32 * sb;
+        if (!(kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) return;
+        fwd_half<D, CAUSAL>(a, st, sK, sV, 32 * sb, kb0, r0, T, qv, lane, 2 * sb);
+    }
+}
+
 template <int D, bool CAUSAL, bool ROPE>
-__device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c,
-                                           unsigned char (&sK)[2][CfgB<D>::BN * CfgB<D>::RB],
-                                           unsigned char (&sV)[2][CfgB<D>::BN * CfgB<D>::RB]) {
+__device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsigned char *ring) {
     using C = CfgB<D>;
+    using R = KVRingB<D>;
     const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
-    const int qrow = c.r0 + col;
+    const int r0 = __builtin_amdgcn_readfirstlane(c.r0);
+    const int qrow = r0 + col;
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
     const __bf16 *kg = a.k + bg * T * D;
     const __bf16 *vg = a.v + bg * T * D;
 
     bf16x8 qv[C::KS];
     load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
+    // The query row has arrived before the first K/V copy is issued; otherwise the compiler,
+    // unable to count the copies issued inside the loop, waits for all of them where it first
+    // reads the row.
+    wait_vm_lgkm0(0);
+    __builtin_amdgcn_sched_barrier(0);
 
-    f32x16 acc[C::ND];
+    FwdState<D> st;
 #pragma unroll
-    for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
-    float m = kNegBig, l = 0.f;
+    for (int dd = 0; dd < C::ND; ++dd) st.acc[dd] = zero16();
+    st.m = kNegBig;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.l4[i] = 0.f;
 
     const int wg_rows = 32 * a.rb;
     const int wg_end = min(c.qt * wg_rows + wg_rows, T);
     const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
+    const bool live = r0 < T;
 
-    KVStagerB<D> stg;
-    stg.init(lane);
-    stg.load(kg, vg, 0, T, wave, nw);
-    stg.store(sK[0], sV[0], 0, T, wave, nw);
-    __syncthreads();
+    R kv;
+    kv.init(wave, nw, lane);
+    kv.issue(kg, vg, 0, T, ring);
+    if (ntiles > 1) kv.issue(kg, vg, 1, T, ring + R::SB);
     for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, T, wave, nw);
-        f32x16 s[2];
-        bool act[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int kb0 = j * C::BN + 32 * sb;
-            act[sb] = c.r0 < T && kb0 < T && (!CAUSAL || kb0 <= c.r0 + 31);
-            if (act[sb]) s[sb] = block_scores<D>(sK[buf], 32 * sb, qv, col, half);
-        }
-        if (act[0] || act[1]) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                if (!act[sb]) continue;
-                const int kb0 = j * C::BN + 32 * sb;
-                if ((CAUSAL && kb0 + 31 > c.r0) || kb0 + 32 > T) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = kb0 + acc_row(v, half);
-                        if ((CAUSAL && key > qrow) || key >= T) s[sb][v] = -INFINITY;
-                    }
-                }
-#pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sb][v]);
-            }
-            mx = fmaxf(mx, swap_halves(mx)) * a.qscale;
-            // The reference maximum m only moves when some row's maximum exceeds it by more
-            // than 2^8: probabilities up to 256 are exact enough in fp32 sums and bf16 operands,
-            // and most tiles then skip the rescale of l and O entirely.
-            if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
-                const float mnew = fmaxf(m, mx);
-                const float alpha = fast_exp2(m - mnew);
-                m = mnew;
-                l *= alpha;
-#pragma unroll
-                for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
-            }
-            float ps = 0.f;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                if (!act[sb]) continue;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    s[sb][v] = fast_exp2(fmaf(s[sb][v], a.qscale, -m));
-                    ps += s[sb][v];
-                }
-            }
-            l += ps;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-                if (act[sb]) block_accum<D>(acc, sV[buf], 32 * sb, s[sb], lane);
-        }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw);
-        __syncthreads();
+        // This wave's copies of tile j have landed (only tile j+1's may be in flight) and its
+        // reads of tile j-1 are done; after the barrier every wave's are, so tile j is complete
+        // and stage (j+2) % NST, last read for tile j-1, is free.
+        wait_vm_lgkm0(j + 1 < ntiles ? kv.lpw : 0);
+        __builtin_amdgcn_s_barrier();
+        const unsigned char *sK = ring + (j % R::NST) * R::SB;
+        if (live) fwd_step<D, CAUSAL>(a, st, sK, sK + R::TB, j * C::BN, r0, T, qv, lane);
+        // Issued after this tile's reads: the compiler makes transposed LDS reads wait for every
+        // copy in flight, and by the next tile's reads these have landed.
+        if (j + 2 < ntiles) kv.issue(kg, vg, j + 2, T, ring + ((j + 2) % R::NST) * R::SB);
     }
 
-    l += swap_halves(l);
+    const float l = sum_halves((st.l4[0] + st.l4[1]) + (st.l4[2] + st.l4[3]));
     if (qrow < T) {
         const float inv = 1.0f / l;
         __bf16 *orow = a.out_o + bh * T * D;
@@ -345,38 +397,38 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c,
         for (int dd = 0; dd < C::ND; ++dd)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                float x[4] = {acc[dd][4 * u] * inv, acc[dd][4 * u + 1] * inv,
-                              acc[dd][4 * u + 2] * inv, acc[dd][4 * u + 3] * inv};
+                float x[4] = {st.acc[dd][4 * u] * inv, st.acc[dd][4 * u + 1] * inv,
+                              st.acc[dd][4 * u + 2] * inv, st.acc[dd][4 * u + 3] * inv};
                 store_row4<D, false>(orow, qrow, 32 * dd + 8 * u + 4 * half, x, 0.f);
             }
-        if (half == 0) a.out_lse[bh * T + qrow] = m * kLn2 + logf(l);
+        if (half == 0) a.out_lse[bh * T + qrow] = st.m * kLn2 + logf(l);
     }
 }
 
 template <int D, bool CAUSAL, bool ROPE>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_FWD_WAVES_PER_EU)))
 fwd_bf16(ArgsB a) {
-    __shared__ __attribute__((aligned(16))) unsigned char sK[2][CfgB<D>::BN * CfgB<D>::RB];
-    __shared__ __attribute__((aligned(16))) unsigned char sV[2][CfgB<D>::BN * CfgB<D>::RB];
+    __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
     const int wave = threadIdx.x >> 6;
     const QWorkB w = decode_qwork_b(a);
-    fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), sK, sV);
+    fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), ring);
     if (w.qt1 >= 0) {
         __syncthreads();
-        fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt1, wave), sK, sV);
+        fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt1, wave), ring);
     }
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c,
-                                          unsigned char (&sK)[2][CfgB<D>::BN * CfgB<D>::RB],
-                                          unsigned char (&sV)[2][CfgB<D>::BN * CfgB<D>::RB]) {
+__device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsigned char *ring) {
     using C = CfgB<D>;
+    using R = KVRingB<D>;
     const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
-    const int qrow = c.r0 + col;
+    const int r0 = __builtin_amdgcn_readfirstlane(c.r0);
+    const int qrow = r0 + col;
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
     const __bf16 *kg = a.k + bg * T * D;
     const __bf16 *vg = a.v + bg * T * D;
@@ -395,7 +447,7 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c,
         for (int s = 0; s < C::KS; ++s)
 #pragma unroll
             for (int i = 0; i < 8; ++i) part += bf2f(dov[s][i]) * bf2f(ov[s][i]);
-        delta = part + swap_halves(part);
+        delta = sum_halves(part);
     }
     float lse2;
     if (qrow < T) {
@@ -413,35 +465,38 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c,
     const int wg_rows = 32 * a.rb;
     const int wg_end = min(c.qt * wg_rows + wg_rows, T);
     const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
+    const bool live = r0 < T;
+    wait_vm_lgkm0(0);  // row loads complete before the first K/V copy (as in the forward)
+    __builtin_amdgcn_sched_barrier(0);
 
-    KVStagerB<D> stg;
-    stg.init(lane);
-    stg.load(kg, vg, 0, T, wave, nw);
-    stg.store(sK[0], sV[0], 0, T, wave, nw);
-    __syncthreads();
+    R kv;
+    kv.init(wave, nw, lane);
+    kv.issue(kg, vg, 0, T, ring);
+    if (ntiles > 1) kv.issue(kg, vg, 1, T, ring + R::SB);
     for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, T, wave, nw);
+        wait_vm_lgkm0(j + 1 < ntiles ? kv.lpw : 0);  // as in the forward
+        __builtin_amdgcn_s_barrier();
+        const unsigned char *sK = ring + (j % R::NST) * R::SB;
+        const unsigned char *sV = sK + R::TB;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int kb0 = j * C::BN + 32 * sb;
-            if (!(c.r0 < T && kb0 < T && (!CAUSAL || kb0 <= c.r0 + 31))) continue;
-            f32x16 p = block_scores<D>(sK[buf], 32 * sb, qv, col, half);
-            const bool edge = (CAUSAL && kb0 + 31 > c.r0) || kb0 + 32 > T;
+            if (!(live && kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) continue;
+            f32x16 p = block_scores<D>(sK, 32 * sb, qv, col, half);
+            const bool edge = (CAUSAL && kb0 + 31 > r0) || kb0 + 32 > T;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int key = kb0 + acc_row(v, half);
                 const bool masked = edge && ((CAUSAL && key > qrow) || key >= T);
                 p[v] = masked ? 0.f : fast_exp2(fmaf(p[v], a.qscale, -lse2));
             }
-            f32x16 ds = block_scores<D>(sV[buf], 32 * sb, dov, col, half);  // dP^T = V dO^T
+            f32x16 ds = block_scores<D>(sV, 32 * sb, dov, col, half);  // dP^T = V dO^T
 #pragma unroll
             for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
-            block_accum<D>(acc, sK[buf], 32 * sb, ds, lane);  // dQ^T += K^T dS^T
+            const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
+            block_accum_x<D>(acc, sK, 32 * sb, db, lane);  // dQ^T += K^T dS^T
         }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw);
-        __syncthreads();
+        if (j + 2 < ntiles) kv.issue(kg, vg, j + 2, T, ring + ((j + 2) % R::NST) * R::SB);
     }
 
     if (qrow < T) {
@@ -460,14 +515,13 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c,
 template <int D, bool CAUSAL, bool ROPE>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_DQ_WAVES_PER_EU)))
 dq_bf16(ArgsB a) {
-    __shared__ __attribute__((aligned(16))) unsigned char sK[2][CfgB<D>::BN * CfgB<D>::RB];
-    __shared__ __attribute__((aligned(16))) unsigned char sV[2][CfgB<D>::BN * CfgB<D>::RB];
+    __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
     const int wave = threadIdx.x >> 6;
     const QWorkB w = decode_qwork_b(a);
-    dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), sK, sV);
+    dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), ring);
     if (w.qt1 >= 0) {
         __syncthreads();
-        dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt1, wave), sK, sV);
+        dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt1, wave), ring);
     }
 }
 

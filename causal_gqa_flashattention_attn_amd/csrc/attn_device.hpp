@@ -103,6 +103,10 @@ __device__ __forceinline__ bf16x4 tile_read_tr4(const unsigned char *t, int k0, 
         (lds_bf16x4 *)(uintptr_t)(t + tile_off<D>(row, col)));
 }
 
+__device__ __forceinline__ bf16x8 join8(const bf16x4 &lo, const bf16x4 &hi) {
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // 8 keys of the transposed operand: (k0 .. +3) from the first read, (k0 + 8 .. +11) from the
 // second, matching the rows held in accumulator registers 8 s .. 8 s + 7 of a lane half.
 template <int D>
@@ -112,12 +116,64 @@ __device__ __forceinline__ bf16x8 tile_read_tr8(const unsigned char *t, int k0, 
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Reductions over the two halves of the wave (lanes l and l ^ 32), result in every lane.
+// v_permlane32_swap(a, b) returns {[a_lo, b_lo], [a_hi, b_hi]} (32-lane halves), so with a = b = x
+// the two results hold x_lo and x_hi in every lane; both halves combine them in the same order.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16 bytes per lane copied from global memory straight into LDS (global_load_lds_dwordx4): lane
+// l writes bytes [16 l, 16 l + 16) of the wave-uniform destination `lds`, from its own address
+// `src`.  No registers are involved; completion is tracked by the vector memory counter.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+__device__ __forceinline__ void dma16(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)lds, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a wave-uniform n: waits until at most n of this wave's
+// vector memory operations are outstanding (n above 8 waits as for 8) and its LDS operations
+// have completed.
+__device__ __forceinline__ void wait_vm_lgkm0(int n) {
+#define NE_VM(N) __builtin_amdgcn_s_waitcnt((N) | (7 << 4))  // expcnt: no wait, lgkmcnt(0)
+    if (n <= 0) NE_VM(0);
+    else if (n == 1) NE_VM(1);
+    else if (n == 2) NE_VM(2);
+    else if (n == 3) NE_VM(3);
+    else if (n == 4) NE_VM(4);
+    else if (n == 5) NE_VM(5);
+    else if (n == 6) NE_VM(6);
+    else if (n == 7) NE_VM(7);
+    else NE_VM(8);
+#undef NE_VM
+}
+
 // Registers 8 s .. 8 s + 7 of an accumulator tile, rounded to bf16, as an MFMA operand.
 __device__ __forceinline__ bf16x8 pack8(const f32x16 &x, int s) {
     bf16x8 r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[8 * s + i];
     return r;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + the sum of the eight bf16 values of v (four v_dot2c_f32_bf16 against ones, in order).
+__device__ __forceinline__ float sum8_bf16(const bf16x8 &v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+    return acc;
 }
 
 }  // namespace ne
