@@ -525,12 +525,17 @@ dq_bf16(ArgsB a) {
     }
 }
 
+// Row stride (floats) of the fp32 partial dK, dV rows in the final reduction: 16 bytes of
+// padding put the rows that 16 lanes write at once in different banks.
+template <int D>
+constexpr int dkdv_red_ld() { return D + 4; }
+
 // LDS bytes per dK/dV wave: the larger of the staged query/dO tiles (+ lse2, delta) and the
 // fp32 partial dK, dV it contributes to the final reduction.
 template <int D>
 constexpr int dkdv_wave_bytes_b() {
     constexpr int stage = 2 * 32 * CfgB<D>::RB + 2 * 32 * 4;
-    constexpr int red = 2 * 32 * D * 4;
+    constexpr int red = 2 * 32 * dkdv_red_ld<D>() * 4;
     return stage > red ? stage : red;
 }
 
@@ -539,7 +544,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
                                              unsigned char *smem_b) {
     using C = CfgB<D>;
     const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
     const size_t bg = (size_t)b * a.Hkv + g;
@@ -592,7 +598,18 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         const int i = i0 + it % per_head;
         // Only this wave reads its staging area: ordering within the wave suffices.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        {
+        if (i * 32 + 32 <= T) {
+#pragma unroll
+            for (int pc = 0; pc < PC; ++pc) {
+                const int r = (lane + 64 * pc) / C::NCH;
+                *reinterpret_cast<bf16x8 *>(sQ + tile_off<D>(r, 8 * sch)) = pq[pc];
+                *reinterpret_cast<bf16x8 *>(sO + tile_off<D>(r, 8 * sch)) = pd[pc];
+            }
+            if (lane < 32) {
+                sL[lane] = plse * kLog2e;
+                sDl[lane] = pdl;
+            }
+        } else {  // the last query block, with padding rows: zeros, and P = 0 there
             const bf16x8 zero = {};
 #pragma unroll
             for (int pc = 0; pc < PC; ++pc) {
@@ -603,7 +620,7 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
             }
             if (lane < 32) {
                 const bool valid = i * 32 + lane < T;
-                sL[lane] = valid ? plse * kLog2e : INFINITY;  // padding rows get P = 0
+                sL[lane] = valid ? plse * kLog2e : INFINITY;
                 sDl[lane] = valid ? pdl : 0.f;
             }
         }
@@ -616,16 +633,16 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
 #pragma unroll
         for (int st = 0; st < C::KS; ++st)
             p = mfma32_bf16(tile_read8<D>(sQ, col, 16 * st + 8 * half), kv[st], p);
-        const bool diag = CAUSAL && i == kb;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const f32x4 L = ld4(sL + 8 * u + 4 * half);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int v = 4 * u + e;
-                const bool masked = diag && krow > i * 32 + acc_row(v, half);
-                p[v] = masked ? 0.f : fast_exp2(fmaf(p[v], a.qscale, -L[e]));
-            }
+            for (int e = 0; e < 4; ++e) p[4 * u + e] = fast_exp2(fmaf(p[4 * u + e], a.qscale, -L[e]));
+        }
+        if (CAUSAL && i == kb) {  // the diagonal block: keys after the query get P = 0
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if (col > acc_row(v, half)) p[v] = 0.f;
         }
         // dP = dO V^T
         f32x16 ds = zero16();
@@ -654,9 +671,10 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int d = 32 * dd + 8 * u + 4 * half;
-                st4(R + col * D + d, f32x4{dk[dd][4 * u] * a.scale, dk[dd][4 * u + 1] * a.scale,
-                                           dk[dd][4 * u + 2] * a.scale, dk[dd][4 * u + 3] * a.scale});
-                st4(R + 32 * D + col * D + d,
+                constexpr int LD = dkdv_red_ld<D>();
+                st4(R + col * LD + d, f32x4{dk[dd][4 * u] * a.scale, dk[dd][4 * u + 1] * a.scale,
+                                            dk[dd][4 * u + 2] * a.scale, dk[dd][4 * u + 3] * a.scale});
+                st4(R + 32 * LD + col * LD + d,
                     f32x4{dv[dd][4 * u], dv[dd][4 * u + 1], dv[dd][4 * u + 2], dv[dd][4 * u + 3]});
             }
     }
@@ -668,7 +686,7 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         f32x4 sum{0.f, 0.f, 0.f, 0.f};
         for (int w = 0; w < nw; ++w)
             sum += ld4(reinterpret_cast<const float *>(smem_b + w * dkdv_wave_bytes_b<D>()) +
-                       t * 32 * D + r * D + cc);
+                       (t * 32 + r) * dkdv_red_ld<D>() + cc);
         const int row = kb * 32 + r;
         if (row < T) {
             float x[4] = {sum[0], sum[1], sum[2], sum[3]};
