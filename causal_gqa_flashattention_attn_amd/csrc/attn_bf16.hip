@@ -481,16 +481,18 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int kb0 = j * C::BN + 32 * sb;
-            if (!(live && kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) continue;
+            if (!(live && kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) break;  // so is the next
             f32x16 p = block_scores<D>(sK, 32 * sb, qv, col, half);
-            const bool edge = (CAUSAL && kb0 + 31 > r0) || kb0 + 32 > T;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = kb0 + acc_row(v, half);
-                const bool masked = edge && ((CAUSAL && key > qrow) || key >= T);
-                p[v] = masked ? 0.f : fast_exp2(fmaf(p[v], a.qscale, -lse2));
-            }
             f32x16 ds = block_scores<D>(sV, 32 * sb, dov, col, half);  // dP^T = V dO^T
+#pragma unroll
+            for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(p[v], a.qscale, -lse2));
+            if ((CAUSAL && kb0 + 31 > r0) || kb0 + 32 > T) {  // a block on the diagonal or the end
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kb0 + acc_row(v, half);
+                    if ((CAUSAL && key > qrow) || key >= T) p[v] = 0.f;
+                }
+            }
 #pragma unroll
             for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
             const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
