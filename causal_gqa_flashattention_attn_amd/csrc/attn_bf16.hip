@@ -409,7 +409,7 @@ template <int D, bool CAUSAL, bool ROPE>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_FWD_WAVES_PER_EU)))
 fwd_bf16(ArgsB a) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const QWorkB w = decode_qwork_b(a);
     fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), ring);
     if (w.qt1 >= 0) {
@@ -518,7 +518,7 @@ template <int D, bool CAUSAL, bool ROPE>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_DQ_WAVES_PER_EU)))
 dq_bf16(ArgsB a) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const QWorkB w = decode_qwork_b(a);
     dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), ring);
     if (w.qt1 >= 0) {

@@ -249,7 +249,8 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
                                          float (&sV)[2][32 * Cfg<D>::LD]) {
     using C = Cfg<D>;
     const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
     const int qrow = c.r0 + col;
@@ -329,7 +330,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_FWD
 fwd_f32(Args a) {
     __shared__ __attribute__((aligned(16))) float sK[2][32 * Cfg<D>::LD];
     __shared__ __attribute__((aligned(16))) float sV[2][32 * Cfg<D>::LD];
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const QTileWork w = decode_qwork(a);
     fwd_tile<D, CAUSAL, ROPE>(a, qtile_of(a, w, w.qt0, wave), sK, sV);
     if (w.qt1 >= 0) {
@@ -343,7 +344,8 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
                                         float (&sV)[2][32 * Cfg<D>::LD]) {
     using C = Cfg<D>;
     const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
     const int qrow = c.r0 + col;
@@ -393,14 +395,16 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
         const int k0 = j * 32;
         if (c.r0 < T && (!CAUSAL || k0 <= c.r0 + 31)) {
             f32x16 p = scores_t<D>(sK[buf], qr, col, half);
-            const bool edge = (CAUSAL && k0 + 31 > c.r0) || k0 + 32 > T;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = k0 + acc_row(v, half);
-                const bool masked = edge && ((CAUSAL && key > qrow) || key >= T);
-                p[v] = masked ? 0.f : fast_exp2(p[v] - lse2);
-            }
             f32x16 ds = scores_t<D>(sV[buf], dor, col, half);  // dP^T = V dO^T
+#pragma unroll
+            for (int v = 0; v < 16; ++v) p[v] = fast_exp2(p[v] - lse2);
+            if ((CAUSAL && k0 + 31 > c.r0) || k0 + 32 > T) {  // a block on the diagonal or the end
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = k0 + acc_row(v, half);
+                    if ((CAUSAL && key > qrow) || key >= T) p[v] = 0.f;
+                }
+            }
 #pragma unroll
             for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
             accum_t<D>(acc, sK[buf], ds, col, half);  // dQ^T += K^T dS^T
@@ -429,7 +433,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_DQ_
 dq_f32(Args a) {
     __shared__ __attribute__((aligned(16))) float sK[2][32 * Cfg<D>::LD];
     __shared__ __attribute__((aligned(16))) float sV[2][32 * Cfg<D>::LD];
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const QTileWork w = decode_qwork(a);
     dq_tile<D, CAUSAL, ROPE>(a, qtile_of(a, w, w.qt0, wave), sK, sV);
     if (w.qt1 >= 0) {
@@ -446,7 +450,8 @@ template <int D, bool CAUSAL, bool ROPE>
 __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, float *smem) {
     using C = Cfg<D>;
     const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
     const size_t bg = (size_t)b * a.Hkv + g;
@@ -517,16 +522,16 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
         // S = Q K'^T (rows: queries acc_row(v, half) of the block; column: this lane's key)
         f32x16 p = chain_lds4<C::NS>(sQ + col * C::LD + C::NS * half, kr, zero16());
         // P = exp2(S - lse2): independent of the dP chain below, so the two can overlap.
-        const bool diag = CAUSAL && i == kb;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const f32x4 L = ld4(sL + 8 * u + 4 * half);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int v = 4 * u + e;
-                const bool masked = diag && krow > i * 32 + acc_row(v, half);
-                p[v] = masked ? 0.f : fast_exp2(p[v] - L[e]);
-            }
+            for (int e = 0; e < 4; ++e) p[4 * u + e] = fast_exp2(p[4 * u + e] - L[e]);
+        }
+        if (CAUSAL && i == kb) {  // the diagonal block: keys after the query get P = 0
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if (col > acc_row(v, half)) p[v] = 0.f;
         }
         // dP = dO V^T
         f32x16 ds = chain_lds4<C::NS>(sO + col * C::LD + C::NS * half, vr, zero16());
