@@ -51,6 +51,7 @@ struct ArgsB {
     const __bf16 *q, *k, *v, *o, *dO;
     const float *lse;
     __bf16 *out_o, *dq, *dk, *dv;
+    __bf16 *qrot;   // dQ pass with RoPE: rotated query rows, written for the dK/dV pass
     float *out_lse, *delta;
     int B, Hq, Hkv, T, G;
     int hpw, rb, nqt;
@@ -434,7 +435,12 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
     const __bf16 *vg = a.v + bg * T * D;
 
     bf16x8 qv[C::KS], dov[C::KS];
-    load_operand_row<D, false>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
+    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
+    if (ROPE && qrow < T) {  // each query row is loaded by exactly one wave: keep its rotation
+#pragma unroll
+        for (int st = 0; st < C::KS; ++st)
+            *reinterpret_cast<bf16x8 *>(a.qrot + (bh * T + qrow) * D + 16 * st + 8 * half) = qv[st];
+    }
     load_operand_row<D, false>(dov, a.dO + bh * T * D, qrow, T, half, 0.f);
 
     // delta_i = sum_d dO_id o_id over this row (fp32), written once for the dK/dV pass.
@@ -801,7 +807,7 @@ hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const v
 
 hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const void *v,
                           const void *o, const float *lse, const void *dO, void *dq, float *delta,
-                          hipStream_t st) {
+                          void *qrot, hipStream_t st) {
     ArgsB a = make_args_b(s);
     a.q = static_cast<const __bf16 *>(q);
     a.k = static_cast<const __bf16 *>(k);
@@ -811,6 +817,7 @@ hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const vo
     a.dO = static_cast<const __bf16 *>(dO);
     a.dq = static_cast<__bf16 *>(dq);
     a.delta = delta;
+    a.qrot = static_cast<__bf16 *>(qrot);
     const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.dq != 0);
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;

@@ -92,6 +92,7 @@ __device__ __forceinline__ f32x4 rope4(f32x4 x, int t, int c, const RopeArgs &r,
 struct Args {
     const float *q, *k, *v, *o, *lse, *dO;
     float *out_o, *out_lse, *dq, *dk, *dv, *delta;
+    float *qrot;  // dQ pass with RoPE: rotated query rows, written for the dK/dV pass
     int B, Hq, Hkv, T, G;
     int hpw, rb, nqt;  // query-tile kernels
     int paired;        // work-groups take mirrored pairs of tiles or key blocks
@@ -354,7 +355,17 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
     const float *vg = a.v + bg * T * D;
 
     float qr[C::NS], dor[C::NS];
-    load_row_half<D, false>(qr, a.q + bh * T * D, qrow, T, half, a.qscale, a.rope);
+    load_row_half<D, ROPE>(qr, a.q + bh * T * D, qrow, T, half, ROPE ? 1.0f : a.qscale, a.rope);
+    if (ROPE) {  // each query row is loaded by exactly one wave: keep its rotation, then scale
+        if (qrow < T) {
+#pragma unroll
+            for (int c = 0; c < C::NS / 4; ++c)
+                st4(a.qrot + (bh * T + qrow) * D + C::NS * half + 4 * c,
+                    f32x4{qr[4 * c], qr[4 * c + 1], qr[4 * c + 2], qr[4 * c + 3]});
+        }
+#pragma unroll
+        for (int i = 0; i < C::NS; ++i) qr[i] *= a.qscale;
+    }
     load_row_half<D, false>(dor, a.dO + bh * T * D, qrow, T, half, 1.0f, a.rope);
 
     // delta_i = sum_d dO_id o_id over this row; written once per row for the dK/dV pass.
@@ -703,7 +714,7 @@ hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const 
 
 hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const float *v,
                          const float *o, const float *lse, const float *dO, float *dq,
-                         float *delta, hipStream_t st) {
+                         float *delta, float *qrot, hipStream_t st) {
     Args a = make_args(s);
     a.q = q;
     a.k = k;
@@ -713,6 +724,7 @@ hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const f
     a.dO = dO;
     a.dq = dq;
     a.delta = delta;
+    a.qrot = qrot;
     const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.dq != 0);
     a.hpw = g.hpw;
     a.rb = g.rb;

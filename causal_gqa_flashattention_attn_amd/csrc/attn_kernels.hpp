@@ -59,15 +59,16 @@ struct PairPolicy {
 constexpr PairPolicy kPairF32{NE_PAIR_F32};
 constexpr PairPolicy kPairBf16{NE_PAIR_BF16};
 
-// With RoPE (s.rope_base > 0) the kernels expect rotated inputs where they stream a tensor
-// through LDS: the forward takes rotated k (and rotates each query row itself), the dQ and
-// dK/dV passes take rotated q and k, and rotate dq and dk back before storing them.
+// With RoPE (s.rope_base > 0) the kernels take rotated k, since they stream it through LDS.
+// The forward and the dQ pass rotate each query row as they load it; the dQ pass also writes
+// the rotated rows to `qrot`, which the dK/dV pass then takes as q (it streams q through LDS).
+// dq and dk are rotated back before they are stored.
 hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const float *v,
                           float *o, float *lse, hipStream_t st);
-// dQ pass: writes dq and delta (= rowsum(dO * o)).
+// dQ pass: writes dq, delta (= rowsum(dO * o)) and, with RoPE, the rotated q to qrot.
 hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const float *v,
                          const float *o, const float *lse, const float *dO, float *dq,
-                         float *delta, hipStream_t st);
+                         float *delta, float *qrot, hipStream_t st);
 // dK/dV pass: reads delta written by the dQ pass.
 hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const float *v,
                            const float *lse, const float *dO, const float *delta, float *dk,
@@ -78,7 +79,7 @@ hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const v
                            float *lse, hipStream_t st);
 hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const void *v,
                           const void *o, const float *lse, const void *dO, void *dq, float *delta,
-                          hipStream_t st);
+                          void *qrot, hipStream_t st);
 hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const void *v,
                             const float *lse, const void *dO, const float *delta, void *dk,
                             void *dv, hipStream_t st);

@@ -113,24 +113,24 @@ int dq_impl(const void *q, const void *k, const void *v, const void *o, const fl
     if (any_misaligned({q, k, v, o, lse, dO, dq, ws})) return NE_ERR_ALIGN;
     const WsLayout L = ws_layout(s, dtype);
     float *delta = static_cast<float *>(ws);
-    const void *qq = q, *kk = k;
+    const void *kk = k;
+    void *qr = nullptr;
     if (s.rope_base > 0.f) {
-        // Queries and keys rotated once into the workspace, for this pass and the dK/dV pass.
-        void *qr = static_cast<char *>(ws) + L.qr;
+        // Keys rotated once into the workspace for both passes; the dQ pass rotates each query
+        // row as it loads it and leaves the rotated rows in the workspace for the dK/dV pass.
         void *kr = static_cast<char *>(ws) + L.kr;
-        if (launch_rope(s, dtype, q, qr, (long long)B * Hq * T, stream) != hipSuccess ||
-            launch_rope(s, dtype, k, kr, (long long)B * Hkv * T, stream) != hipSuccess)
+        if (launch_rope(s, dtype, k, kr, (long long)B * Hkv * T, stream) != hipSuccess)
             return NE_ERR_HIP;
-        qq = qr;
         kk = kr;
+        qr = static_cast<char *>(ws) + L.qr;
     }
     const hipError_t e =
         dtype == NE_BF16
-            ? ne::launch_dq_bf16(s, qq, kk, v, o, lse, dO, dq, delta, stream)
-            : ne::launch_dq_f32(s, static_cast<const float *>(qq), static_cast<const float *>(kk),
+            ? ne::launch_dq_bf16(s, q, kk, v, o, lse, dO, dq, delta, qr, stream)
+            : ne::launch_dq_f32(s, static_cast<const float *>(q), static_cast<const float *>(kk),
                                 static_cast<const float *>(v), static_cast<const float *>(o), lse,
                                 static_cast<const float *>(dO), static_cast<float *>(dq), delta,
-                                stream);
+                                static_cast<float *>(qr), stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
