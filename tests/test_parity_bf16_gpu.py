@@ -32,6 +32,9 @@ def test_bf16_rope_workload(ne, oracle_mod):
 BF16_CASES = [
     (1, 4, 2, 64, 32), (2, 12, 4, 130, 64), (1, 6, 3, 517, 64), (1, 16, 4, 256, 64),
     (1, 2, 1, 100, 64), (1, 8, 2, 33, 32), (2, 5, 5, 1, 64),
+    # group sizes 5..8: 5..8 waves share each staged K/V tile, some copying a piece twice
+    (1, 10, 2, 77, 64), (1, 6, 1, 100, 64), (1, 7, 1, 90, 32), (1, 8, 1, 200, 64),
+    (1, 7, 1, 130, 64),
 ]
 
 

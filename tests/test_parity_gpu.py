@@ -39,6 +39,8 @@ RAGGED = [
     (1, 4, 2, 1, 32), (1, 3, 1, 17, 64), (2, 4, 4, 37, 32), (1, 6, 2, 65, 64),
     (1, 2, 1, 100, 64), (1, 8, 2, 130, 32), (2, 12, 4, 255, 64), (1, 16, 2, 33, 64),
     (1, 5, 5, 96, 32), (1, 1, 1, 31, 64), (3, 2, 2, 7, 64),
+    # group sizes 5..8: work-groups of 5..8 waves
+    (1, 10, 2, 77, 64), (1, 6, 1, 100, 64), (1, 7, 1, 90, 32), (1, 8, 1, 200, 64),
 ]
 
 
