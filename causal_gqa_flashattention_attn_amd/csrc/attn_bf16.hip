@@ -260,6 +260,40 @@ __device__ __forceinline__ void block_accum(f32x16 (&acc)[CfgB<D>::ND], const un
     }
 }
 
+// block_accum for a tile that LDS copies may be filling concurrently: the transposed operand
+// is read with tile_read_tr4_asm, all reads first, and each product waits only for its own two
+// reads (reads issued later may still be in flight).
+template <int D>
+__device__ __forceinline__ void block_accum_async(f32x16 (&acc)[CfgB<D>::ND],
+                                                  const unsigned char *tile, int r0,
+                                                  const f32x16 &x, int lane) {
+    constexpr int ND = CfgB<D>::ND;
+    bf16x4 lo[2][ND], hi[2][ND];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dd = 0; dd < ND; ++dd) {
+            lo[s2][dd] = tile_read_tr4_asm<D>(tile, r0 + 16 * s2, 32 * dd, lane);
+            hi[s2][dd] = tile_read_tr4_asm<D>(tile, r0 + 16 * s2 + 8, 32 * dd, lane);
+        }
+    const bf16x8 xb[2] = {pack8(x, 0), pack8(x, 1)};
+    if constexpr (ND == 2) {
+        lds_wait_n<6>(lo[0][0], hi[0][0]);
+        acc[0] = mfma32_bf16(join8(lo[0][0], hi[0][0]), xb[0], acc[0]);
+        lds_wait_n<4>(lo[0][1], hi[0][1]);
+        acc[1] = mfma32_bf16(join8(lo[0][1], hi[0][1]), xb[0], acc[1]);
+        lds_wait_n<2>(lo[1][0], hi[1][0]);
+        acc[0] = mfma32_bf16(join8(lo[1][0], hi[1][0]), xb[1], acc[0]);
+        lds_wait_n<0>(lo[1][1], hi[1][1]);
+        acc[1] = mfma32_bf16(join8(lo[1][1], hi[1][1]), xb[1], acc[1]);
+    } else {
+        lds_wait_n<2>(lo[0][0], hi[0][0]);
+        acc[0] = mfma32_bf16(join8(lo[0][0], hi[0][0]), xb[0], acc[0]);
+        lds_wait_n<0>(lo[1][0], hi[1][0]);
+        acc[0] = mfma32_bf16(join8(lo[1][0], hi[1][0]), xb[1], acc[0]);
+    }
+}
+
 // acc (D x 32, transposed) += M_tile[r0 .. r0+31]^T x X, X given as its two bf16 operand halves.
 template <int D>
 __device__ __forceinline__ void block_accum_x(f32x16 (&acc)[CfgB<D>::ND], const unsigned char *tile,
@@ -538,11 +572,25 @@ dq_bf16(ArgsB a) {
 template <int D>
 constexpr int dkdv_red_ld() { return D + 4; }
 
-// LDS bytes per dK/dV wave: the larger of the staged query/dO tiles (+ lse2, delta) and the
-// fp32 partial dK, dV it contributes to the final reduction.
+// Staging of the dK/dV items.  Each wave copies its own (query head, 32-row query block) items
+// straight into two private LDS stages, one item ahead: the query tile and the dO tile in the
+// swizzled layout (NPQ 1 KB pieces each, laid out as in KVRingB), then the 32 lse and the 32
+// delta values of the rows in one 256-byte copy.  Every wave issues NDMA copies per item.
+template <int D>
+struct ItemStageB {
+    using C = CfgB<D>;
+    static constexpr int TBQ = 32 * C::RB;      // bytes of a 32-row tile
+    static constexpr int NPQ = TBQ / 1024;      // 1 KB pieces per tile
+    static constexpr int RPP = 1024 / C::RB;    // tile rows per piece
+    static constexpr int SB = 2 * TBQ + 256;    // bytes of a stage
+    static constexpr int NDMA = 2 * NPQ + 1;    // copies per item
+};
+
+// LDS bytes per dK/dV wave: the larger of its two item stages and the fp32 partial dK, dV it
+// contributes to the final reduction.
 template <int D>
 constexpr int dkdv_wave_bytes_b() {
-    constexpr int stage = 2 * 32 * CfgB<D>::RB + 2 * 32 * 4;
+    constexpr int stage = 2 * ItemStageB<D>::SB;
     constexpr int red = 2 * 32 * dkdv_red_ld<D>() * 4;
     return stage > red ? stage : red;
 }
@@ -551,6 +599,7 @@ template <int D, bool CAUSAL, bool ROPE>
 __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int kb,
                                              unsigned char *smem_b) {
     using C = CfgB<D>;
+    using S = ItemStageB<D>;
     const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -562,6 +611,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     bf16x8 kv[C::KS], vv[C::KS];
     load_operand_row<D, false>(kv, a.k + bg * T * D, krow, T, half, a.rope_lb);
     load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, 0.f);
+    wait_vm_lgkm0(0);  // the K, V rows have arrived before the first item copy is issued
+    __builtin_amdgcn_sched_barrier(0);
 
     f32x16 dk[C::ND], dv[C::ND];
 #pragma unroll
@@ -570,77 +621,67 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         dv[dd] = zero16();
     }
 
-    unsigned char *wbuf = smem_b + wave * dkdv_wave_bytes_b<D>();
-    unsigned char *sQ = wbuf;
-    unsigned char *sO = wbuf + 32 * C::RB;
-    float *sL = reinterpret_cast<float *>(wbuf + 2 * 32 * C::RB);
-    float *sDl = sL + 32;
-
     const int nqb = (T + 31) / 32;
     const int i0 = CAUSAL ? kb : 0;
     const int per_head = nqb - i0;
     const int nitems = a.G * per_head;
 
-    // Staging of one item (query head hh, query block i): each lane moves 32*NCH/64 chunks of
-    // the query tile and of the dO tile, held in registers one item ahead.
-    constexpr int PC = 32 * C::NCH / 64;
-    const int sch = lane % C::NCH;  // fixed column chunk of this lane
-    bf16x8 pq[PC], pd[PC];
-    float plse = 0.f, pdl = 0.f;
-    auto prefetch = [&](int it) {
+    // This lane's 16 bytes of a piece: row lrow of the piece, swizzled chunk (by row parity).
+    const int lrow = lane / C::NCH;
+    const int off0 = 2 * (lrow * D + 8 * chunk_swizzle<D>(lrow, lane % C::NCH));
+    const int off1 = 2 * (lrow * D + 8 * chunk_swizzle<D>(S::RPP + lrow, lane % C::NCH));
+    // Starts the copies of item `it` into `st`.  Rows past the end read row T - 1; their lse is
+    // replaced by +inf once the item has landed, so their probabilities are 0.
+    auto issue = [&](int it, unsigned char *st) {
         const int hh = it / per_head, i = i0 + it % per_head;
         const size_t bh = (size_t)b * a.Hq + (size_t)g * a.G + hh;
+        const unsigned char *qb = reinterpret_cast<const unsigned char *>(a.q + bh * T * D);
+        const unsigned char *ob = reinterpret_cast<const unsigned char *>(a.dO + bh * T * D);
+        const bool whole = i * 32 + 32 <= T;
 #pragma unroll
-        for (int pc = 0; pc < PC; ++pc) {
-            const int row = min(i * 32 + (lane + 64 * pc) / C::NCH, T - 1);
-            pq[pc] = *reinterpret_cast<const bf16x8 *>(a.q + (bh * T + row) * D + 8 * sch);
-            pd[pc] = *reinterpret_cast<const bf16x8 *>(a.dO + (bh * T + row) * D + 8 * sch);
+        for (int pc = 0; pc < S::NPQ; ++pc) {
+            const int row0 = i * 32 + pc * S::RPP;
+            const int off = (pc & 1) ? off1 : off0;
+            if (whole) {
+                dma16(qb + (size_t)row0 * (2 * D) + off, st + pc * 1024);
+                dma16(ob + (size_t)row0 * (2 * D) + off, st + S::TBQ + pc * 1024);
+            } else {
+                const int r = min(row0 + lrow, T - 1);
+                const int o = off - 2 * lrow * D;
+                dma16(qb + (size_t)r * (2 * D) + o, st + pc * 1024);
+                dma16(ob + (size_t)r * (2 * D) + o, st + S::TBQ + pc * 1024);
+            }
         }
-        const int lrow = min(i * 32 + col, T - 1);
-        plse = a.lse[bh * T + lrow];
-        pdl = a.delta[bh * T + lrow];
+        const int r = min(i * 32 + col, T - 1);  // lanes 0..31: lse, lanes 32..63: delta
+        dma4((half ? a.delta : a.lse) + bh * T + r, st + 2 * S::TBQ);
     };
 
-    if (wave < nitems) prefetch(wave);
-    for (int it = wave; it < nitems; it += nw) {
+    unsigned char *wbuf = smem_b + wave * dkdv_wave_bytes_b<D>();
+    if (wave < nitems) issue(wave, wbuf);
+    if (wave + nw < nitems) issue(wave + nw, wbuf + S::SB);
+    int k = 0;
+    for (int it = wave; it < nitems; it += nw, ++k) {
         const int i = i0 + it % per_head;
-        // Only this wave reads its staging area: ordering within the wave suffices.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        if (i * 32 + 32 <= T) {
-#pragma unroll
-            for (int pc = 0; pc < PC; ++pc) {
-                const int r = (lane + 64 * pc) / C::NCH;
-                *reinterpret_cast<bf16x8 *>(sQ + tile_off<D>(r, 8 * sch)) = pq[pc];
-                *reinterpret_cast<bf16x8 *>(sO + tile_off<D>(r, 8 * sch)) = pd[pc];
-            }
-            if (lane < 32) {
-                sL[lane] = plse * kLog2e;
-                sDl[lane] = pdl;
-            }
-        } else {  // the last query block, with padding rows: zeros, and P = 0 there
-            const bf16x8 zero = {};
-#pragma unroll
-            for (int pc = 0; pc < PC; ++pc) {
-                const int r = (lane + 64 * pc) / C::NCH;
-                const int row = i * 32 + r;
-                *reinterpret_cast<bf16x8 *>(sQ + tile_off<D>(r, 8 * sch)) = row < T ? pq[pc] : zero;
-                *reinterpret_cast<bf16x8 *>(sO + tile_off<D>(r, 8 * sch)) = row < T ? pd[pc] : zero;
-            }
-            if (lane < 32) {
-                const bool valid = i * 32 + lane < T;
-                sL[lane] = valid ? plse * kLog2e : INFINITY;
-                sDl[lane] = valid ? pdl : 0.f;
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        prefetch(min(it + nw, nitems - 1));  // unconditional: the last item is fetched again
+        unsigned char *st = wbuf + (k & 1) * S::SB;
+        const unsigned char *sQ = st;
+        const unsigned char *sO = st + S::TBQ;
+        float *sL = reinterpret_cast<float *>(st + 2 * S::TBQ);
+        const float *sDl = sL + 32;
+        // This item's copies have landed (the next item's may still be in flight); the stage
+        // is private to the wave, so no barrier is needed.
+        wait_vm_lgkm0(it + nw < nitems ? S::NDMA : 0);
+        if (lane < 32) sL[lane] = i * 32 + lane < T ? sL[lane] * kLog2e : INFINITY;
 
         // S = Q K'^T (rows: queries acc_row(v, half) of the block; column: this lane's key)
         f32x16 p = zero16();
 #pragma unroll
-        for (int st = 0; st < C::KS; ++st)
-            p = mfma32_bf16(tile_read8<D>(sQ, col, 16 * st + 8 * half), kv[st], p);
+        for (int st2 = 0; st2 < C::KS; ++st2)
+            p = mfma32_bf16(tile_read8<D>(sQ, col, 16 * st2 + 8 * half), kv[st2], p);
+        // dP = dO V^T
+        f32x16 ds = zero16();
+#pragma unroll
+        for (int st2 = 0; st2 < C::KS; ++st2)
+            ds = mfma32_bf16(tile_read8<D>(sO, col, 16 * st2 + 8 * half), vv[st2], ds);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const f32x4 L = ld4(sL + 8 * u + 4 * half);
@@ -652,13 +693,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
             for (int v = 0; v < 16; ++v)
                 if (col > acc_row(v, half)) p[v] = 0.f;
         }
-        // dP = dO V^T
-        f32x16 ds = zero16();
-#pragma unroll
-        for (int st = 0; st < C::KS; ++st)
-            ds = mfma32_bf16(tile_read8<D>(sO, col, 16 * st + 8 * half), vv[st], ds);
         // dV^T += dO^T P
-        block_accum<D>(dv, sO, 0, p, lane);
+        block_accum_async<D>(dv, sO, 0, p, lane);
         // dS = P (dP - delta)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -667,7 +703,9 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
             for (int e = 0; e < 4; ++e) ds[4 * u + e] = p[4 * u + e] * (ds[4 * u + e] - Dl[e]);
         }
         // dK^T += Q^T dS
-        block_accum<D>(dk, sQ, 0, ds, lane);
+        block_accum_async<D>(dk, sQ, 0, ds, lane);
+        // The stage is free once this item's reads are done: copy the item after next into it.
+        if (it + 2 * nw < nitems) issue(it + 2 * nw, st);
     }
 
     // Add the waves' partial sums in LDS (fixed wave order), rotate dK back, round, store.

@@ -103,6 +103,30 @@ __device__ __forceinline__ bf16x4 tile_read_tr4(const unsigned char *t, int k0, 
         (lds_bf16x4 *)(uintptr_t)(t + tile_off<D>(row, col)));
 }
 
+// The transposed read above, issued as inline assembly.  For tiles that LDS copies (dma16)
+// fill, the compiler makes the intrinsic wait for every copy in flight, since it cannot rule
+// out that they alias; it knows nothing of this form, so the caller must pass the result
+// through lds_wait_n before using it.
+template <int D>
+__device__ __forceinline__ bf16x4 tile_read_tr4_asm(const unsigned char *t, int k0, int c0,
+                                                    int lane) {
+    const int row = k0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    typedef __attribute__((address_space(3))) const unsigned char lds_u8;
+    const uint32_t addr = (uint32_t)(uintptr_t)(lds_u8 *)(t + tile_off<D>(row, col));
+    bf16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+
+// s_waitcnt lgkmcnt(N): waits until at most N of this wave's LDS operations are outstanding.
+// They complete in order, so a read followed by N or more later LDS operations of the wave
+// has landed.  a and b pass through the wait, so nothing that uses them moves above it.
+template <int N>
+__device__ __forceinline__ void lds_wait_n(bf16x4 &a, bf16x4 &b) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
 __device__ __forceinline__ bf16x8 join8(const bf16x4 &lo, const bf16x4 &hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
@@ -139,8 +163,13 @@ __device__ __forceinline__ void dma16(const void *src, void *lds) {
     __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)lds, 16, 0, 0);
 }
 
+// 4 bytes per lane, global -> LDS: lane l writes bytes [4 l, 4 l + 4) of `lds`.
+__device__ __forceinline__ void dma4(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)lds, 4, 0, 0);
+}
+
 // s_waitcnt vmcnt(n) lgkmcnt(0) for a wave-uniform n: waits until at most n of this wave's
-// vector memory operations are outstanding (n above 8 waits as for 8) and its LDS operations
+// vector memory operations are outstanding (n above 15 waits as for 15) and its LDS operations
 // have completed.
 __device__ __forceinline__ void wait_vm_lgkm0(int n) {
 #define NE_VM(N) __builtin_amdgcn_s_waitcnt((N) | (7 << 4))  // expcnt: no wait, lgkmcnt(0)
@@ -152,7 +181,14 @@ __device__ __forceinline__ void wait_vm_lgkm0(int n) {
     else if (n == 5) NE_VM(5);
     else if (n == 6) NE_VM(6);
     else if (n == 7) NE_VM(7);
-    else NE_VM(8);
+    else if (n == 8) NE_VM(8);
+    else if (n == 9) NE_VM(9);
+    else if (n == 10) NE_VM(10);
+    else if (n == 11) NE_VM(11);
+    else if (n == 12) NE_VM(12);
+    else if (n == 13) NE_VM(13);
+    else if (n == 14) NE_VM(14);
+    else NE_VM(15);
 #undef NE_VM
 }
 
