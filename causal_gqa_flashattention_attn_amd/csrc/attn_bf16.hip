@@ -260,37 +260,45 @@ __device__ __forceinline__ void block_accum(f32x16 (&acc)[CfgB<D>::ND], const un
     }
 }
 
-// block_accum for a tile that LDS copies may be filling concurrently: the transposed operand
-// is read with tile_read_tr4_asm, all reads first, and each product waits only for its own two
-// reads (reads issued later may still be in flight).
+// A transposed operand M_tile[r0 .. r0+31]^T (D x 32) in flight: read with tile_read_tr4_asm for
+// tiles that LDS copies may be filling concurrently, so it can be requested well before use.
 template <int D>
-__device__ __forceinline__ void block_accum_async(f32x16 (&acc)[CfgB<D>::ND],
-                                                  const unsigned char *tile, int r0,
-                                                  const f32x16 &x, int lane) {
-    constexpr int ND = CfgB<D>::ND;
-    bf16x4 lo[2][ND], hi[2][ND];
+struct TrOperand {
+    bf16x4 lo[2][CfgB<D>::ND], hi[2][CfgB<D>::ND];
+    static constexpr int NREAD = 4 * CfgB<D>::ND;  // LDS reads per operand
+};
+
+template <int D>
+__device__ __forceinline__ void issue_tr(TrOperand<D> &op, const unsigned char *tile, int r0,
+                                         int lane) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int dd = 0; dd < ND; ++dd) {
-            lo[s2][dd] = tile_read_tr4_asm<D>(tile, r0 + 16 * s2, 32 * dd, lane);
-            hi[s2][dd] = tile_read_tr4_asm<D>(tile, r0 + 16 * s2 + 8, 32 * dd, lane);
+        for (int dd = 0; dd < CfgB<D>::ND; ++dd) {
+            op.lo[s2][dd] = tile_read_tr4_asm<D>(tile, r0 + 16 * s2, 32 * dd, lane);
+            op.hi[s2][dd] = tile_read_tr4_asm<D>(tile, r0 + 16 * s2 + 8, 32 * dd, lane);
         }
-    const bf16x8 xb[2] = {pack8(x, 0), pack8(x, 1)};
-    if constexpr (ND == 2) {
-        lds_wait_n<6>(lo[0][0], hi[0][0]);
-        acc[0] = mfma32_bf16(join8(lo[0][0], hi[0][0]), xb[0], acc[0]);
-        lds_wait_n<4>(lo[0][1], hi[0][1]);
-        acc[1] = mfma32_bf16(join8(lo[0][1], hi[0][1]), xb[0], acc[1]);
-        lds_wait_n<2>(lo[1][0], hi[1][0]);
-        acc[0] = mfma32_bf16(join8(lo[1][0], hi[1][0]), xb[1], acc[0]);
-        lds_wait_n<0>(lo[1][1], hi[1][1]);
-        acc[1] = mfma32_bf16(join8(lo[1][1], hi[1][1]), xb[1], acc[1]);
+}
+
+// acc (D x 32, transposed) += op x X, X given as its two bf16 operand halves.  LATER: how many
+// transposed reads were issued after op's; each product waits only for its own two reads.
+template <int D, int LATER>
+__device__ __forceinline__ void accum_tr(f32x16 (&acc)[CfgB<D>::ND], TrOperand<D> &op,
+                                         const bf16x8 (&xb)[2]) {
+    if constexpr (CfgB<D>::ND == 2) {
+        lds_wait_n<LATER + 6>(op.lo[0][0], op.hi[0][0]);
+        acc[0] = mfma32_bf16(join8(op.lo[0][0], op.hi[0][0]), xb[0], acc[0]);
+        lds_wait_n<LATER + 4>(op.lo[0][1], op.hi[0][1]);
+        acc[1] = mfma32_bf16(join8(op.lo[0][1], op.hi[0][1]), xb[0], acc[1]);
+        lds_wait_n<LATER + 2>(op.lo[1][0], op.hi[1][0]);
+        acc[0] = mfma32_bf16(join8(op.lo[1][0], op.hi[1][0]), xb[1], acc[0]);
+        lds_wait_n<LATER>(op.lo[1][1], op.hi[1][1]);
+        acc[1] = mfma32_bf16(join8(op.lo[1][1], op.hi[1][1]), xb[1], acc[1]);
     } else {
-        lds_wait_n<2>(lo[0][0], hi[0][0]);
-        acc[0] = mfma32_bf16(join8(lo[0][0], hi[0][0]), xb[0], acc[0]);
-        lds_wait_n<0>(lo[1][0], hi[1][0]);
-        acc[0] = mfma32_bf16(join8(lo[1][0], hi[1][0]), xb[1], acc[0]);
+        lds_wait_n<LATER + 2>(op.lo[0][0], op.hi[0][0]);
+        acc[0] = mfma32_bf16(join8(op.lo[0][0], op.hi[0][0]), xb[0], acc[0]);
+        lds_wait_n<LATER>(op.lo[1][0], op.hi[1][0]);
+        acc[0] = mfma32_bf16(join8(op.lo[1][0], op.hi[1][0]), xb[1], acc[0]);
     }
 }
 
@@ -682,6 +690,11 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
 #pragma unroll
         for (int st2 = 0; st2 < C::KS; ++st2)
             ds = mfma32_bf16(tile_read8<D>(sO, col, 16 * st2 + 8 * half), vv[st2], ds);
+        // The transposed operands of dV and dK are requested now, so their latency overlaps
+        // the exponentials.
+        TrOperand<D> tdo, tq;
+        issue_tr<D>(tdo, sO, 0, lane);
+        issue_tr<D>(tq, sQ, 0, lane);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const f32x4 L = ld4(sL + 8 * u + 4 * half);
@@ -694,7 +707,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
                 if (col > acc_row(v, half)) p[v] = 0.f;
         }
         // dV^T += dO^T P
-        block_accum_async<D>(dv, sO, 0, p, lane);
+        const bf16x8 pb[2] = {pack8(p, 0), pack8(p, 1)};
+        accum_tr<D, TrOperand<D>::NREAD>(dv, tdo, pb);
         // dS = P (dP - delta)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -703,7 +717,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
             for (int e = 0; e < 4; ++e) ds[4 * u + e] = p[4 * u + e] * (ds[4 * u + e] - Dl[e]);
         }
         // dK^T += Q^T dS
-        block_accum_async<D>(dk, sQ, 0, ds, lane);
+        const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
+        accum_tr<D, 0>(dk, tq, db);
         // The stage is free once this item's reads are done: copy the item after next into it.
         if (it + 2 * nw < nitems) issue(it + 2 * nw, st);
     }
