@@ -178,6 +178,7 @@ template <int D>
 struct KVRingB {
     using C = CfgB<D>;
     static constexpr int NST = 3;                 // stages
+    static constexpr int PD = NST - 1;            // tiles requested ahead of the one in use
     static constexpr int TB = C::BN * C::RB;      // bytes of one K (or V) tile
     static constexpr int SB = 2 * TB;             // bytes of one stage
     static constexpr int PPT = TB / 1024;         // pieces per tensor tile
@@ -395,13 +396,20 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
     const __bf16 *kg = a.k + bg * T * D;
     const __bf16 *vg = a.v + bg * T * D;
 
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
+    const bool live = r0 < T;
+
+    // The first two K/V tiles are requested before the query row, so the two latencies overlap
+    // (the first use of the row then waits for all three).
+    R kv;
+    kv.init(wave, nw, lane);
+#pragma unroll
+    for (int t = 0; t < R::PD; ++t)
+        if (t < ntiles) kv.issue(kg, vg, t, T, ring + t * R::SB);
     bf16x8 qv[C::KS];
     load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
-    // The query row has arrived before the first K/V copy is issued; otherwise the compiler,
-    // unable to count the copies issued inside the loop, waits for all of them where it first
-    // reads the row.
-    wait_vm_lgkm0(0);
-    __builtin_amdgcn_sched_barrier(0);
 
     FwdState<D> st;
 #pragma unroll
@@ -409,27 +417,21 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
     st.m = kNegBig;
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.l4[i] = 0.f;
+    // Everything requested so far has landed before the loop, so the compiler places no wait
+    // for the row inside it.
+    wait_vm_lgkm0(0);
 
-    const int wg_rows = 32 * a.rb;
-    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
-    const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
-    const bool live = r0 < T;
-
-    R kv;
-    kv.init(wave, nw, lane);
-    kv.issue(kg, vg, 0, T, ring);
-    if (ntiles > 1) kv.issue(kg, vg, 1, T, ring + R::SB);
     for (int j = 0; j < ntiles; ++j) {
-        // This wave's copies of tile j have landed (only tile j+1's may be in flight) and its
-        // reads of tile j-1 are done; after the barrier every wave's are, so tile j is complete
-        // and stage (j+2) % NST, last read for tile j-1, is free.
-        wait_vm_lgkm0(j + 1 < ntiles ? kv.lpw : 0);
+        // This wave's copies of tile j have landed (only the next PD - 1 tiles' may be in flight)
+        // and its reads of tile j-1 are done; after the barrier every wave's are, so tile j is
+        // complete and stage (j + PD) % NST, last read for tile j-1, is free.
+        wait_vm_lgkm0(min(R::PD - 1, ntiles - 1 - j) * kv.lpw);
         __builtin_amdgcn_s_barrier();
         const unsigned char *sK = ring + (j % R::NST) * R::SB;
         if (live) fwd_step<D, CAUSAL>(a, st, sK, sK + R::TB, j * C::BN, r0, T, qv, lane);
         // Issued after this tile's reads: the compiler makes transposed LDS reads wait for every
         // copy in flight, and by the next tile's reads these have landed.
-        if (j + 2 < ntiles) kv.issue(kg, vg, j + 2, T, ring + ((j + 2) % R::NST) * R::SB);
+        if (j + R::PD < ntiles) kv.issue(kg, vg, j + R::PD, T, ring + ((j + R::PD) % R::NST) * R::SB);
     }
 
     const float l = sum_halves((st.l4[0] + st.l4[1]) + (st.l4[2] + st.l4[3]));
@@ -476,6 +478,17 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
     const __bf16 *kg = a.k + bg * T * D;
     const __bf16 *vg = a.v + bg * T * D;
 
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
+    const bool live = r0 < T;
+
+    // The first two K/V tiles are requested before the rows, so the latencies overlap.
+    R kv;
+    kv.init(wave, nw, lane);
+#pragma unroll
+    for (int t = 0; t < R::PD; ++t)
+        if (t < ntiles) kv.issue(kg, vg, t, T, ring + t * R::SB);
     bf16x8 qv[C::KS], dov[C::KS];
     load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
     if (ROPE && qrow < T) {  // each query row is loaded by exactly one wave: keep its rotation
@@ -509,20 +522,10 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
     f32x16 acc[C::ND];
 #pragma unroll
     for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
+    wait_vm_lgkm0(0);  // as in the forward
 
-    const int wg_rows = 32 * a.rb;
-    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
-    const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
-    const bool live = r0 < T;
-    wait_vm_lgkm0(0);  // row loads complete before the first K/V copy (as in the forward)
-    __builtin_amdgcn_sched_barrier(0);
-
-    R kv;
-    kv.init(wave, nw, lane);
-    kv.issue(kg, vg, 0, T, ring);
-    if (ntiles > 1) kv.issue(kg, vg, 1, T, ring + R::SB);
     for (int j = 0; j < ntiles; ++j) {
-        wait_vm_lgkm0(j + 1 < ntiles ? kv.lpw : 0);  // as in the forward
+        wait_vm_lgkm0(min(R::PD - 1, ntiles - 1 - j) * kv.lpw);  // as in the forward
         __builtin_amdgcn_s_barrier();
         const unsigned char *sK = ring + (j % R::NST) * R::SB;
         const unsigned char *sV = sK + R::TB;
@@ -546,7 +549,7 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
             const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
             block_accum_x<D>(acc, sK, 32 * sb, db, lane);  // dQ^T += K^T dS^T
         }
-        if (j + 2 < ntiles) kv.issue(kg, vg, j + 2, T, ring + ((j + 2) % R::NST) * R::SB);
+        if (j + R::PD < ntiles) kv.issue(kg, vg, j + R::PD, T, ring + ((j + R::PD) % R::NST) * R::SB);
     }
 
     if (qrow < T) {
@@ -616,12 +619,6 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     const size_t bg = (size_t)b * a.Hkv + g;
     const int krow = kb * 32 + col;
 
-    bf16x8 kv[C::KS], vv[C::KS];
-    load_operand_row<D, false>(kv, a.k + bg * T * D, krow, T, half, a.rope_lb);
-    load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, 0.f);
-    wait_vm_lgkm0(0);  // the K, V rows have arrived before the first item copy is issued
-    __builtin_amdgcn_sched_barrier(0);
-
     f32x16 dk[C::ND], dv[C::ND];
 #pragma unroll
     for (int dd = 0; dd < C::ND; ++dd) {
@@ -664,9 +661,15 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         dma4((half ? a.delta : a.lse) + bh * T + r, st + 2 * S::TBQ);
     };
 
+    // The first two items are requested before the K, V rows, so the latencies overlap; all of
+    // it has landed before the loop, so the compiler places no wait for the rows inside it.
     unsigned char *wbuf = smem_b + wave * dkdv_wave_bytes_b<D>();
     if (wave < nitems) issue(wave, wbuf);
     if (wave + nw < nitems) issue(wave + nw, wbuf + S::SB);
+    bf16x8 kv[C::KS], vv[C::KS];
+    load_operand_row<D, false>(kv, a.k + bg * T * D, krow, T, half, a.rope_lb);
+    load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, 0.f);
+    wait_vm_lgkm0(0);
     int k = 0;
     for (int it = wave; it < nitems; it += nw, ++k) {
         const int i = i0 + it % per_head;
