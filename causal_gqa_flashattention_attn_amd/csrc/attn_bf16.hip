@@ -20,12 +20,13 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
 
 #ifndef NE_BF16_FWD_WAVES_PER_EU
-#define NE_BF16_FWD_WAVES_PER_EU 2
+#define NE_BF16_FWD_WAVES_PER_EU 3
 #endif
 #ifndef NE_BF16_DQ_WAVES_PER_EU
 #define NE_BF16_DQ_WAVES_PER_EU 3
@@ -421,17 +422,27 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
     // for the row inside it.
     wait_vm_lgkm0(0);
 
-    for (int j = 0; j < ntiles; ++j) {
+    // Tile j uses stage j % NST.  The loop is unrolled over the stages so that each stage's
+    // address is a constant: LDS reads then carry it in their offset field instead of adding it.
+    auto iter = [&](int j, auto stage) {
+        constexpr int ST = decltype(stage)::value;
         // This wave's copies of tile j have landed (only the next PD - 1 tiles' may be in flight)
         // and its reads of tile j-1 are done; after the barrier every wave's are, so tile j is
         // complete and stage (j + PD) % NST, last read for tile j-1, is free.
         wait_vm_lgkm0(min(R::PD - 1, ntiles - 1 - j) * kv.lpw);
         __builtin_amdgcn_s_barrier();
-        const unsigned char *sK = ring + (j % R::NST) * R::SB;
+        const unsigned char *sK = ring + ST * R::SB;
         if (live) fwd_step<D, CAUSAL>(a, st, sK, sK + R::TB, j * C::BN, r0, T, qv, lane);
         // Issued after this tile's reads: the compiler makes transposed LDS reads wait for every
         // copy in flight, and by the next tile's reads these have landed.
-        if (j + R::PD < ntiles) kv.issue(kg, vg, j + R::PD, T, ring + ((j + R::PD) % R::NST) * R::SB);
+        if (j + R::PD < ntiles)
+            kv.issue(kg, vg, j + R::PD, T, ring + ((ST + R::PD) % R::NST) * R::SB);
+    };
+    static_assert(R::NST == 3, "the loop below is unrolled over three stages");
+    for (int j = 0; j < ntiles; j += 3) {
+        iter(j, std::integral_constant<int, 0>{});
+        if (j + 1 < ntiles) iter(j + 1, std::integral_constant<int, 1>{});
+        if (j + 2 < ntiles) iter(j + 2, std::integral_constant<int, 2>{});
     }
 
     const float l = sum_halves((st.l4[0] + st.l4[1]) + (st.l4[2] + st.l4[3]));
@@ -524,10 +535,11 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
     for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
     wait_vm_lgkm0(0);  // as in the forward
 
-    for (int j = 0; j < ntiles; ++j) {
-        wait_vm_lgkm0(min(R::PD - 1, ntiles - 1 - j) * kv.lpw);  // as in the forward
+    auto iter = [&](int j, auto stage) {  // unrolled over the stages, as in the forward
+        constexpr int ST = decltype(stage)::value;
+        wait_vm_lgkm0(min(R::PD - 1, ntiles - 1 - j) * kv.lpw);
         __builtin_amdgcn_s_barrier();
-        const unsigned char *sK = ring + (j % R::NST) * R::SB;
+        const unsigned char *sK = ring + ST * R::SB;
         const unsigned char *sV = sK + R::TB;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -549,7 +561,13 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
             const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
             block_accum_x<D>(acc, sK, 32 * sb, db, lane);  // dQ^T += K^T dS^T
         }
-        if (j + R::PD < ntiles) kv.issue(kg, vg, j + R::PD, T, ring + ((j + R::PD) % R::NST) * R::SB);
+        if (j + R::PD < ntiles)
+            kv.issue(kg, vg, j + R::PD, T, ring + ((ST + R::PD) % R::NST) * R::SB);
+    };
+    for (int j = 0; j < ntiles; j += 3) {
+        iter(j, std::integral_constant<int, 0>{});
+        if (j + 1 < ntiles) iter(j + 1, std::integral_constant<int, 1>{});
+        if (j + 2 < ntiles) iter(j + 2, std::integral_constant<int, 2>{});
     }
 
     if (qrow < T) {
