@@ -167,11 +167,12 @@ __device__ __forceinline__ QTileB qtile_of_b(const ArgsB &a, const QWorkB &w, in
 
 // K and V tiles of BN rows staged by direct global -> LDS copies into a ring of NST stages
 // (stage = K tile then V tile, rows in the swizzled layout of tile_off).  A stage is NPC 1 KB
-// pieces; one wave-wide dma16 fills one piece, and lane l fills the 16-byte slot l of it, so a
+// pieces; one wave-wide copy fills one piece, and lane l fills the 16-byte slot l of it, so a
 // lane loads the logical chunk that the swizzle places in its slot (the swizzle is an XOR, its
 // own inverse).  Within a tensor tile, piece q covers rows q * RPP .. + RPP - 1 and the lane's
-// row is q * RPP + lane / NCH; the swizzle depends on the row modulo 16, so one column offset
-// per parity of q covers every piece.  Wave w copies pieces w, w + nw, ...; a wave with a
+// row is q * RPP + lane / NCH; the lane's column offset only depends on the parity of q.  The
+// copies go through buffer resources on the head's K and V, so the address of a whole tile's
+// piece is a per-lane offset plus a uniform one.  Wave w copies pieces w, w + nw, ...; a wave with a
 // shorter share copies its first piece again, so every wave issues lpw copies per tile and can
 // wait on a fixed count.  Rows past the end read row T - 1: those keys are masked, so only
 // finiteness matters.
@@ -188,21 +189,40 @@ struct KVRingB {
     static constexpr int MAXL = NPC / 2;          // pieces per wave (query-tile groups: >= 2 waves)
     int wave, nw, lpw;  // wave-uniform
     int lrow;           // lane / NCH: the lane's row within a piece
-    int off0, off1;     // byte offset of the lane's 16 bytes within an even / odd piece's rows
+    int chb;            // byte offset of the lane's 16 bytes within its row, even pieces
+    int offw;           // with an even wave count, the lane's offset within each of its pieces
+    static constexpr int PX = 16 * swizzle_piece_xor<D>();  // odd pieces: offset ^ PX
 
     __device__ __forceinline__ void init(int wave_, int nw_, int lane) {
         wave = wave_;
         nw = nw_;
         lpw = (NPC + nw - 1) / nw;
         lrow = lane / C::NCH;
-        // Rows lrow and RPP + lrow have the swizzle of every row of even and odd pieces.
-        off0 = 2 * (lrow * D + 8 * chunk_swizzle<D>(lrow, lane % C::NCH));
-        off1 = 2 * (lrow * D + 8 * chunk_swizzle<D>(RPP + lrow, lane % C::NCH));
+        chb = 16 * chunk_swizzle<D>(lrow, lane % C::NCH);
+        // Piece wave + i nw has the parity of the wave when nw is even (PPT is even).
+        offw = (lrow * C::RB + chb) ^ ((wave & 1) * PX);
     }
-    // Starts the copies of tile `tile` into `stage`.
+    // Starts the copies of tile `tile` into `stage`.  Addresses are offsets within the head
+    // (kg, vg), split into a per-lane part and a wave-uniform part.
     __device__ __forceinline__ void issue(const __bf16 *kg, const __bf16 *vg, int tile, int T,
                                           unsigned char *stage) const {
-        const bool whole = (tile + 1) * C::BN <= T;  // no row past the end
+        const unsigned bytes = (unsigned)T * C::RB;
+        const buf_rsrc_t rk = raw_rsrc(kg, bytes), rv = raw_rsrc(vg, bytes);
+        if ((tile + 1) * C::BN <= T && (nw & 1) == 0) {
+            // No row past the end.
+#pragma unroll
+            for (int i = 0; i < MAXL; ++i)
+                if (i < lpw) {
+                    int pc = wave + i * nw;
+                    if (pc >= NPC) pc = wave;
+                    const bool isv = pc >= PPT;
+                    const int q = isv ? pc - PPT : pc;
+                    dma16_buf(isv ? rv : rk, (unsigned)offw, (unsigned)(tile * TB + q * 1024),
+                              stage + pc * 1024);
+                }
+            return;
+        }
+        // Rows past the end read row T - 1 instead.
 #pragma unroll
         for (int i = 0; i < MAXL; ++i)
             if (i < lpw) {
@@ -210,15 +230,9 @@ struct KVRingB {
                 if (pc >= NPC) pc = wave;
                 const bool isv = pc >= PPT;
                 const int q = isv ? pc - PPT : pc;
-                const int row0 = tile * C::BN + q * RPP;  // first row of the piece
-                const unsigned char *base = reinterpret_cast<const unsigned char *>(isv ? vg : kg);
-                const int off = (q & 1) ? off1 : off0;
-                if (whole) {
-                    dma16(base + (size_t)row0 * (2 * D) + off, stage + pc * 1024);
-                } else {
-                    const int r = min(row0 + lrow, T - 1);
-                    dma16(base + (size_t)r * (2 * D) + (off - 2 * lrow * D), stage + pc * 1024);
-                }
+                const int r = min(tile * C::BN + q * RPP + lrow, T - 1);
+                dma16_buf(isv ? rv : rk, (unsigned)((r * C::RB + chb) ^ ((q & 1) * PX)), 0u,
+                          stage + pc * 1024);
             }
     }
 };
@@ -649,30 +663,34 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     const int per_head = nqb - i0;
     const int nitems = a.G * per_head;
 
-    // This lane's 16 bytes of a piece: row lrow of the piece, swizzled chunk (by row parity).
+    // This lane's 16 bytes of a piece: row lrow of the piece, swizzled chunk (by piece parity).
+    constexpr int PX = 16 * swizzle_piece_xor<D>();
     const int lrow = lane / C::NCH;
-    const int off0 = 2 * (lrow * D + 8 * chunk_swizzle<D>(lrow, lane % C::NCH));
-    const int off1 = 2 * (lrow * D + 8 * chunk_swizzle<D>(S::RPP + lrow, lane % C::NCH));
-    // Starts the copies of item `it` into `st`.  Rows past the end read row T - 1; their lse is
-    // replaced by +inf once the item has landed, so their probabilities are 0.
+    const int chb = 16 * chunk_swizzle<D>(lrow, lane % C::NCH);
+    const int off0 = lrow * C::RB + chb, off1 = off0 ^ PX;
+    // Starts the copies of item `it` into `st`, through buffer resources on the head's q and dO.
+    // Rows past the end read row T - 1; their lse is replaced by +inf once the item has landed,
+    // so their probabilities are 0.
     auto issue = [&](int it, unsigned char *st) {
         const int hh = it / per_head, i = i0 + it % per_head;
         const size_t bh = (size_t)b * a.Hq + (size_t)g * a.G + hh;
-        const unsigned char *qb = reinterpret_cast<const unsigned char *>(a.q + bh * T * D);
-        const unsigned char *ob = reinterpret_cast<const unsigned char *>(a.dO + bh * T * D);
-        const bool whole = i * 32 + 32 <= T;
+        const unsigned bytes = (unsigned)T * C::RB;
+        const buf_rsrc_t rq = raw_rsrc(a.q + bh * T * D, bytes);
+        const buf_rsrc_t ro = raw_rsrc(a.dO + bh * T * D, bytes);
+        if (i * 32 + 32 <= T) {
 #pragma unroll
-        for (int pc = 0; pc < S::NPQ; ++pc) {
-            const int row0 = i * 32 + pc * S::RPP;
-            const int off = (pc & 1) ? off1 : off0;
-            if (whole) {
-                dma16(qb + (size_t)row0 * (2 * D) + off, st + pc * 1024);
-                dma16(ob + (size_t)row0 * (2 * D) + off, st + S::TBQ + pc * 1024);
-            } else {
-                const int r = min(row0 + lrow, T - 1);
-                const int o = off - 2 * lrow * D;
-                dma16(qb + (size_t)r * (2 * D) + o, st + pc * 1024);
-                dma16(ob + (size_t)r * (2 * D) + o, st + S::TBQ + pc * 1024);
+            for (int pc = 0; pc < S::NPQ; ++pc) {
+                const unsigned soff = (unsigned)((i * 32 + pc * S::RPP) * C::RB);
+                dma16_buf(rq, (unsigned)((pc & 1) ? off1 : off0), soff, st + pc * 1024);
+                dma16_buf(ro, (unsigned)((pc & 1) ? off1 : off0), soff, st + S::TBQ + pc * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int pc = 0; pc < S::NPQ; ++pc) {
+                const int r = min(i * 32 + pc * S::RPP + lrow, T - 1);
+                const unsigned vo = (unsigned)((r * C::RB + chb) ^ ((pc & 1) * PX));
+                dma16_buf(rq, vo, 0u, st + pc * 1024);
+                dma16_buf(ro, vo, 0u, st + S::TBQ + pc * 1024);
             }
         }
         const int r = min(i * 32 + col, T - 1);  // lanes 0..31: lse, lanes 32..63: delta

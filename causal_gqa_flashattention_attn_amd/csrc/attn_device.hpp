@@ -74,10 +74,28 @@ __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 //          f(r) = 2 * (((r & 3) + ((r >> 2) & 3)) & 3) + ((r >> 3) & 1).
 //   D = 32 (64-byte rows):  chunk c of row r is stored at c ^ ((r >> 2) & 3).
 template <int D>
-__device__ __forceinline__ int chunk_swizzle(int row, int ch) {
+__host__ __device__ __forceinline__ constexpr int chunk_swizzle(int row, int ch) {
     if constexpr (D == 64) return ch ^ (2 * (((row & 3) + ((row >> 2) & 3)) & 3) + ((row >> 3) & 1));
     else return ch ^ ((row >> 2) & 3);
 }
+
+// Copies that fill a tile 1024 bytes at a time cover rows [p R, p R + R) with piece p, R = 1024 /
+// (2 D).  The chunk permutation of row p R + r is that of row r XOR'd with a constant that only
+// depends on the parity of p; swizzle_piece_xor gives it (D = 64: 5, D = 32: 0).
+template <int D>
+constexpr int swizzle_piece_xor() { return D == 64 ? 5 : 0; }
+template <int D>
+constexpr bool swizzle_piece_xor_holds() {
+    constexpr int R = 1024 / (2 * D);
+    for (int p = 0; p < 8; ++p)
+        for (int r = 0; r < R; ++r)
+            for (int c = 0; c < D / 8; ++c)
+                if (chunk_swizzle<D>(p * R + r, c) != (chunk_swizzle<D>(r, c) ^ ((p & 1) * swizzle_piece_xor<D>())))
+                    return false;
+    return true;
+}
+static_assert(swizzle_piece_xor_holds<64>() && swizzle_piece_xor_holds<32>(),
+              "piece permutation depends on more than the piece's parity");
 
 // Byte offset of element (row, col) in a swizzled tile; col must be a multiple of 4.
 template <int D>
@@ -161,6 +179,18 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 __device__ __forceinline__ void dma16(const void *src, void *lds) {
     __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)lds, 16, 0, 0);
+}
+
+// The same copy through a buffer resource: lane l reads `bytes` bytes at byte offset
+// soff + voff (soff wave-uniform) past the resource's base.  The address arithmetic is done by
+// the memory unit, so a copy costs one instruction besides the uniform operands.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+__device__ __forceinline__ buf_rsrc_t raw_rsrc(const void *base, unsigned bytes) {
+    // Raw (unstructured) buffer: stride 0, 32-bit dwords, bounds = `bytes`.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16_buf(buf_rsrc_t r, unsigned voff, unsigned soff, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, soff, 0, 0);
 }
 
 // 4 bytes per lane, global -> LDS: lane l writes bytes [4 l, 4 l + 4) of `lds`.
