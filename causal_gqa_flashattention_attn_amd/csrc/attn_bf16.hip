@@ -335,6 +335,7 @@ template <int D>
 struct FwdState {
     f32x16 acc[CfgB<D>::ND];
     float m;
+    float mthr;  // (m + 8) / qscale: raw scores above it make m move
     float l4[4];
 };
 
@@ -356,18 +357,23 @@ __device__ __forceinline__ void fwd_half(const ArgsB &a, FwdState<D> &st, const 
             if ((CAUSAL && key > qrow) || key >= T) s[v] = -INFINITY;
         }
     }
-    // Maximum over the 32 keys of each row: four independent chains, then the two lane halves.
-    float mq[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) mq[c] = fmaxf(fmaxf(s[4 * c], s[4 * c + 1]), fmaxf(s[4 * c + 2], s[4 * c + 3]));
-    const float mx = max_halves(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * a.qscale;
+    // Maximum of this lane's 16 scores, a tree of three-input maxima.  (IEEE maximum: unlike
+    // fmaxf it needs no quieting of its inputs first, and -inf from the mask is neutral.)
+    const auto mx3 = [](float x, float y, float z) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+    };
+    const float lmax = __builtin_elementwise_maximum(
+        mx3(mx3(s[0], s[1], s[2]), mx3(s[3], s[4], s[5]), mx3(s[6], s[7], s[8])),
+        mx3(mx3(s[9], s[10], s[11]), mx3(s[12], s[13], s[14]), s[15]));
     // The reference maximum m only moves when some row's maximum exceeds it by more than 2^8:
     // probabilities up to 256 are exact enough in fp32 sums and bf16 operands, and most steps
-    // then skip the rescale of l and O entirely.
-    if (__builtin_amdgcn_ballot_w64(mx > st.m + 8.0f) != 0) {
-        const float mnew = fmaxf(st.m, mx);
+    // then skip the rescale of l and O entirely.  The test is per lane, on raw scores; the row
+    // maximum over both lane halves is only formed when m moves.
+    if (__builtin_amdgcn_ballot_w64(lmax > st.mthr) != 0) {
+        const float mnew = fmaxf(st.m, max_halves(lmax) * a.qscale);
         const float alpha = fast_exp2(st.m - mnew);
         st.m = mnew;
+        st.mthr = (mnew + 8.0f) / a.qscale;
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.l4[i] *= alpha;
 #pragma unroll
@@ -430,6 +436,7 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
 #pragma unroll
     for (int dd = 0; dd < C::ND; ++dd) st.acc[dd] = zero16();
     st.m = kNegBig;
+    st.mthr = kNegBig;
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.l4[i] = 0.f;
     // Everything requested so far has landed before the loop, so the compiler places no wait

@@ -68,3 +68,38 @@ def test_bf16_determinism_and_causality(ne):
     c = gpu_fwd_bwd(ne, y, rope_base=w.rope_base, dtype=torch.bfloat16, with_bwd=False)
     assert np.array_equal(a["o"][:, :, :t + 1], c["o"][:, :, :t + 1])
     assert np.array_equal(a["lse"][:, :, :t + 1], c["lse"][:, :, :t + 1])
+
+
+def _ramp_inputs(B, Hq, Hkv, T, D, peak, seed):
+    """Scores that rise (peak > 0) or fall (peak < 0) along the key axis: the keys carry a
+    common direction u with weight peak * sqrt(D) * ramp(t), every query has unit weight on u,
+    so the score of key t is about peak * ramp(t) plus noise of order one."""
+    import torch
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    ramp = np.linspace(0.0, 1.0, T) ** 2
+    if peak < 0:
+        ramp = ramp[::-1].copy()
+    q = 0.3 * rng.standard_normal((B, Hq, T, D)) + u
+    k = 0.3 * rng.standard_normal((B, Hkv, T, D)) + abs(peak) * np.sqrt(D) * ramp[None, None, :, None] * u
+    v = rng.standard_normal((B, Hkv, T, D))
+    dO = rng.standard_normal((B, Hq, T, D))
+    rnd = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    return {"q": rnd(q), "k": rnd(k), "v": rnd(v), "dO": rnd(dO)}
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("peak", [20.0, 200.0, 4000.0, -200.0])
+def test_bf16_scores_growing_along_keys(ne, oracle_mod, peak, causal):
+    """Row maxima that jump far above those of the first key tile (by 2^5 to past the fp32
+    exponent range in base-2 units) or only fall: the forward's reference maximum has to move,
+    or never does.  Forward only: with keys this large, dq = sum dS k cancels terms far larger
+    than itself, which a bf16 dS cannot resolve to the bar whatever the forward does."""
+    import torch
+    x = _ramp_inputs(1, 4, 2, 300, 64, peak, seed=11)
+    print(f"\n[case] bf16 ramp peak={peak} causal={causal} B1 Hq4 Hkv2 T300 D64", flush=True)
+    res = gpu_fwd_bwd(ne, x, causal=causal, dtype=torch.bfloat16, with_bwd=False)
+    ref = oracle_fwd_bwd(oracle_mod, x, causal=causal, with_bwd=False)
+    e = assert_bf16(res, ref, f"ramp {peak}")
+    print("  " + " ".join(f"{k}={v:.2e}" for k, v in e.items() if k.endswith("_rel")))
