@@ -284,6 +284,36 @@ struct TrOperand {
     static constexpr int NREAD = 4 * CfgB<D>::ND;  // LDS reads per operand
 };
 
+// Lane addresses of a TrOperand read from a tile at offset 0 of a region: [h][dd] for the rows
+// 8 h .. of each 16-row group and the columns 32 dd ..
+template <int D>
+struct TrAddr {
+    uint32_t a[2][CfgB<D>::ND];
+    __device__ __forceinline__ void init(const unsigned char *region, int lane) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int dd = 0; dd < CfgB<D>::ND; ++dd) a[h][dd] = tr4_lane_addr<D>(region, 8 * h, 32 * dd, lane);
+    }
+};
+
+// Issues the reads of the operand M^T for the 32-row tile at byte offset OFF of the region, in
+// the order accum_tr's waits count on (as issue_tr).
+template <int D, int OFF>
+__device__ __forceinline__ void issue_tr_at(TrOperand<D> &op, const TrAddr<D> &ad) {
+    constexpr int G16 = 16 * CfgB<D>::RB;  // bytes of 16 rows
+#pragma unroll
+    for (int dd = 0; dd < CfgB<D>::ND; ++dd) {
+        op.lo[0][dd] = lds_read_tr4<OFF>(ad.a[0][dd]);
+        op.hi[0][dd] = lds_read_tr4<OFF>(ad.a[1][dd]);
+    }
+#pragma unroll
+    for (int dd = 0; dd < CfgB<D>::ND; ++dd) {
+        op.lo[1][dd] = lds_read_tr4<OFF + G16>(ad.a[0][dd]);
+        op.hi[1][dd] = lds_read_tr4<OFF + G16>(ad.a[1][dd]);
+    }
+}
+
 template <int D>
 __device__ __forceinline__ void issue_tr(TrOperand<D> &op, const unsigned char *tile, int r0,
                                          int lane) {
@@ -685,19 +715,26 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         const buf_rsrc_t rq = raw_rsrc(a.q + bh * T * D, bytes);
         const buf_rsrc_t ro = raw_rsrc(a.dO + bh * T * D, bytes);
         if (i * 32 + 32 <= T) {
-#pragma unroll
-            for (int pc = 0; pc < S::NPQ; ++pc) {
-                const unsigned soff = (unsigned)((i * 32 + pc * S::RPP) * C::RB);
-                dma16_buf(rq, (unsigned)((pc & 1) ? off1 : off0), soff, st + pc * 1024);
-                dma16_buf(ro, (unsigned)((pc & 1) ? off1 : off0), soff, st + S::TBQ + pc * 1024);
-            }
+            // Piece pc sits 1 KB further on in both the tensor and the stage: an instruction
+            // offset, so the destinations of a stage are two values.
+            const unsigned soff = (unsigned)(i * 32 * C::RB);
+            static_for<S::NPQ>([&](auto pcc) {
+                constexpr int pc = decltype(pcc)::value;
+                dma16_buf_imm<pc * 1024>(rq, (unsigned)((pc & 1) ? off1 : off0), soff, st);
+                dma16_buf_imm<pc * 1024>(ro, (unsigned)((pc & 1) ? off1 : off0), soff, st + S::TBQ);
+            });
         } else {
+            // Rare (the last item of a head with T % 32 != 0): the stage address is made opaque
+            // so that its per-piece destinations are formed here, not held across the loop.
+            typedef __attribute__((address_space(3))) unsigned char lds_u8;
+            uint32_t sto = (uint32_t)(uintptr_t)(lds_u8 *)st;
+            asm volatile("" : "+s"(sto));
 #pragma unroll
             for (int pc = 0; pc < S::NPQ; ++pc) {
                 const int r = min(i * 32 + pc * S::RPP + lrow, T - 1);
                 const unsigned vo = (unsigned)((r * C::RB + chb) ^ ((pc & 1) * PX));
-                dma16_buf(rq, vo, 0u, st + pc * 1024);
-                dma16_buf(ro, vo, 0u, st + S::TBQ + pc * 1024);
+                dma16_buf_at(rq, vo, 0u, sto + pc * 1024);
+                dma16_buf_at(ro, vo, 0u, sto + S::TBQ + pc * 1024);
             }
         }
         const int r = min(i * 32 + col, T - 1);  // lanes 0..31: lse, lanes 32..63: delta
@@ -713,10 +750,13 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     load_operand_row<D, false>(kv, a.k + bg * T * D, krow, T, half, a.rope_lb);
     load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, 0.f);
     wait_vm_lgkm0(0);
-    int k = 0;
-    for (int it = wave; it < nitems; it += nw, ++k) {
+    TrAddr<D> tra;  // transposed reads of the stage-0 Q tile; other tiles are immediate offsets
+    tra.init(wbuf, lane);
+    // One item in stage ST (compile-time, so that every LDS offset of the item is an immediate).
+    auto item = [&](int it, auto stage) {
+        constexpr int ST = decltype(stage)::value;
         const int i = i0 + it % per_head;
-        unsigned char *st = wbuf + (k & 1) * S::SB;
+        unsigned char *st = wbuf + ST * S::SB;
         const unsigned char *sQ = st;
         const unsigned char *sO = st + S::TBQ;
         float *sL = reinterpret_cast<float *>(st + 2 * S::TBQ);
@@ -724,23 +764,30 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         // This item's copies have landed (the next item's may still be in flight); the stage
         // is private to the wave, so no barrier is needed.
         wait_vm_lgkm0(it + nw < nitems ? S::NDMA : 0);
-        if (lane < 32) sL[lane] = i * 32 + lane < T ? sL[lane] * kLog2e : INFINITY;
+        // lse of rows past the end -> +inf (P = 0); delta -> -delta, the start of dP - delta.
+        sL[lane] = lane >= 32 ? -sL[lane] : i * 32 + lane < T ? sL[lane] * kLog2e : INFINITY;
 
         // S = Q K'^T (rows: queries acc_row(v, half) of the block; column: this lane's key)
         f32x16 p = zero16();
 #pragma unroll
         for (int st2 = 0; st2 < C::KS; ++st2)
             p = mfma32_bf16(tile_read8<D>(sQ, col, 16 * st2 + 8 * half), kv[st2], p);
-        // dP = dO V^T
-        f32x16 ds = zero16();
+        // dP - delta = dO V^T - delta (rows of the accumulator: queries)
+        f32x16 ds;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 Dl = ld4(sDl + 8 * u + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds[4 * u + e] = Dl[e];
+        }
 #pragma unroll
         for (int st2 = 0; st2 < C::KS; ++st2)
             ds = mfma32_bf16(tile_read8<D>(sO, col, 16 * st2 + 8 * half), vv[st2], ds);
         // The transposed operands of dV and dK are requested now, so their latency overlaps
         // the exponentials.
         TrOperand<D> tdo, tq;
-        issue_tr<D>(tdo, sO, 0, lane);
-        issue_tr<D>(tq, sQ, 0, lane);
+        issue_tr_at<D, ST * S::SB + S::TBQ>(tdo, tra);
+        issue_tr_at<D, ST * S::SB>(tq, tra);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const f32x4 L = ld4(sL + 8 * u + 4 * half);
@@ -757,16 +804,16 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         accum_tr<D, TrOperand<D>::NREAD>(dv, tdo, pb);
         // dS = P (dP - delta)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const f32x4 Dl = ld4(sDl + 8 * u + 4 * half);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ds[4 * u + e] = p[4 * u + e] * (ds[4 * u + e] - Dl[e]);
-        }
+        for (int v = 0; v < 16; ++v) ds[v] *= p[v];
         // dK^T += Q^T dS
         const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
         accum_tr<D, 0>(dk, tq, db);
         // The stage is free once this item's reads are done: copy the item after next into it.
         if (it + 2 * nw < nitems) issue(it + 2 * nw, st);
+    };
+    for (int it = wave; it < nitems; it += 2 * nw) {
+        item(it, std::integral_constant<int, 0>{});
+        if (it + nw < nitems) item(it + nw, std::integral_constant<int, 1>{});
     }
 
     // Add the waves' partial sums in LDS (fixed wave order), rotate dK back, round, store.

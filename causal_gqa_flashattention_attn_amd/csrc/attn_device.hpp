@@ -12,6 +12,8 @@
 // register v, whose row index is acc_row(v, half).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,6 +46,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Value of lane (l ^ 32): exchanges the two halves of the wave.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, each with I a compile-time constant.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ void st4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
@@ -137,6 +148,27 @@ __device__ __forceinline__ bf16x4 tile_read_tr4_asm(const unsigned char *t, int 
     return r;
 }
 
+// The transposed read at LDS byte address addr + OFF (OFF < 65536, an immediate of the
+// instruction), for addresses precomputed by tr4_lane_addr; the same wait rules apply.
+template <int OFF>
+__device__ __forceinline__ bf16x4 lds_read_tr4(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset out of range");
+    bf16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+
+// LDS byte address of this lane's transposed read of rows k0 .. k0 + 3 (k0 a multiple of 4 below
+// 16), columns c0 .. of the swizzled tile at `t`.  The chunk permutation repeats every 16 rows,
+// so rows k0 + 16 j are read at this address plus 16 j rows.
+template <int D>
+__device__ __forceinline__ uint32_t tr4_lane_addr(const unsigned char *t, int k0, int c0, int lane) {
+    const int row = k0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    typedef __attribute__((address_space(3))) const unsigned char lds_u8;
+    return (uint32_t)(uintptr_t)(lds_u8 *)(t + tile_off<D>(row, col));
+}
+
 // s_waitcnt lgkmcnt(N): waits until at most N of this wave's LDS operations are outstanding.
 // They complete in order, so a read followed by N or more later LDS operations of the wave
 // has landed.  a and b pass through the wait, so nothing that uses them moves above it.
@@ -191,6 +223,16 @@ __device__ __forceinline__ buf_rsrc_t raw_rsrc(const void *base, unsigned bytes)
 }
 __device__ __forceinline__ void dma16_buf(buf_rsrc_t r, unsigned voff, unsigned soff, void *lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, soff, 0, 0);
+}
+// The destination as a 32-bit LDS byte address.
+__device__ __forceinline__ void dma16_buf_at(buf_rsrc_t r, unsigned voff, unsigned soff, uint32_t lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(uintptr_t)lds, 16, voff, soff, 0, 0);
+}
+// With an instruction offset IMM, added to both the memory offset and the LDS destination.
+template <int IMM>
+__device__ __forceinline__ void dma16_buf_imm(buf_rsrc_t r, unsigned voff, unsigned soff, void *lds) {
+    static_assert(IMM >= 0 && IMM < 4096, "buffer instruction offset out of range");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, soff, IMM, 0);
 }
 
 // 4 bytes per lane, global -> LDS: lane l writes bytes [4 l, 4 l + 4) of `lds`.
