@@ -190,8 +190,10 @@ struct KVRingB {
     int wave, nw, lpw;  // wave-uniform
     int lrow;           // lane / NCH: the lane's row within a piece
     int chb;            // byte offset of the lane's 16 bytes within its row, even pieces
-    int offw;           // with an even wave count, the lane's offset within each of its pieces
+    int off0, off1;     // the lane's offset within an even / odd piece
+    int offw;           // ... within piece number `wave`
     static constexpr int PX = 16 * swizzle_piece_xor<D>();  // odd pieces: offset ^ PX
+    static_assert(PPT <= 4 || PPT % 4 == 0, "piece runs are at most four instruction offsets");
 
     __device__ __forceinline__ void init(int wave_, int nw_, int lane) {
         wave = wave_;
@@ -199,8 +201,9 @@ struct KVRingB {
         lpw = (NPC + nw - 1) / nw;
         lrow = lane / C::NCH;
         chb = 16 * chunk_swizzle<D>(lrow, lane % C::NCH);
-        // Piece wave + i nw has the parity of the wave when nw is even (PPT is even).
-        offw = (lrow * C::RB + chb) ^ ((wave & 1) * PX);
+        off0 = lrow * C::RB + chb;
+        off1 = off0 ^ PX;
+        offw = (wave & 1) ? off1 : off0;
     }
     // Starts the copies of tile `tile` into `stage`.  Addresses are offsets within the head
     // (kg, vg), split into a per-lane part and a wave-uniform part.
@@ -208,18 +211,24 @@ struct KVRingB {
                                           unsigned char *stage) const {
         const unsigned bytes = (unsigned)T * C::RB;
         const buf_rsrc_t rk = raw_rsrc(kg, bytes), rv = raw_rsrc(vg, bytes);
-        if ((tile + 1) * C::BN <= T && (nw & 1) == 0) {
-            // No row past the end.
-#pragma unroll
-            for (int i = 0; i < MAXL; ++i)
-                if (i < lpw) {
-                    int pc = wave + i * nw;
-                    if (pc >= NPC) pc = wave;
-                    const bool isv = pc >= PPT;
-                    const int q = isv ? pc - PPT : pc;
-                    dma16_buf(isv ? rv : rk, (unsigned)offw, (unsigned)(tile * TB + q * 1024),
-                              stage + pc * 1024);
+        const uint32_t sa = opaque_lds_addr(stage);
+        if ((tile + 1) * C::BN <= T && PPT % nw == 0) {
+            // No row past the end, and nw divides the pieces of a tensor tile: wave w copies
+            // the ppw consecutive pieces w ppw .. of K and of V (the same count, lpw, as below).
+            // Consecutive pieces are 1 KB apart in the tensor and in the stage alike: an
+            // instruction offset.  With ppw even, piece parity is that of j; with ppw = 1, of w.
+            const int ppw = PPT / nw;
+            const int p0 = wave * ppw;
+            const unsigned soff = (unsigned)(tile * TB + p0 * 1024);
+            const uint32_t dk = sa + p0 * 1024, dv = sa + TB + p0 * 1024;
+            static_for<(PPT < 4 ? PPT : 4)>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if (j < ppw) {
+                    const unsigned vo = (unsigned)(j == 0 ? (ppw == 1 ? offw : off0) : (j & 1) ? off1 : off0);
+                    dma16_buf_imm_at<j * 1024>(rk, vo, soff, dk);
+                    dma16_buf_imm_at<j * 1024>(rv, vo, soff, dv);
                 }
+            });
             return;
         }
         // Rows past the end read row T - 1 instead.
@@ -231,8 +240,8 @@ struct KVRingB {
                 const bool isv = pc >= PPT;
                 const int q = isv ? pc - PPT : pc;
                 const int r = min(tile * C::BN + q * RPP + lrow, T - 1);
-                dma16_buf(isv ? rv : rk, (unsigned)((r * C::RB + chb) ^ ((q & 1) * PX)), 0u,
-                          stage + pc * 1024);
+                dma16_buf_at(isv ? rv : rk, (unsigned)((r * C::RB + chb) ^ ((q & 1) * PX)), 0u,
+                             sa + pc * 1024);
             }
     }
 };

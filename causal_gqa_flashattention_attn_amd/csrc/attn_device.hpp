@@ -234,6 +234,20 @@ __device__ __forceinline__ void dma16_buf_imm(buf_rsrc_t r, unsigned voff, unsig
     static_assert(IMM >= 0 && IMM < 4096, "buffer instruction offset out of range");
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, soff, IMM, 0);
 }
+template <int IMM>
+__device__ __forceinline__ void dma16_buf_imm_at(buf_rsrc_t r, unsigned voff, unsigned soff, uint32_t lds) {
+    static_assert(IMM >= 0 && IMM < 4096, "buffer instruction offset out of range");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(uintptr_t)lds, 16, voff, soff, IMM, 0);
+}
+
+// The LDS byte address of `p`, hidden from the optimiser: values derived from it are formed
+// where they are used instead of being hoisted out of loops (scalar registers are scarce).
+__device__ __forceinline__ uint32_t opaque_lds_addr(const void *p) {
+    typedef __attribute__((address_space(3))) const unsigned char lds_u8c;
+    uint32_t a = (uint32_t)(uintptr_t)(lds_u8c *)p;
+    asm volatile("" : "+s"(a));
+    return a;
+}
 
 // 4 bytes per lane, global -> LDS: lane l writes bytes [4 l, 4 l + 4) of `lds`.
 __device__ __forceinline__ void dma4(const void *src, void *lds) {
