@@ -441,11 +441,11 @@ __device__ __forceinline__ void fwd_step(const ArgsB &a, FwdState<D> &st, const 
     }
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+template <int D, bool CAUSAL, bool ROPE, int NWC>
 __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsigned char *ring) {
     using C = CfgB<D>;
     using R = KVRingB<D>;
-    const int nw = blockDim.x >> 6;
+    const int nw = NWC ? NWC : blockDim.x >> 6;  // a compile-time count makes the waits immediates
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
@@ -521,24 +521,26 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
     }
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+// NWC: the waves per work-group when known at compile time (4: groups of four query heads),
+// else 0.
+template <int D, bool CAUSAL, bool ROPE, int NWC>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_FWD_WAVES_PER_EU)))
 fwd_bf16(ArgsB a) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const QWorkB w = decode_qwork_b(a);
-    fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), ring);
+    fwd_tile_b<D, CAUSAL, ROPE, NWC>(a, qtile_of_b(a, w, w.qt0, wave), ring);
     if (w.qt1 >= 0) {
         __syncthreads();
-        fwd_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt1, wave), ring);
+        fwd_tile_b<D, CAUSAL, ROPE, NWC>(a, qtile_of_b(a, w, w.qt1, wave), ring);
     }
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+template <int D, bool CAUSAL, bool ROPE, int NWC>
 __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsigned char *ring) {
     using C = CfgB<D>;
     using R = KVRingB<D>;
-    const int nw = blockDim.x >> 6;
+    const int nw = NWC ? NWC : blockDim.x >> 6;  // a compile-time count makes the waits immediates
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
@@ -643,16 +645,18 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
     }
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+// NWC: the waves per work-group when known at compile time (4: groups of four query heads),
+// else 0.
+template <int D, bool CAUSAL, bool ROPE, int NWC>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_DQ_WAVES_PER_EU)))
 dq_bf16(ArgsB a) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const QWorkB w = decode_qwork_b(a);
-    dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt0, wave), ring);
+    dq_tile_b<D, CAUSAL, ROPE, NWC>(a, qtile_of_b(a, w, w.qt0, wave), ring);
     if (w.qt1 >= 0) {
         __syncthreads();
-        dq_tile_b<D, CAUSAL, ROPE>(a, qtile_of_b(a, w, w.qt1, wave), ring);
+        dq_tile_b<D, CAUSAL, ROPE, NWC>(a, qtile_of_b(a, w, w.qt1, wave), ring);
     }
 }
 
@@ -926,16 +930,30 @@ ArgsB make_args_b(const Shape &s) {
     return a;
 }
 
-#define NE_PICK_B(KERNEL)                                                                    \
-    template <int D>                                                                         \
+#define NE_PICK_B(KERNEL, TPARAMS, TARGS)                                                    \
+    template <TPARAMS>                                                                       \
     const void *pick_##KERNEL(bool causal, bool rope) {                                      \
-        if (causal) return rope ? (const void *)KERNEL<D, true, true> : (const void *)KERNEL<D, true, false>; \
-        return rope ? (const void *)KERNEL<D, false, true> : (const void *)KERNEL<D, false, false>; \
+        if (causal)                                                                          \
+            return rope ? (const void *)KERNEL<D, true, true TARGS>                          \
+                        : (const void *)KERNEL<D, true, false TARGS>;                        \
+        return rope ? (const void *)KERNEL<D, false, true TARGS>                             \
+                    : (const void *)KERNEL<D, false, false TARGS>;                           \
     }
-NE_PICK_B(fwd_bf16)
-NE_PICK_B(dq_bf16)
-NE_PICK_B(dkdv_bf16)
+#define NE_COMMA ,
+NE_PICK_B(fwd_bf16, int D NE_COMMA int NWC, NE_COMMA NWC)
+NE_PICK_B(dq_bf16, int D NE_COMMA int NWC, NE_COMMA NWC)
+NE_PICK_B(dkdv_bf16, int D, )
+#undef NE_COMMA
 #undef NE_PICK_B
+
+// The query-tile kernel for this shape: four-wave groups get the variant with the count built in.
+template <const void *(*P64_4)(bool, bool), const void *(*P64)(bool, bool),
+          const void *(*P32_4)(bool, bool), const void *(*P32)(bool, bool)>
+const void *pick_qtile(const Shape &s, int nwaves) {
+    const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
+    if (s.D == 64) return nwaves == 4 ? P64_4(causal, rope) : P64(causal, rope);
+    return nwaves == 4 ? P32_4(causal, rope) : P32(causal, rope);
+}
 
 hipError_t launch_b(const void *fn, long long blocks, int threads, size_t lds, hipStream_t st,
                     ArgsB &a) {
@@ -955,8 +973,8 @@ hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const v
     a.out_lse = lse;
     const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.fwd != 0);
     a.paired = g.paired;
-    const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
-    const void *fn = s.D == 64 ? pick_fwd_bf16<64>(causal, rope) : pick_fwd_bf16<32>(causal, rope);
+    const void *fn = pick_qtile<pick_fwd_bf16<64, 4>, pick_fwd_bf16<64, 0>, pick_fwd_bf16<32, 4>,
+                                pick_fwd_bf16<32, 0>>(s, g.nwaves);
     return launch_b(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
 }
 
@@ -975,8 +993,8 @@ hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const vo
     a.qrot = static_cast<__bf16 *>(qrot);
     const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.dq != 0);
     a.paired = g.paired;
-    const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
-    const void *fn = s.D == 64 ? pick_dq_bf16<64>(causal, rope) : pick_dq_bf16<32>(causal, rope);
+    const void *fn = pick_qtile<pick_dq_bf16<64, 4>, pick_dq_bf16<64, 0>, pick_dq_bf16<32, 4>,
+                                pick_dq_bf16<32, 0>>(s, g.nwaves);
     return launch_b(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
 }
 
