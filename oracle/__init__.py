@@ -11,6 +11,8 @@ NanoEuler pages each step follows.  This module only marshals numpy arrays:
 * ``attn_fwd(q, k, v, causal, rope_base, rope_pairing) -> (o, lse)``
 * ``attn_bwd(q, k, v, dO, causal, rope_base, rope_pairing) -> (dq, dk, dv)``
 * ``rope(x, base, pairing, inverse) -> x rotated``
+* ``attn_decode(q, k, v, lens) -> (o, lse)``: one query per (batch, head) against a key/value
+  cache [B, Hkv, Tc, D], keys 0 .. lens[b] - 1 visible
 
 Shapes: q, dO: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; lse: [B, Hq, T].  Inputs of any float
 dtype are converted exactly to float64.  ``rope_base = 0`` disables RoPE.
@@ -28,7 +30,7 @@ _SRC = os.path.join(_HERE, "oracle_attn.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-__all__ = ["build", "attn_fwd", "attn_bwd", "rope", "num_threads"]
+__all__ = ["build", "attn_fwd", "attn_bwd", "attn_decode", "rope", "num_threads"]
 
 
 def build() -> str:
@@ -55,6 +57,9 @@ def _load():
     lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i,
                                     ctypes.c_double, i]
     lib.oracle_attn_bwd.restype = i
+    lib.oracle_attn_decode.argtypes = [dp, dp, dp, ctypes.POINTER(ctypes.c_int), dp, dp,
+                                       i, i, i, i, i]
+    lib.oracle_attn_decode.restype = i
     lib.oracle_rope.argtypes = [dp, i, i, i, i, ctypes.c_double, i, i]
     lib.oracle_rope.restype = i
     lib.oracle_num_threads.argtypes = []
@@ -113,6 +118,25 @@ def attn_bwd(q, k, v, dO, causal: bool = True, rope_base: float = 0.0, rope_pair
                                  float(rope_base), int(rope_pairing))
     _check(rc, "oracle_attn_bwd")
     return dq, dk, dv
+
+
+def attn_decode(q, k, v, lens):
+    """q [B,Hq,D]; k, v [B,Hkv,Tc,D]; lens [B] -> (o [B,Hq,D], lse [B,Hq]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 3 or k.ndim != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, D], k and v [B, Hkv, Tc, D]")
+    B, Hq, D = q.shape
+    _, Hkv, Tc, Dk = k.shape
+    if k.shape[0] != B or Dk != D:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape}")
+    ln = np.ascontiguousarray(np.asarray(lens, dtype=np.int32).reshape(B))
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    rc = _load().oracle_attn_decode(_ptr(q), _ptr(k), _ptr(v),
+                                    ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), _ptr(o),
+                                    _ptr(lse), B, Hq, Hkv, Tc, D)
+    _check(rc, "oracle_attn_decode")
+    return o, lse
 
 
 def rope(x, base: float, pairing: int = 0, inverse: bool = False) -> np.ndarray:

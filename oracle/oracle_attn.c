@@ -283,6 +283,64 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
     return failed ? -2 : 0;
 }
 
+/*
+ * Decode step against a key/value cache.  The pages say the attention supports a KV cache for
+ * autoregressive generation ("NanoEuler" article on ainews.cool, section "technical deep
+ * dive", attention item) and list GPU generation among the program's modes (Japanese README
+ * translation, command list).  Reading: one new query per (batch, query head); it sees the
+ * cached keys 0 .. lens[b] - 1 of its key/value head, which already include its own position,
+ * so no further mask applies.  It is the last row of causal attention over a sequence of
+ * length lens[b] whose final query is q (the test-suite checks exactly that).  Any RoPE has
+ * been applied to q and to the cached keys by the caller.
+ *
+ * q, o: [B][Hq][D]; k, v: [B][Hkv][Tc][D] (the cache, Tc >= every lens[b]); lse: [B][Hq];
+ * lens: [B].  lens[b] = 0 gives o = 0 and lse = -inf.
+ */
+int oracle_attn_decode(const double *q, const double *k, const double *v, const int *lens,
+                       double *o, double *lse, int B, int Hq, int Hkv, int Tc, int D)
+{
+    if (check_args(B, Hq, Hkv, Tc, D, 0, 0)) return -1;
+    if (!q || !k || !v || !lens || !o) return -1;
+    for (int b = 0; b < B; ++b)
+        if (lens[b] < 0 || lens[b] > Tc) return -1;
+    int G = Hq / Hkv;
+    double scale = 1.0 / sqrt((double)D);
+    int failed = 0;
+
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)Tc * sizeof(double));
+        if (!s) {
+            #pragma omp atomic write
+            failed = 1;
+        }
+        #pragma omp for collapse(2) schedule(dynamic, 4)
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < Hq; ++h) {
+                if (!s) continue;
+                int g = h / G, n = lens[b];
+                const double *qh = q + ((size_t)b * Hq + h) * D;
+                double *oh = o + ((size_t)b * Hq + h) * D;
+                for (int d = 0; d < D; ++d) oh[d] = 0.0;
+                double m = -INFINITY;
+                for (int j = 0; j < n; ++j) {
+                    s[j] = dot(qh, k + IDX4(b, g, j, 0, Hkv, Tc, D), D) * scale;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int j = 0; j < n; ++j) l += exp(s[j] - m);
+                for (int j = 0; j < n; ++j) {
+                    double p = exp(s[j] - m) / l;
+                    const double *vj = v + IDX4(b, g, j, 0, Hkv, Tc, D);
+                    for (int d = 0; d < D; ++d) oh[d] += p * vj[d];
+                }
+                if (lse) lse[(size_t)b * Hq + h] = n > 0 ? m + log(l) : -INFINITY;
+            }
+        free(s);
+    }
+    return failed ? -2 : 0;
+}
+
 /* Number of OpenMP threads a parallel region of this library uses. */
 int oracle_num_threads(void)
 {
