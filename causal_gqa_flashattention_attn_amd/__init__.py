@@ -2,16 +2,18 @@
 
 The functions named like the C entry points (``ne_attn_fwd``, ``ne_attn_bwd``,
 ``ne_attn_fwd_ex``, ``ne_attn_bwd_ex``, ``ne_attn_bwd_dq_ex``, ``ne_attn_bwd_dkdv_ex``,
-``ne_attn_workspace_bytes``, ``ne_attn_bwd_workspace_bytes``, ``ne_attn_strerror``) only
+``ne_attn_decode``, ``ne_attn_workspace_bytes``, ``ne_attn_decode_workspace_bytes``,
+``ne_attn_bwd_workspace_bytes``, ``ne_attn_strerror``) only
 marshal arguments: they read sizes from tensor shapes, pass ``data_ptr()`` and the current
 HIP stream, and raise ``NeAttnError`` on a non-zero status.  All arithmetic happens in the HIP
 kernels.  PyTorch provides device memory and streams.
 
-``forward`` and ``backward`` are conveniences that allocate the outputs and the workspace with
-torch and call the entry points.
+``forward``, ``backward`` and ``decode`` are conveniences that allocate the outputs and the
+workspace with torch and call the entry points.
 
 Tensor layout: q, o, dO, dq: [B, Hq, T, D]; k, v, dk, dv: [B, Hkv, T, D]; lse: [B, Hq, T]
 float32; all contiguous on one GPU; float32, or bfloat16 through the ``_ex`` entry points.
+Decode: q, o: [B, Hq, D]; k_cache, v_cache: [B, Hkv, Tc, D]; lse: [B, Hq]; lens: int32 [B].
 """
 from __future__ import annotations
 
@@ -21,9 +23,9 @@ import os
 __all__ = [
     "NeAttnError", "library_path", "load", "lib",
     "ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex",
-    "ne_attn_workspace_bytes", "ne_attn_bwd_workspace_bytes", "ne_attn_strerror",
-    "forward", "backward", "workspace",
+    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_decode",
+    "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes", "ne_attn_bwd_workspace_bytes",
+    "ne_attn_strerror", "forward", "backward", "decode", "workspace",
     "NE_OK", "NE_ERR_NULL", "NE_ERR_SHAPE", "NE_ERR_UNSUPPORTED", "NE_ERR_ALIGN", "NE_ERR_HIP",
     "NE_F32", "NE_BF16", "EXPORTED_SYMBOLS",
 ]
@@ -32,7 +34,8 @@ NE_OK, NE_ERR_NULL, NE_ERR_SHAPE, NE_ERR_UNSUPPORTED, NE_ERR_ALIGN, NE_ERR_HIP =
 NE_F32, NE_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-                    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_workspace_bytes",
+                    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_decode",
+                    "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
                     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +78,9 @@ def load():
         getattr(L, name).restype = i
     L.ne_attn_workspace_bytes.argtypes = [i] * 6 + [f]
     L.ne_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.ne_attn_decode.argtypes = [vp] * 7 + [i] * 6 + [vp]
+    L.ne_attn_decode_workspace_bytes.argtypes = [i] * 6
+    L.ne_attn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.ne_attn_bwd_workspace_bytes.argtypes = [i, i, i]
     L.ne_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.ne_attn_strerror.argtypes = [i]
@@ -99,6 +105,11 @@ def ne_attn_workspace_bytes(B: int, Hq: int, Hkv: int, T: int, D: int, dtype: in
                             rope_base: float = 0.0) -> int:
     return int(load().ne_attn_workspace_bytes(int(B), int(Hq), int(Hkv), int(T), int(D),
                                               int(dtype), float(rope_base)))
+
+
+def ne_attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Tc: int, D: int, dtype: int) -> int:
+    return int(load().ne_attn_decode_workspace_bytes(int(B), int(Hq), int(Hkv), int(Tc), int(D),
+                                                     int(dtype)))
 
 
 # ----------------------------------------------------------------------------- marshalling
@@ -272,6 +283,34 @@ def ne_attn_bwd_dkdv_ex(q, k, v, lse, dO, workspace, dk, dv, causal: bool = True
     _raise(rc, "ne_attn_bwd_dkdv_ex")
 
 
+def ne_attn_decode(q, k_cache, v_cache, lens, o, lse, workspace, stream=None):
+    """One decode step: q [B, Hq, D] against the cache [B, Hkv, Tc, D], keys 0 .. lens[b]-1
+    (lens: int32 [B] on the device)."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, Hq, D]; k_cache, v_cache [B, Hkv, Tc, D]")
+    B, Hq, D = q.shape
+    _, Hkv, Tc, Dk = k_cache.shape
+    if k_cache.shape[0] != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k_cache{tuple(k_cache.shape)}")
+    dt = _dtype_code(q)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("o", o)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have dtype {q.dtype}")
+    if o.shape != q.shape or tuple(lse.shape) != (B, Hq) or lse.dtype != torch.float32:
+        raise ValueError("o must match q; lse must be float32 [B, Hq]")
+    if tuple(lens.shape) != (B,) or lens.dtype != torch.int32:
+        raise ValueError("lens must be int32 [B]")
+    _check_tensors(dict(q=q, k_cache=k_cache, v_cache=v_cache, lens=lens, o=o, lse=lse),
+                   q.device)
+    _ws_check(workspace, ne_attn_decode_workspace_bytes(B, Hq, Hkv, Tc, D, dt), q.device)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_decode(_p(q), _p(k_cache), _p(v_cache), _p(lens), _p(o), _p(lse),
+                                   _p(workspace), B, Hq, Hkv, Tc, D, dt,
+                                   _stream(stream, q.device))
+    _raise(rc, "ne_attn_decode")
+
+
 # ----------------------------------------------------------------------------- conveniences
 
 def workspace(q, k, rope_base: float = 0.0):
@@ -304,3 +343,18 @@ def backward(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0, s
     ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, rope_base), causal=causal,
                    rope_base=rope_base, stream=stream)
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, lens, stream=None):
+    """Allocates o, lse and the workspace and runs one decode step; returns (o, lse)."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    n = ne_attn_decode_workspace_bytes(B, Hq, k_cache.shape[1], k_cache.shape[2], D,
+                                       _dtype_code(q))
+    if n == 0:
+        raise ValueError("invalid shape for a decode workspace")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    ne_attn_decode(q, k_cache, v_cache, lens, o, lse, ws, stream=stream)
+    return o, lse

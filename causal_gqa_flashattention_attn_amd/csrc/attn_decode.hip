@@ -1,0 +1,297 @@
+// attn_decode.hip -- one decode step of grouped-query attention against a key/value cache.
+//
+// The pages say the attention supports a KV cache for autoregressive generation ("NanoEuler"
+// article on ainews.cool, section "technical deep dive", attention item).  Each (batch, query
+// head) has one new query; it attends to the cached keys 0 .. lens[b] - 1 of its key/value head
+// (its own position included), with scale 1/sqrt(D).  Any RoPE has been applied by the caller.
+//
+// The step reads the whole cache once and does about 4 flops per byte of it, so it is bound by
+// HBM bandwidth, not by arithmetic: it runs on the vector ALUs, with every lane streaming 16
+// bytes of a key (value) row per load.  The work is split over the cache length (split-KV):
+//   decode_split  grid (split, batch x kv head x query-head chunk), 4 waves of 64 keys each;
+//                 one work-group serves every query head of its key/value head, so each cache
+//                 row is read once.  Each lane keeps an online softmax (running maximum, sum,
+//                 output slice) per query head over the keys it saw; lanes, then waves, are
+//                 merged, and the split's (o / l, lse) goes to the workspace.
+//   decode_merge  per (batch, query head): log-sum-exp of the splits' lse, weighted sum of their
+//                 outputs.  Splits past lens[b] are neither computed nor read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "attn_device.hpp"
+#include "attn_kernels.hpp"
+
+namespace ne {
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecKeysPerWave = 64;
+constexpr int kDecSplit = kDecWaves * kDecKeysPerWave;  // keys per split
+
+struct DecArgs {
+    const void *q, *k, *v;
+    const int *lens;
+    void *o;
+    float *lse;
+    float *part_o, *part_lse;  // workspace: [nsplit][B][Hq][D] and [nsplit][B][Hq]
+    int B, Hq, Hkv, Tc, G, nhc, nsplit;
+    float qscale;  // log2(e) / sqrt(D): scores in base-2 units
+};
+
+// Lane geometry: a lane streams E elements (16 bytes) of a row; LPK lanes cover a row of D;
+// one wave-wide load covers KPI rows; a wave's 64 keys take NIT loads, issued PASS at a time
+// (fewer at once for wide head groups, whose per-head state takes the registers).
+template <int D, typename T, int GC>
+struct DecCfg {
+    static constexpr int E = 16 / sizeof(T);
+    static constexpr int LPK = D / E;
+    static constexpr int KPI = 64 / LPK;
+    static constexpr int NIT = kDecKeysPerWave / KPI;
+    static constexpr int PMAX = GC <= 2 ? 8 : GC == 4 ? 4 : 2;
+    static constexpr int PASS = NIT < PMAX ? NIT : PMAX;
+    static_assert(LPK >= 1 && 64 % LPK == 0 && NIT % PASS == 0, "unsupported head size");
+};
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a row, kept raw until used.
+template <typename T>
+__device__ __forceinline__ u32x4_t load_raw16(const T *p) {
+    return *reinterpret_cast<const u32x4_t *>(p);
+}
+
+// Element e of a raw 16-byte chunk as fp32.
+template <typename T>
+__device__ __forceinline__ float raw_elt(const u32x4_t &r, int e) {
+    if constexpr (sizeof(T) == 4) {
+        return __uint_as_float(r[e]);
+    } else {
+        const unsigned w = r[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_row16(const T *p, float (&x)[16 / sizeof(T)]) {
+    const u32x4_t r = load_raw16<T>(p);
+#pragma unroll
+    for (int e = 0; e < 16 / (int)sizeof(T); ++e) x[e] = raw_elt<T>(r, e);
+}
+
+template <typename T>
+__device__ __forceinline__ T to_elt(float x) {
+    return (T)x;
+}
+
+// Running (m, l, o) of one query head over some keys: scores in base 2, o unnormalised.
+template <int E>
+struct DecState {
+    float m, l, o[E];
+};
+
+template <int E>
+__device__ __forceinline__ void dec_merge(DecState<E> &a, float m2, float l2, const float (&o2)[E]) {
+    const float mn = fmaxf(a.m, m2);
+    const float s1 = fast_exp2(a.m - mn), s2 = fast_exp2(m2 - mn);
+    a.l = a.l * s1 + l2 * s2;
+#pragma unroll
+    for (int e = 0; e < E; ++e) a.o[e] = a.o[e] * s1 + o2[e] * s2;
+    a.m = mn;
+}
+
+template <int D, typename T, int GC>
+__global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
+    using C = DecCfg<D, T, GC>;
+    constexpr int E = C::E;
+    const int s = blockIdx.x;
+    int y = blockIdx.y;
+    const int hc = y % a.nhc;
+    y /= a.nhc;
+    const int g = y % a.Hkv;
+    const int b = y / a.Hkv;
+    const int len = min(max(a.lens[b], 0), a.Tc);
+    const int k0 = s * kDecSplit;
+    if (k0 >= len) return;  // past the cached length: the merge does not read this split
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % C::LPK, kl = lane / C::LPK;
+    const int h0 = g * a.G + hc * GC;
+    const int gn = min(GC, a.G - hc * GC);
+
+    float qv[GC][E];
+    DecState<E> st[GC];
+#pragma unroll
+    for (int gi = 0; gi < GC; ++gi) {
+        float x[E];
+        if (gi < gn)
+            load_row16<T>(static_cast<const T *>(a.q) + ((size_t)b * a.Hq + h0 + gi) * D + sub * E, x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            qv[gi][e] = gi < gn ? x[e] * a.qscale : 0.f;
+            st[gi].o[e] = 0.f;
+        }
+        st[gi].m = kNegBig;
+        st[gi].l = 0.f;
+    }
+
+    const size_t row0 = ((size_t)b * a.Hkv + g) * a.Tc;
+    const T *kb = static_cast<const T *>(a.k) + row0 * D + sub * E;
+    const T *vb = static_cast<const T *>(a.v) + row0 * D + sub * E;
+    const int kw = k0 + wave * kDecKeysPerWave;
+#pragma unroll
+    for (int p0 = 0; p0 < C::NIT; p0 += C::PASS) {
+        if (kw + p0 * C::KPI >= len) break;  // wave-uniform
+        // Every load of the pass is requested before the first is used.
+        u32x4_t kr[C::PASS], vr[C::PASS];
+#pragma unroll
+        for (int i = 0; i < C::PASS; ++i) {
+            const int j = min(kw + (p0 + i) * C::KPI + kl, len - 1);
+            kr[i] = load_raw16<T>(kb + (size_t)j * D);
+            vr[i] = load_raw16<T>(vb + (size_t)j * D);
+        }
+#pragma unroll
+        for (int i = 0; i < C::PASS; ++i) {
+            const bool valid = kw + (p0 + i) * C::KPI + kl < len;
+#pragma unroll
+            for (int gi = 0; gi < GC; ++gi) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) d = fmaf(qv[gi][e], raw_elt<T>(kr[i], e), d);
+                // the row's dot product: sum over the LPK lanes that hold it
+#pragma unroll
+                for (int w = 1; w < C::LPK; w <<= 1) d += __shfl_xor(d, w, 64);
+                const float sc = valid ? d : -INFINITY;
+                const float mn = fmaxf(st[gi].m, sc);
+                const float al = fast_exp2(st[gi].m - mn), p = fast_exp2(sc - mn);
+                st[gi].l = st[gi].l * al + p;
+#pragma unroll
+                for (int e = 0; e < E; ++e) st[gi].o[e] = fmaf(p, raw_elt<T>(vr[i], e), st[gi].o[e] * al);
+                st[gi].m = mn;
+            }
+        }
+    }
+
+    // Merge the KPI lanes that hold the same slice of different keys (xor over the key index).
+#pragma unroll
+    for (int w = C::LPK; w < 64; w <<= 1)
+#pragma unroll
+        for (int gi = 0; gi < GC; ++gi) {
+            float o2[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) o2[e] = __shfl_xor(st[gi].o[e], w, 64);
+            const float m2 = __shfl_xor(st[gi].m, w, 64), l2 = __shfl_xor(st[gi].l, w, 64);
+            dec_merge<E>(st[gi], m2, l2, o2);
+        }
+
+    // Merge the waves in LDS (fixed order), then lanes 0 .. LPK-1 of wave 0 write the split.
+    __shared__ float red[kDecWaves][GC][D + 2];
+    if (kl == 0)
+#pragma unroll
+        for (int gi = 0; gi < GC; ++gi) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) red[wave][gi][sub * E + e] = st[gi].o[e];
+            if (sub == 0) {
+                red[wave][gi][D] = st[gi].m;
+                red[wave][gi][D + 1] = st[gi].l;
+            }
+        }
+    __syncthreads();
+    if (wave != 0 || kl != 0) return;
+#pragma unroll
+    for (int gi = 0; gi < GC; ++gi) {
+        if (gi >= gn) break;
+        DecState<E> t;
+        t.m = red[0][gi][D];
+        t.l = red[0][gi][D + 1];
+#pragma unroll
+        for (int e = 0; e < E; ++e) t.o[e] = red[0][gi][sub * E + e];
+        for (int w = 1; w < kDecWaves; ++w) {
+            float o2[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) o2[e] = red[w][gi][sub * E + e];
+            dec_merge<E>(t, red[w][gi][D], red[w][gi][D + 1], o2);
+        }
+        const size_t bh = (size_t)b * a.Hq + h0 + gi;
+        const size_t ps = (size_t)s * a.B * a.Hq + bh;
+        const float inv = t.l > 0.f ? 1.0f / t.l : 0.f;
+        float *po = a.part_o + ps * D + sub * E;
+#pragma unroll
+        for (int e = 0; e < E; e += 4) *reinterpret_cast<f32x4 *>(po + e) =
+            f32x4{t.o[e] * inv, t.o[e + 1] * inv, t.o[e + 2] * inv, t.o[e + 3] * inv};
+        if (sub == 0) a.part_lse[ps] = t.l > 0.f ? (t.m + __log2f(t.l)) * kLn2 : -INFINITY;
+    }
+}
+
+// One wave per (batch, query head): lane d < D combines column d of the splits' outputs.
+template <int D, typename T>
+__global__ void __launch_bounds__(256) decode_merge(DecArgs a) {
+    const int lane = threadIdx.x & 63;
+    const long long bh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (bh >= (long long)a.B * a.Hq) return;
+    const int b = (int)(bh / a.Hq);
+    const int len = min(max(a.lens[b], 0), a.Tc);
+    const int ns = (len + kDecSplit - 1) / kDecSplit;
+    const size_t stride = (size_t)a.B * a.Hq;
+    float mx = -INFINITY;
+    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_lse[s * stride + bh]);
+    float wsum = 0.f, acc = 0.f;
+    if (mx > -INFINITY)
+        for (int s = 0; s < ns; ++s) {
+            const float w = __expf(a.part_lse[s * stride + bh] - mx);
+            wsum += w;
+            if (lane < D) acc += w * a.part_o[(s * stride + bh) * D + lane];
+        }
+    if (lane < D) static_cast<T *>(a.o)[bh * D + lane] = to_elt<T>(wsum > 0.f ? acc / wsum : 0.f);
+    if (lane == 0) a.lse[bh] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+}
+
+template <int D, typename T>
+hipError_t launch_decode_t(DecArgs &a, hipStream_t st) {
+    // Query heads per work-group: the whole group when it is small, else chunks of 8.
+    const int gc = a.G <= 1 ? 1 : a.G <= 2 ? 2 : a.G <= 4 ? 4 : 8;
+    a.nhc = (a.G + gc - 1) / gc;
+    const void *fn = gc == 1   ? (const void *)decode_split<D, T, 1>
+                     : gc == 2 ? (const void *)decode_split<D, T, 2>
+                     : gc == 4 ? (const void *)decode_split<D, T, 4>
+                               : (const void *)decode_split<D, T, 8>;
+    void *params[] = {&a};
+    const long long gy = (long long)a.B * a.Hkv * a.nhc;
+    if (gy > 65535) return hipErrorInvalidValue;
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)a.nsplit, (unsigned)gy), dim3(64 * kDecWaves),
+                                   params, 0, st);
+    if (e != hipSuccess) return e;
+    const long long nbh = (long long)a.B * a.Hq;
+    return hipLaunchKernel((const void *)decode_merge<D, T>, dim3((unsigned)((nbh + 3) / 4)),
+                           dim3(256), params, 0, st);
+}
+
+}  // namespace
+
+int decode_splits(int Tc) { return (Tc + kDecSplit - 1) / kDecSplit; }
+
+hipError_t launch_decode(const Shape &s, int bf16, const void *q, const void *k, const void *v,
+                         const int *lens, void *o, float *lse, float *part_o, float *part_lse,
+                         hipStream_t st) {
+    DecArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.lens = lens;
+    a.o = o;
+    a.lse = lse;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.B = s.B;
+    a.Hq = s.Hq;
+    a.Hkv = s.Hkv;
+    a.Tc = s.T;
+    a.G = s.G;
+    a.nsplit = decode_splits(s.T);
+    a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));
+    if (bf16) return s.D == 64 ? launch_decode_t<64, __bf16>(a, st) : launch_decode_t<32, __bf16>(a, st);
+    return s.D == 64 ? launch_decode_t<64, float>(a, st) : launch_decode_t<32, float>(a, st);
+}
+
+}  // namespace ne

@@ -103,4 +103,13 @@ hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long r
 hipError_t launch_rope_bf16(const Shape &s, const void *x, void *y, long long rows,
                             hipStream_t st);
 
+// Decode step against a key/value cache (s.T = cache length Tc): one query per (batch, query
+// head), keys 0 .. lens[b] - 1.  q, o: [B][Hq][D]; k, v: [B][Hkv][Tc][D] (bf16 when bf16 != 0,
+// else fp32); lse [B][Hq] fp32; part_o, part_lse: workspace of decode_splits(Tc) splits,
+// [split][B][Hq][D] and [split][B][Hq] fp32.
+int decode_splits(int Tc);
+hipError_t launch_decode(const Shape &s, int bf16, const void *q, const void *k, const void *v,
+                         const int *lens, void *o, float *lse, float *part_o, float *part_lse,
+                         hipStream_t st);
+
 }  // namespace ne

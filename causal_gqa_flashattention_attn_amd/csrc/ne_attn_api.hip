@@ -175,6 +175,28 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
                      stream);
 }
 
+// Decode workspace: the splits' outputs then their lse, each region 256-aligned.
+struct DecLayout {
+    size_t part_lse, total;
+};
+
+DecLayout dec_layout(int B, int Hq, int Tc, int D) {
+    const size_t ns = (size_t)ne::decode_splits(Tc);
+    DecLayout L{};
+    L.part_lse = up256(4 * ns * (size_t)B * (size_t)Hq * (size_t)D);
+    L.total = L.part_lse + up256(4 * ns * (size_t)B * (size_t)Hq);
+    return L;
+}
+
+int decode_check(int B, int Hq, int Hkv, int Tc, int D, int dtype, ne::Shape &s) {
+    const int rc = check_shape(B, Hq, Hkv, Tc, D, 0, dtype, 0.f, s);
+    if (rc != NE_OK) return rc;
+    // Work-groups per split: (batch, key/value head, chunk of up to 8 query heads).
+    const long long gy = (long long)B * Hkv * ((s.G + 7) / 8);
+    if (gy > 65535) return NE_ERR_SHAPE;
+    return NE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,6 +250,29 @@ size_t ne_attn_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int dtype,
     ne::Shape s;
     if (check_shape(B, Hq, Hkv, T, D, 1, dtype, rope_base, s) != NE_OK) return 0;
     return ws_layout(s, dtype).total;
+}
+
+int ne_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *lens,
+                   void *o, float *lse, void *workspace, int B, int Hq, int Hkv, int Tc, int D,
+                   int dtype, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !lens || !o || !lse || !workspace) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = decode_check(B, Hq, Hkv, Tc, D, dtype, s);
+    if (rc != NE_OK) return rc;
+    if (any_misaligned({q, k_cache, v_cache, lens, o, lse, workspace})) return NE_ERR_ALIGN;
+    const DecLayout L = dec_layout(B, Hq, Tc, D);
+    float *part_o = static_cast<float *>(workspace);
+    float *part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.part_lse);
+    return ne::launch_decode(s, dtype == NE_BF16, q, k_cache, v_cache, lens, o, lse, part_o,
+                             part_lse, stream) == hipSuccess
+               ? NE_OK
+               : NE_ERR_HIP;
+}
+
+size_t ne_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Tc, int D, int dtype) {
+    ne::Shape s;
+    if (decode_check(B, Hq, Hkv, Tc, D, dtype, s) != NE_OK) return 0;
+    return dec_layout(B, Hq, Tc, D).total;
 }
 
 size_t ne_attn_bwd_workspace_bytes(int B, int Hq, int T) {

@@ -138,6 +138,31 @@ int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float
 size_t ne_attn_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int dtype,
                                float rope_base);
 
+/*
+ * One decode step against a key/value cache, for autoregressive generation (the pages say the
+ * attention supports a KV cache for it: "NanoEuler" article on ainews.cool, section "technical
+ * deep dive", attention item).  Each (batch b, query head h) has one new query q[b][h]; it
+ * attends to the cached keys j = 0 .. lens[b] - 1 of key/value head h / (Hq / Hkv), which
+ * include its own position, so no further mask applies:
+ *   s_j = q . k_j / sqrt(D),  lse = log sum_j exp(s_j),  o = sum_j exp(s_j - lse) v_j.
+ * Any RoPE must already be applied to q and to the cached keys.
+ *
+ * q, o: [B][Hq][D]; k_cache, v_cache: [B][Hkv][Tc][D] (Tc = cache capacity); dtype NE_F32 or
+ * NE_BF16 for these four (arithmetic in fp32); lse: [B][Hq] float32; lens: [B] int32, in device
+ * memory, read by the kernels (a value outside 0 .. Tc is clamped to it; lens[b] = 0 gives
+ * o = 0, lse = -inf).  workspace: caller-owned device memory of
+ * ne_attn_decode_workspace_bytes(...) bytes (partial results of the splits of the cache; its
+ * contents on return are unspecified).  Errors as above; NE_ERR_SHAPE also when
+ * B * Hkv * ceil(Hq / Hkv / 8) exceeds 65535.
+ */
+int ne_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *lens,
+                   void *o, float *lse, void *workspace, int B, int Hq, int Hkv, int Tc, int D,
+                   int dtype, hipStream_t stream);
+
+/* Bytes of the decode workspace: 4 * S * B * Hq * (D + 1) with S = ceil(Tc / 256), in two
+ * regions each rounded up to 256 bytes; 0 if the arguments are invalid. */
+size_t ne_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Tc, int D, int dtype);
+
 /* Bytes of the workspace of ne_attn_bwd: 4 * B * Hq * T (0 if an argument is below 1). */
 size_t ne_attn_bwd_workspace_bytes(int B, int Hq, int T);
 

@@ -182,3 +182,36 @@ def test_single_hip_runtime_in_process():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout.strip().splitlines()[-1]
     assert out == "1"
+
+
+def decode_call(ne, ptrs=None, B=2, Hq=4, Hkv=2, Tc=300, D=64, dtype=0):
+    L = ne.load()
+    p = ptrs or [A] * 7
+    return L.ne_attn_decode(*[VP(x) for x in p], B, Hq, Hkv, Tc, D, dtype, VP(0))
+
+
+def test_decode_workspace_bytes(ne):
+    """Splits of 256 cached keys: outputs [S][B][Hq][D] then lse [S][B][Hq], fp32, each region
+    on a 256-byte boundary."""
+    B, Hq, Hkv, Tc, D = 3, 6, 2, 700, 64
+    S = (Tc + 255) // 256
+    for dtype in (0, 1):
+        assert ne.ne_attn_decode_workspace_bytes(B, Hq, Hkv, Tc, D, dtype) == (
+            up256(4 * S * B * Hq * D) + up256(4 * S * B * Hq))
+    assert ne.ne_attn_decode_workspace_bytes(B, Hq, 4, Tc, D, 0) == 0     # Hq % Hkv
+    assert ne.ne_attn_decode_workspace_bytes(B, Hq, Hkv, 0, D, 0) == 0    # empty cache
+    assert ne.ne_attn_decode_workspace_bytes(B, Hq, Hkv, Tc, 128, 0) == 0  # unsupported D
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_decode_validates(ne, which):
+    p = [A] * 7
+    p[which] = 0
+    assert decode_call(ne, p) == ne.NE_ERR_NULL
+    p[which] = A + 4
+    assert decode_call(ne, p) == ne.NE_ERR_ALIGN
+    assert decode_call(ne, Hkv=3) == ne.NE_ERR_SHAPE
+    assert decode_call(ne, Tc=0) == ne.NE_ERR_SHAPE
+    assert decode_call(ne, B=70000, Hq=1, Hkv=1) == ne.NE_ERR_SHAPE   # grid rows past 65535
+    assert decode_call(ne, D=48) == ne.NE_ERR_UNSUPPORTED
+    assert decode_call(ne, dtype=3) == ne.NE_ERR_UNSUPPORTED
