@@ -16,11 +16,19 @@ Per-kernel durations come from HIP events recorded on the stream the kernels are
 around every launch of the timed steps.  The `roofline` object describes the kernel with the
 largest average duration; `cpu_baseline` times the fp64 oracle on the host cores on a bounded
 sample of the same workload.  Prints one JSON line.
+
+    python bench.py --workload decode_gpu_model | decode_long
+
+times instead one decode step against a key/value cache (ne_attn_decode: split kernel then
+merge kernel): `value` is GB/s of the cache positions actually attended (plus q, o, lse) per
+wall-clock step, and `roofline` compares the same bytes over the HIP-event time of the step
+with the HBM peak.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import gc
 import hashlib
 import json
@@ -122,8 +130,114 @@ def cpu_baseline(w, x, min_seconds: float):
                       f"(B=1 Hq{w.Hq} Hkv{w.Hkv} T{w.T} D{w.D}), {el:.1f} s, fp64"}
 
 
+def cpu_baseline_decode(w, x, min_seconds: float):
+    """The fp64 oracle's decode step on batch rows 0, 1, 2, ... of the same inputs (cycling)
+    until `min_seconds` have passed; GB/s of cached keys and values read."""
+    import oracle
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        b = done % w.B
+        sl = slice(b, b + 1)
+        oracle.attn_decode(x["q"][sl], x["k"][sl], x["v"][sl], x["lens"][sl])
+        nbytes += dataclasses.replace(w, B=1).cache_bytes(x["lens"][sl])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or done >= 64 * w.B:
+            break
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} single-row decode steps of {w.name} (B=1 Hq{w.Hq} Hkv{w.Hkv} "
+                      f"Tc{w.Tc} D{w.D}, lengths of the batch rows cycled), {el:.1f} s, fp64"}
+
+
+def main_decode(a):
+    """Decode step (`--workload decode_*`): GB/s of the key/value cache read per step."""
+    import numpy as np
+    import torch
+
+    import causal_gqa_flashattention_attn_amd as ne
+    from workloads import DECODE_WORKLOADS, make_decode_inputs
+
+    w = DECODE_WORKLOADS[a.workload]
+    x = make_decode_inputs(w, a.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(dt).contiguous() for n in ("q", "k", "v"))
+    lens = torch.from_numpy(x["lens"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    code = ne.NE_BF16 if w.dtype == "bf16" else ne.NE_F32
+    ws = torch.empty(ne.ne_attn_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Tc, w.D, code),
+                     dtype=torch.uint8, device=dev)
+    L = ne.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = (P(q), P(k), P(v), P(lens), P(o), P(lse), P(ws), w.B, w.Hq, w.Hkv, w.Tc, w.D, code,
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+
+    def step():
+        rc = L.ne_attn_decode(*args)
+        if rc != ne.NE_OK:
+            raise ne.NeAttnError(rc, "ne_attn_decode")
+
+    if a.copy_mib > 0:  # a device copy of known size, to calibrate byte counters
+        src = torch.ones(a.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    gc.disable()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(a.steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    ms_per_step = (t1 - t0) * 1e3 / a.steps
+    ev_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)]))
+    nbytes = w.cache_bytes(x["lens"])
+    line = {
+        "metric": f"attn decode GB/s (cache bytes read per step), B{w.B} Hq{w.Hq}/Hkv{w.Hkv} "
+                  f"Tc{w.Tc} D{w.D} {w.dtype}",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tc": w.Tc,
+                   "D": w.D, "cached_positions": int(np.sum(x["lens"])), "seed": a.seed},
+        "roofline": {"bound": "hbm", "kernel": "decode step (split + merge)",
+                     "achieved": round(nbytes / (ev_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline_decode(w, x, a.cpu_seconds),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
+    if a.workload.startswith("decode"):
+        world = int(os.environ.get("WORLD_SIZE", "1"))
+        if a.gpus != 1 or world != 1:
+            print("bench.py measures one GPU only (run with --gpus 1)", file=sys.stderr)
+            sys.exit(2)
+        return main_decode(a)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:

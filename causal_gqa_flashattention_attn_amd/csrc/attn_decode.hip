@@ -49,7 +49,7 @@ struct DecCfg {
     static constexpr int LPK = D / E;
     static constexpr int KPI = 64 / LPK;
     static constexpr int NIT = kDecKeysPerWave / KPI;
-    static constexpr int PMAX = GC <= 2 ? 8 : GC == 4 ? 4 : 2;
+    static constexpr int PMAX = GC <= 4 ? 8 : 4;
     static constexpr int PASS = NIT < PMAX ? NIT : PMAX;
     static_assert(LPK >= 1 && 64 % LPK == 0 && NIT % PASS == 0, "unsupported head size");
 };
@@ -83,6 +83,23 @@ __device__ __forceinline__ void load_row16(const T *p, float (&x)[16 / sizeof(T)
 template <typename T>
 __device__ __forceinline__ T to_elt(float x) {
     return (T)x;
+}
+
+// Sum over each aligned group of N lanes (N = 4, 8 or 16), left in every lane of the group, by
+// DPP moves (plain VALU operations): swaps within quads, then the mirror of each 8- and 16-lane
+// row.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1 .. 16 lanes");
+    auto dpp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value,
+                                                       0xf, 0xf, false));
+    };
+    if constexpr (N >= 2) x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm 1,0,3,2
+    if constexpr (N >= 4) x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
+    if constexpr (N >= 8) x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    if constexpr (N >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}); // row_mirror
+    return x;
 }
 
 // Running (m, l, o) of one query head over some keys: scores in base 2, o unnormalised.
@@ -151,6 +168,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
             kr[i] = load_raw16<T>(kb + (size_t)j * D);
             vr[i] = load_raw16<T>(vb + (size_t)j * D);
         }
+        // Scores of the pass's keys, then one running-maximum update per head, then the sums.
+        float sc[C::PASS][GC];
 #pragma unroll
         for (int i = 0; i < C::PASS; ++i) {
             const bool valid = kw + (p0 + i) * C::KPI + kl < len;
@@ -159,18 +178,31 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) d = fmaf(qv[gi][e], raw_elt<T>(kr[i], e), d);
-                // the row's dot product: sum over the LPK lanes that hold it
-#pragma unroll
-                for (int w = 1; w < C::LPK; w <<= 1) d += __shfl_xor(d, w, 64);
-                const float sc = valid ? d : -INFINITY;
-                const float mn = fmaxf(st[gi].m, sc);
-                const float al = fast_exp2(st[gi].m - mn), p = fast_exp2(sc - mn);
-                st[gi].l = st[gi].l * al + p;
-#pragma unroll
-                for (int e = 0; e < E; ++e) st[gi].o[e] = fmaf(p, raw_elt<T>(vr[i], e), st[gi].o[e] * al);
-                st[gi].m = mn;
+                d = group_sum<C::LPK>(d);  // the row's dot product: its LPK lanes together
+                sc[i][gi] = valid ? d : -INFINITY;
             }
         }
+#pragma unroll
+        for (int gi = 0; gi < GC; ++gi) {
+            float pm = sc[0][gi];
+#pragma unroll
+            for (int i = 1; i < C::PASS; ++i) pm = fmaxf(pm, sc[i][gi]);
+            const float mn = fmaxf(st[gi].m, pm);
+            const float al = fast_exp2(st[gi].m - mn);
+            st[gi].l *= al;
+#pragma unroll
+            for (int e = 0; e < E; ++e) st[gi].o[e] *= al;
+            st[gi].m = mn;
+        }
+#pragma unroll
+        for (int i = 0; i < C::PASS; ++i)
+#pragma unroll
+            for (int gi = 0; gi < GC; ++gi) {
+                const float p = fast_exp2(sc[i][gi] - st[gi].m);
+                st[gi].l += p;
+#pragma unroll
+                for (int e = 0; e < E; ++e) st[gi].o[e] = fmaf(p, raw_elt<T>(vr[i], e), st[gi].o[e]);
+            }
     }
 
     // Merge the KPI lanes that hold the same slice of different keys (xor over the key index).
@@ -224,26 +256,44 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
     }
 }
 
-// One wave per (batch, query head): lane d < D combines column d of the splits' outputs.
+// One wave per (batch, query head).  The splits' lse are combined across lanes (one split per
+// lane, in rounds of 64); the outputs with 16-byte loads, 64 / (D / 4) splits per wave-wide load,
+// all loads independent, then summed over the lanes that hold the same columns.
 template <int D, typename T>
-__global__ void __launch_bounds__(256) decode_merge(DecArgs a) {
-    const int lane = threadIdx.x & 63;
-    const long long bh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (bh >= (long long)a.B * a.Hq) return;
+__global__ void __launch_bounds__(64) decode_merge(DecArgs a) {
+    constexpr int LPR = D / 4;       // lanes per output row (4 floats each)
+    constexpr int RPW = 64 / LPR;    // rows (splits) per wave-wide load
+    const int lane = threadIdx.x;
+    const long long bh = blockIdx.x;  // one single-wave work-group each, to reach every CU
     const int b = (int)(bh / a.Hq);
     const int len = min(max(a.lens[b], 0), a.Tc);
     const int ns = (len + kDecSplit - 1) / kDecSplit;
     const size_t stride = (size_t)a.B * a.Hq;
     float mx = -INFINITY;
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_lse[s * stride + bh]);
-    float wsum = 0.f, acc = 0.f;
+    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, a.part_lse[s * stride + bh]);
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) mx = fmaxf(mx, __shfl_xor(mx, w, 64));
+    float wsum = 0.f;
+    for (int s = lane; s < ns; s += 64) wsum += __expf(a.part_lse[s * stride + bh] - mx);
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) wsum += __shfl_xor(wsum, w, 64);
+    const int sub = lane % LPR, r = lane / LPR;
+    f32x4 acc{0.f, 0.f, 0.f, 0.f};
     if (mx > -INFINITY)
-        for (int s = 0; s < ns; ++s) {
+        for (int s = r; s < ns; s += RPW) {
             const float w = __expf(a.part_lse[s * stride + bh] - mx);
-            wsum += w;
-            if (lane < D) acc += w * a.part_o[(s * stride + bh) * D + lane];
+            acc += w * *reinterpret_cast<const f32x4 *>(a.part_o + (s * stride + bh) * D + 4 * sub);
         }
-    if (lane < D) static_cast<T *>(a.o)[bh * D + lane] = to_elt<T>(wsum > 0.f ? acc / wsum : 0.f);
+#pragma unroll
+    for (int w = LPR; w < 64; w <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], w, 64);
+    if (r == 0) {
+        const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+        T *orow = static_cast<T *>(a.o) + bh * D + 4 * sub;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) orow[e] = to_elt<T>(acc[e] * inv);
+    }
     if (lane == 0) a.lse[bh] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
@@ -263,8 +313,8 @@ hipError_t launch_decode_t(DecArgs &a, hipStream_t st) {
                                    params, 0, st);
     if (e != hipSuccess) return e;
     const long long nbh = (long long)a.B * a.Hq;
-    return hipLaunchKernel((const void *)decode_merge<D, T>, dim3((unsigned)((nbh + 3) / 4)),
-                           dim3(256), params, 0, st);
+    return hipLaunchKernel((const void *)decode_merge<D, T>, dim3((unsigned)nbh), dim3(64), params,
+                           0, st);
 }
 
 }  // namespace

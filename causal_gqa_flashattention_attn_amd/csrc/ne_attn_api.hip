@@ -194,6 +194,7 @@ int decode_check(int B, int Hq, int Hkv, int Tc, int D, int dtype, ne::Shape &s)
     // Work-groups per split: (batch, key/value head, chunk of up to 8 query heads).
     const long long gy = (long long)B * Hkv * ((s.G + 7) / 8);
     if (gy > 65535) return NE_ERR_SHAPE;
+    if ((long long)B * Hq > 0x7fffffffLL) return NE_ERR_SHAPE;  // merge: a work-group per row
     return NE_OK;
 }
 

@@ -105,3 +105,50 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     if w.dtype == "bf16":
         q, k, v, dO = (round_to_bf16(a) for a in (q, k, v, dO))
     return {"q": q, "k": k, "v": v, "dO": dO}
+
+
+# ---------------------------------------------------------------------------- decode steps
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: a query per (batch, head) against a key/value cache of capacity Tc.
+    Cached lengths are drawn uniformly from [min_len_frac * Tc, Tc] (a generation batch in
+    which every sequence has its own length)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Tc: int
+    D: int
+    dtype: str = "f32"
+    min_len_frac: float = 0.5
+    note: str = ""
+
+    def cache_bytes(self, lens) -> int:
+        """Algorithmic HBM bytes of one step: the cached keys and values of every valid
+        position, q read and o written, lse written."""
+        elt = 2 if self.dtype == "bf16" else 4
+        return (2 * elt * self.Hkv * self.D * int(np.sum(lens))
+                + 2 * elt * self.B * self.Hq * self.D + 4 * self.B * self.Hq)
+
+
+DECODE_WORKLOADS = {
+    "decode_gpu_model": DecodeWorkload("decode_gpu_model", 16, 12, 4, 512, 64, min_len_frac=0.0,
+                                       note="GPU-model heads, generation within its 512 context"),
+    "decode_long": DecodeWorkload("decode_long", 32, 16, 4, 8192, 64, dtype="bf16",
+                                  note="wider model, bf16 cache of 8192 positions"),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: int = 0) -> dict:
+    """float32 q [B,Hq,D], k, v [B,Hkv,Tc,D] (i.i.d. N(0,1), drawn in that order, bf16-rounded
+    for bf16) and int32 lens [B] drawn last."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((w.B, w.Hq, w.D), dtype=np.float32)
+    k = rng.standard_normal((w.B, w.Hkv, w.Tc, w.D), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.Hkv, w.Tc, w.D), dtype=np.float32)
+    lo = max(1, int(round(w.min_len_frac * w.Tc)))
+    lens = rng.integers(lo, w.Tc + 1, size=w.B).astype(np.int32)
+    if w.dtype == "bf16":
+        q, k, v = (round_to_bf16(a) for a in (q, k, v))
+    return {"q": q, "k": k, "v": v, "lens": lens}
