@@ -58,8 +58,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum host time spent on the oracle sample")
     p.add_argument("--copy-mib", type=int, default=0,
-                   help="run one plain device-to-device copy of this many MiB before the steps "
-                        "(reference dispatch of known size for HBM counter calibration)")
+                   help="run three plain device-to-device copies of this many MiB before the "
+                        "steps (reference dispatches of known size for HBM counter calibration)")
     p.add_argument("--graph", action="store_true",
                    help="replay the step from a captured HIP graph instead of eager launches")
     return p.parse_args()
@@ -91,6 +91,19 @@ def source_digest() -> str:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def calibration_copies(torch, dev, mib: int):
+    """Three device-to-device copies of `mib` MiB, each between synchronisations, so that byte
+    counters can be scaled by what they read for a copy of known size (the median copy: a
+    counter can credit part of a dispatch's traffic to its neighbour)."""
+    src = torch.ones(mib * (1 << 18), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    del src, dst
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -181,13 +194,8 @@ def main_decode(a):
         if rc != ne.NE_OK:
             raise ne.NeAttnError(rc, "ne_attn_decode")
 
-    if a.copy_mib > 0:  # a device copy of known size, to calibrate byte counters
-        src = torch.ones(a.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    if a.copy_mib > 0:
+        calibration_copies(torch, dev, a.copy_mib)
 
     for _ in range(a.warmup):
         step()
@@ -224,7 +232,8 @@ def main_decode(a):
         "roofline": {"bound": "hbm", "kernel": "decode step (split + merge)",
                      "achieved": round(nbytes / (ev_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(nbytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+                     "traffic": measured_traffic("decode", w.name),
+                     "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline_decode(w, x, a.cpu_seconds),
     }
     print(json.dumps(line), flush=True)
@@ -291,12 +300,7 @@ def main():
             ev[3].record()
 
     if a.copy_mib > 0:
-        src = torch.ones(a.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copies(torch, dev, a.copy_mib)
 
     graph = None
     if a.graph:
