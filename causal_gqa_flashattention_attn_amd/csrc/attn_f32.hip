@@ -96,6 +96,8 @@ struct Args {
     int B, Hq, Hkv, T, G;
     int hpw, rb, nqt;  // query-tile kernels
     int paired;        // work-groups take mirrored pairs of tiles or key blocks
+    int mstep;         // unpaired causal query tiles: mirrored tiles this many rows of the
+                       // launch order apart (0: longest first)
     int nkb;           // key blocks per head (dK/dV)
     float qscale;      // scale * log2(e)
     float scale;       // 1 / sqrt(D)
@@ -123,8 +125,18 @@ __device__ __forceinline__ QTileWork decode_qwork(const Args &a) {
     r /= nhc;
     w.g = r % a.Hkv;
     w.b = r / a.Hkv;
-    // Longest tile first under a causal mask (the order is immaterial otherwise).
-    w.qt0 = a.nqt - 1 - t;
+    if (a.mstep > 0) {
+        // Rows t and t + mstep of the launch order are `per * mstep` work-groups apart, one
+        // stride of the compute units when work-groups go round-robin over them: those rows
+        // take mirrored tiles (lengths summing to nqt + 1), so every unit gets the same work.
+        // Within each block of 2 mstep rows the long tiles come first.
+        const int u = t / (2 * a.mstep), k = t % (2 * a.mstep);
+        const int pr = u * a.mstep + k % a.mstep;  // pair index, 0 .. nqt/2 - 1
+        w.qt0 = k < a.mstep ? a.nqt - 1 - pr : pr;
+    } else {
+        // Longest tile first under a causal mask (the order is immaterial otherwise).
+        w.qt0 = a.nqt - 1 - t;
+    }
     w.qt1 = a.paired && t < w.qt0 ? t : -1;
     return w;
 }
@@ -666,6 +678,24 @@ hipError_t launch(const void *fn, long long blocks, int threads, size_t lds, hip
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), params, lds, st);
 }
 
+// Launch-order distance of mirrored tiles for an unpaired causal launch of `fn` (see
+// decode_qwork): compute units / work-groups per tile index, when every work-group of the
+// launch is resident at once (then the order decides which work shares a unit) and the shape
+// divides evenly; otherwise 0, longest tile first, which suits launches of several rounds.
+int mirror_step(const Shape &s, const QTileGeom &g, const void *fn) {
+    if (!s.causal || g.paired) return 0;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * g.nwaves, 0) != hipSuccess)
+        return 0;
+    if (g.nblocks > (long long)per_cu * cus) return 0;
+    const long long per = (long long)s.B * s.Hkv * (s.G / g.hpw);
+    if (per <= 0 || cus % per != 0) return 0;
+    const int ms = (int)(cus / per);
+    return g.nqt % (2 * ms) == 0 ? ms : 0;
+}
+
 }  // namespace
 
 QTileGeom qtile_geometry(const Shape &s, bool pair) {
@@ -702,13 +732,14 @@ hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const 
     a.v = v;
     a.out_o = o;
     a.out_lse = lse;
-    const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.fwd != 0);
+    const QTileGeom g = qtile_geometry(s, s.causal && kPairF32.fwd != 0 ? 1 : 0);
     a.hpw = g.hpw;
     a.rb = g.rb;
     a.nqt = g.nqt;
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
     const void *fn = s.D == 64 ? pick_fwd_f32<64>(causal, rope) : pick_fwd_f32<32>(causal, rope);
+    a.mstep = mirror_step(s, g, fn);
     return launch(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
 }
 

@@ -41,6 +41,8 @@ RAGGED = [
     (1, 5, 5, 96, 32), (1, 1, 1, 31, 64), (3, 2, 2, 7, 64),
     # group sizes 5..8: work-groups of 5..8 waves
     (1, 10, 2, 77, 64), (1, 6, 1, 100, 64), (1, 7, 1, 90, 32), (1, 8, 1, 200, 64),
+    # 256 work-groups per tile index: the forward's mirrored tile order with a stride of one row
+    (64, 4, 4, 128, 32),
 ]
 
 
