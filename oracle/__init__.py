@@ -13,6 +13,8 @@ NanoEuler pages each step follows.  This module only marshals numpy arrays:
 * ``rope(x, base, pairing, inverse) -> x rotated``
 * ``attn_decode(q, k, v, lens) -> (o, lse)``: one query per (batch, head) against a key/value
   cache [B, Hkv, Tc, D], keys 0 .. lens[b] - 1 visible
+* ``attn_prefill(q, k, v) -> (o, lse)``: a chunk of Tq queries [B, Hq, Tq, D] at positions
+  Tk - Tq .. Tk - 1 against keys [B, Hkv, Tk, D], causal
 
 Shapes: q, dO: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; lse: [B, Hq, T].  Inputs of any float
 dtype are converted exactly to float64.  ``rope_base = 0`` disables RoPE.
@@ -30,7 +32,8 @@ _SRC = os.path.join(_HERE, "oracle_attn.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-__all__ = ["build", "attn_fwd", "attn_bwd", "attn_decode", "rope", "num_threads"]
+__all__ = ["build", "attn_fwd", "attn_bwd", "attn_decode", "attn_prefill", "rope",
+           "num_threads"]
 
 
 def build() -> str:
@@ -60,6 +63,8 @@ def _load():
     lib.oracle_attn_decode.argtypes = [dp, dp, dp, ctypes.POINTER(ctypes.c_int), dp, dp,
                                        i, i, i, i, i]
     lib.oracle_attn_decode.restype = i
+    lib.oracle_attn_prefill.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i]
+    lib.oracle_attn_prefill.restype = i
     lib.oracle_rope.argtypes = [dp, i, i, i, i, ctypes.c_double, i, i]
     lib.oracle_rope.restype = i
     lib.oracle_num_threads.argtypes = []
@@ -136,6 +141,24 @@ def attn_decode(q, k, v, lens):
                                     ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), _ptr(o),
                                     _ptr(lse), B, Hq, Hkv, Tc, D)
     _check(rc, "oracle_attn_decode")
+    return o, lse
+
+
+def attn_prefill(q, k, v):
+    """q [B,Hq,Tq,D] at positions Tk-Tq .. Tk-1; k, v [B,Hkv,Tk,D] -> (o [B,Hq,Tq,D],
+    lse [B,Hq,Tq]) in float64, causal."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, Tq, D], k and v [B, Hkv, Tk, D]")
+    B, Hq, Tq, D = q.shape
+    _, Hkv, Tk, Dk = k.shape
+    if k.shape[0] != B or Dk != D:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape}")
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq, Tq), dtype=np.float64)
+    rc = _load().oracle_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                     Tq, Tk, D)
+    _check(rc, "oracle_attn_prefill")
     return o, lse
 
 

@@ -341,6 +341,61 @@ int oracle_attn_decode(const double *q, const double *k, const double *v, const 
     return failed ? -2 : 0;
 }
 
+/*
+ * Prefill of a chunk of Tq new queries against a cache that already holds Tk - Tq earlier
+ * positions plus the chunk's own (Tk keys in all): query i of the chunk is at position
+ * i + Tk - Tq and, causally, sees keys 0 .. i + Tk - Tq.  Reading: the generation mode the pages
+ * mention (KV cache for autoregressive generation: "NanoEuler" article on ainews.cool, section
+ * "technical deep dive") processes a prompt, or a continuation, in chunks; with Tq = Tk this is
+ * the causal forward, with Tq = 1 a decode step.  The test-suite pins both.  Any RoPE has been
+ * applied by the caller.
+ *
+ * q, o: [B][Hq][Tq][D]; k, v: [B][Hkv][Tk][D]; lse: [B][Hq][Tq].  1 <= Tq <= Tk.
+ */
+int oracle_attn_prefill(const double *q, const double *k, const double *v, double *o,
+                        double *lse, int B, int Hq, int Hkv, int Tq, int Tk, int D)
+{
+    if (check_args(B, Hq, Hkv, Tk, D, 0, 0) || Tq < 1 || Tq > Tk) return -1;
+    if (!q || !k || !v || !o) return -1;
+    int G = Hq / Hkv, off = Tk - Tq;
+    double scale = 1.0 / sqrt((double)D);
+    int failed = 0;
+
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)Tk * sizeof(double));
+        if (!s) {
+            #pragma omp atomic write
+            failed = 1;
+        }
+        #pragma omp for collapse(3) schedule(dynamic, 16)
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < Hq; ++h)
+                for (int i = 0; i < Tq; ++i) {
+                    if (!s) continue;
+                    int g = h / G, n = i + off + 1;
+                    const double *qi = q + IDX4(b, h, i, 0, Hq, Tq, D);
+                    double m = -INFINITY;
+                    for (int j = 0; j < n; ++j) {
+                        s[j] = dot(qi, k + IDX4(b, g, j, 0, Hkv, Tk, D), D) * scale;
+                        if (s[j] > m) m = s[j];
+                    }
+                    double l = 0.0;
+                    for (int j = 0; j < n; ++j) l += exp(s[j] - m);
+                    double *oi = o + IDX4(b, h, i, 0, Hq, Tq, D);
+                    for (int d = 0; d < D; ++d) oi[d] = 0.0;
+                    for (int j = 0; j < n; ++j) {
+                        double p = exp(s[j] - m) / l;
+                        const double *vj = v + IDX4(b, g, j, 0, Hkv, Tk, D);
+                        for (int d = 0; d < D; ++d) oi[d] += p * vj[d];
+                    }
+                    if (lse) lse[((size_t)b * Hq + h) * Tq + i] = m + log(l);
+                }
+        free(s);
+    }
+    return failed ? -2 : 0;
+}
+
 /* Number of OpenMP threads a parallel region of this library uses. */
 int oracle_num_threads(void)
 {

@@ -1,8 +1,8 @@
-"""Pins for the oracle's decode step (one query per head against a key/value cache).
+"""Pins for the oracle's decode step and chunked prefill against a key/value cache.
 
-Decode is the last row of causal attention over a sequence that ends with the new query, so
-the decode oracle is pinned to the causal oracle (itself pinned by brute force, the library's
-fp64 attention and finite differences) and to closed forms.
+Decode is the last row of causal attention over a sequence that ends with the new query, and a
+prefill chunk its last rows, so both are pinned to the causal oracle (itself pinned by brute
+force, the library's fp64 attention and finite differences) and to closed forms.
 """
 import math
 
@@ -63,3 +63,33 @@ def test_decode_rejects_lengths_past_the_cache():
     q, k, v = cache(1, 2, 1, 4, 8, [4], seed=5)
     with pytest.raises(ValueError):
         oracle.attn_decode(q, k, v, [5])
+
+
+# ---------------------------------------------------------------- chunked prefill
+
+@pytest.mark.parametrize("Tq,Tk", [(5, 23), (1, 9), (16, 16), (7, 8)])
+def test_prefill_is_last_rows_of_causal_attention(Tq, Tk):
+    """A chunk of Tq queries at positions Tk-Tq .. Tk-1 is the last Tq rows of causal
+    attention over Tk positions (earlier query rows arbitrary)."""
+    B, Hq, Hkv, D = 2, 6, 2, 16
+    r = np.random.default_rng(6)
+    q = r.standard_normal((B, Hq, Tq, D))
+    k = r.standard_normal((B, Hkv, Tk, D))
+    v = r.standard_normal((B, Hkv, Tk, D))
+    o, lse = oracle.attn_prefill(q, k, v)
+    qf = np.concatenate([r.standard_normal((B, Hq, Tk - Tq, D)), q], axis=2)
+    of, lf = oracle.attn_fwd(qf, k, v, causal=True)
+    np.testing.assert_allclose(o, of[:, :, Tk - Tq:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lf[:, :, Tk - Tq:], rtol=0, atol=1e-12)
+
+
+def test_prefill_of_one_query_is_a_decode_step():
+    B, Hq, Hkv, Tk, D = 3, 4, 2, 19, 8
+    r = np.random.default_rng(8)
+    q = r.standard_normal((B, Hq, 1, D))
+    k = r.standard_normal((B, Hkv, Tk, D))
+    v = r.standard_normal((B, Hkv, Tk, D))
+    o, lse = oracle.attn_prefill(q, k, v)
+    od, ld = oracle.attn_decode(q[:, :, 0], k, v, [Tk] * B)
+    np.testing.assert_allclose(o[:, :, 0], od, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[:, :, 0], ld, rtol=0, atol=1e-12)
