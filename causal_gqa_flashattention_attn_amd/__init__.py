@@ -2,18 +2,19 @@
 
 The functions named like the C entry points (``ne_attn_fwd``, ``ne_attn_bwd``,
 ``ne_attn_fwd_ex``, ``ne_attn_bwd_ex``, ``ne_attn_bwd_dq_ex``, ``ne_attn_bwd_dkdv_ex``,
-``ne_attn_decode``, ``ne_attn_workspace_bytes``, ``ne_attn_decode_workspace_bytes``,
+``ne_attn_decode``, ``ne_attn_prefill``, ``ne_attn_workspace_bytes``, ``ne_attn_decode_workspace_bytes``,
 ``ne_attn_bwd_workspace_bytes``, ``ne_attn_strerror``) only
 marshal arguments: they read sizes from tensor shapes, pass ``data_ptr()`` and the current
 HIP stream, and raise ``NeAttnError`` on a non-zero status.  All arithmetic happens in the HIP
 kernels.  PyTorch provides device memory and streams.
 
-``forward``, ``backward`` and ``decode`` are conveniences that allocate the outputs and the
+``forward``, ``backward``, ``decode`` and ``prefill`` are conveniences that allocate the outputs and the
 workspace with torch and call the entry points.
 
 Tensor layout: q, o, dO, dq: [B, Hq, T, D]; k, v, dk, dv: [B, Hkv, T, D]; lse: [B, Hq, T]
 float32; all contiguous on one GPU; float32, or bfloat16 through the ``_ex`` entry points.
 Decode: q, o: [B, Hq, D]; k_cache, v_cache: [B, Hkv, Tc, D]; lse: [B, Hq]; lens: int32 [B].
+Prefill: q, o: [B, Hq, Tq, D]; k_cache, v_cache: [B, Hkv, Tk, D]; lse: [B, Hq, Tq].
 """
 from __future__ import annotations
 
@@ -23,9 +24,9 @@ import os
 __all__ = [
     "NeAttnError", "library_path", "load", "lib",
     "ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_decode",
+    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_decode", "ne_attn_prefill",
     "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes", "ne_attn_bwd_workspace_bytes",
-    "ne_attn_strerror", "forward", "backward", "decode", "workspace",
+    "ne_attn_strerror", "forward", "backward", "decode", "prefill", "workspace",
     "NE_OK", "NE_ERR_NULL", "NE_ERR_SHAPE", "NE_ERR_UNSUPPORTED", "NE_ERR_ALIGN", "NE_ERR_HIP",
     "NE_F32", "NE_BF16", "EXPORTED_SYMBOLS",
 ]
@@ -35,7 +36,7 @@ NE_F32, NE_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
                     "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_decode",
-                    "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
+                    "ne_attn_prefill", "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
                     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,7 @@ def load():
     L.ne_attn_workspace_bytes.argtypes = [i] * 6 + [f]
     L.ne_attn_workspace_bytes.restype = ctypes.c_size_t
     L.ne_attn_decode.argtypes = [vp] * 7 + [i] * 6 + [vp]
+    L.ne_attn_prefill.argtypes = [vp] * 5 + [i] * 7 + [vp]
     L.ne_attn_decode_workspace_bytes.argtypes = [i] * 6
     L.ne_attn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.ne_attn_bwd_workspace_bytes.argtypes = [i, i, i]
@@ -311,6 +313,28 @@ def ne_attn_decode(q, k_cache, v_cache, lens, o, lse, workspace, stream=None):
     _raise(rc, "ne_attn_decode")
 
 
+def ne_attn_prefill(q, k_cache, v_cache, o, lse, stream=None):
+    """A chunk of Tq queries at positions Tk-Tq .. Tk-1 against the cache [B, Hkv, Tk, D]."""
+    torch = _torch()
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, Hq, Tq, D]; k_cache, v_cache [B, Hkv, Tk, D]")
+    B, Hq, Tq, D = q.shape
+    _, Hkv, Tk, Dk = k_cache.shape
+    if k_cache.shape[0] != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k_cache{tuple(k_cache.shape)}")
+    dt = _dtype_code(q)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("o", o)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have dtype {q.dtype}")
+    if o.shape != q.shape or tuple(lse.shape) != (B, Hq, Tq) or lse.dtype != torch.float32:
+        raise ValueError("o must match q; lse must be float32 [B, Hq, Tq]")
+    _check_tensors(dict(q=q, k_cache=k_cache, v_cache=v_cache, o=o, lse=lse), q.device)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_prefill(_p(q), _p(k_cache), _p(v_cache), _p(o), _p(lse), B, Hq, Hkv,
+                                    Tq, Tk, D, dt, _stream(stream, q.device))
+    _raise(rc, "ne_attn_prefill")
+
+
 # ----------------------------------------------------------------------------- conveniences
 
 def workspace(q, k, rope_base: float = 0.0):
@@ -357,4 +381,13 @@ def decode(q, k_cache, v_cache, lens, stream=None):
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     ws = torch.empty(n, dtype=torch.uint8, device=q.device)
     ne_attn_decode(q, k_cache, v_cache, lens, o, lse, ws, stream=stream)
+    return o, lse
+
+
+def prefill(q, k_cache, v_cache, stream=None):
+    """Allocates o, lse and runs a prefill chunk; returns (o, lse)."""
+    torch = _torch()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ne_attn_prefill(q, k_cache, v_cache, o, lse, stream=stream)
     return o, lse

@@ -58,6 +58,7 @@ struct ArgsB {
     int hpw, rb, nqt;
     int paired;     // work-groups take mirrored pairs of tiles or key blocks
     int nkb;        // key blocks per head (dK/dV)
+    int Tk, qoff;   // forward: key length and position of query row 0 (Tk = T, 0 usually)
     float qscale;   // scale * log2(e)
     float scale;    // 1 / sqrt(D)
     float rope_lb;  // log2(rope base)
@@ -429,6 +430,7 @@ __device__ __forceinline__ void fwd_half(const ArgsB &a, FwdState<D> &st, const 
 
 // One 64-key tile of the forward: its two 32-key halves one after the other (a half entirely
 // above the diagonal or past the end is skipped, and then so is the second).
+// (r0 is the position of the wave's first query row, T the number of keys.)
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void fwd_step(const ArgsB &a, FwdState<D> &st, const unsigned char *sK,
                                          const unsigned char *sV, int kt0, int r0, int T,
@@ -449,16 +451,18 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
-    const int T = a.T;
+    // T query rows; Tk keys; query row r is at position r + qo (a prefill chunk; 0 usually).
+    // The half-tile steps take positions and Tk.
+    const int T = a.T, Tk = a.Tk, qo = a.qoff;
     const int r0 = __builtin_amdgcn_readfirstlane(c.r0);
     const int qrow = r0 + col;
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
-    const __bf16 *kg = a.k + bg * T * D;
-    const __bf16 *vg = a.v + bg * T * D;
+    const __bf16 *kg = a.k + bg * Tk * D;
+    const __bf16 *vg = a.v + bg * Tk * D;
 
     const int wg_rows = 32 * a.rb;
     const int wg_end = min(c.qt * wg_rows + wg_rows, T);
-    const int ntiles = CAUSAL ? (wg_end - 1) / C::BN + 1 : (T + C::BN - 1) / C::BN;
+    const int ntiles = CAUSAL ? (wg_end - 1 + qo) / C::BN + 1 : (Tk + C::BN - 1) / C::BN;
     const bool live = r0 < T;
 
     // The first two K/V tiles are requested before the query row, so the two latencies overlap
@@ -467,7 +471,7 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
     kv.init(wave, nw, lane);
 #pragma unroll
     for (int t = 0; t < R::PD; ++t)
-        if (t < ntiles) kv.issue(kg, vg, t, T, ring + t * R::SB);
+        if (t < ntiles) kv.issue(kg, vg, t, Tk, ring + t * R::SB);
     bf16x8 qv[C::KS];
     load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
 
@@ -492,11 +496,11 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
         wait_vm_lgkm0(min(R::PD - 1, ntiles - 1 - j) * kv.lpw);
         __builtin_amdgcn_s_barrier();
         const unsigned char *sK = ring + ST * R::SB;
-        if (live) fwd_step<D, CAUSAL>(a, st, sK, sK + R::TB, j * C::BN, r0, T, qv, lane);
+        if (live) fwd_step<D, CAUSAL>(a, st, sK, sK + R::TB, j * C::BN, r0 + qo, Tk, qv, lane);
         // Issued after this tile's reads: the compiler makes transposed LDS reads wait for every
         // copy in flight, and by the next tile's reads these have landed.
         if (j + R::PD < ntiles)
-            kv.issue(kg, vg, j + R::PD, T, ring + ((ST + R::PD) % R::NST) * R::SB);
+            kv.issue(kg, vg, j + R::PD, Tk, ring + ((ST + R::PD) % R::NST) * R::SB);
     };
     static_assert(R::NST == 3, "the loop below is unrolled over three stages");
     for (int j = 0; j < ntiles; j += 3) {
@@ -918,6 +922,8 @@ ArgsB make_args_b(const Shape &s) {
     a.Hq = s.Hq;
     a.Hkv = s.Hkv;
     a.T = s.T;
+    a.Tk = s.Tk > 0 ? s.Tk : s.T;
+    a.qoff = a.Tk - s.T;
     a.G = s.G;
     a.scale = (float)(1.0 / sqrt((double)s.D));
     a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));

@@ -94,6 +94,7 @@ struct Args {
     float *out_o, *out_lse, *dq, *dk, *dv, *delta;
     float *qrot;  // dQ pass with RoPE: rotated query rows, written for the dK/dV pass
     int B, Hq, Hkv, T, G;
+    int Tk, qoff;      // forward: key length and position of query row 0 (Tk = T, 0 usually)
     int hpw, rb, nqt;  // query-tile kernels
     int paired;        // work-groups take mirrored pairs of tiles or key blocks
     int mstep;         // unpaired causal query tiles: mirrored tiles this many rows of the
@@ -265,11 +266,13 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
-    const int T = a.T;
+    // T query rows; Tk keys; query row r is at position r + qo (a prefill chunk; 0 usually).
+    const int T = a.T, Tk = a.Tk, qo = a.qoff;
     const int qrow = c.r0 + col;
+    const int p0 = c.r0 + qo;  // position of the wave's first row
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
-    const float *kg = a.k + bg * T * D;
-    const float *vg = a.v + bg * T * D;
+    const float *kg = a.k + bg * Tk * D;
+    const float *vg = a.v + bg * Tk * D;
 
     float qr[C::NS];
     load_row_half<D, ROPE>(qr, a.q + bh * T * D, qrow, T, half, a.qscale, a.rope);
@@ -281,24 +284,24 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
 
     const int wg_rows = 32 * a.rb;
     const int wg_end = min(c.qt * wg_rows + wg_rows, T);
-    const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
+    const int ntiles = CAUSAL ? (wg_end - 1 + qo) / 32 + 1 : (Tk + 31) / 32;
 
     KVStager<D> stg;
-    stg.load(kg, vg, 0, T, wave, nw, lane);
-    stg.store(sK[0], sV[0], 0, T, wave, nw, lane);
+    stg.load(kg, vg, 0, Tk, wave, nw, lane);
+    stg.store(sK[0], sV[0], 0, Tk, wave, nw, lane);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
         const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, T, wave, nw, lane);
+        if (more) stg.load(kg, vg, j + 1, Tk, wave, nw, lane);
         const int k0 = j * 32;
-        if (c.r0 < T && (!CAUSAL || k0 <= c.r0 + 31)) {
+        if (c.r0 < T && (!CAUSAL || k0 <= p0 + 31)) {
             f32x16 s = scores_t<D>(sK[buf], qr, col, half);
-            if ((CAUSAL && k0 + 31 > c.r0) || k0 + 32 > T) {
+            if ((CAUSAL && k0 + 31 > p0) || k0 + 32 > Tk) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int key = k0 + acc_row(v, half);
-                    if ((CAUSAL && key > qrow) || key >= T) s[v] = -INFINITY;
+                    if ((CAUSAL && key > qrow + qo) || key >= Tk) s[v] = -INFINITY;
                 }
             }
             float mx = s[0];
@@ -319,7 +322,7 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
             for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
             accum_t<D>(acc, sV[buf], s, col, half);
         }
-        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw, lane);
+        if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, Tk, wave, nw, lane);
         __syncthreads();
     }
 
@@ -654,6 +657,8 @@ Args make_args(const Shape &s) {
     a.Hq = s.Hq;
     a.Hkv = s.Hkv;
     a.T = s.T;
+    a.Tk = s.Tk > 0 ? s.Tk : s.T;
+    a.qoff = a.Tk - s.T;
     a.G = s.G;
     a.scale = (float)(1.0 / sqrt((double)s.D));
     a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));

@@ -12,6 +12,9 @@ struct Shape {
     int B, Hq, Hkv, T, D, G;  // G = Hq / Hkv
     int causal;
     float rope_base;          // 0: no RoPE
+    // Forward only: keys/values of length Tk >= T, query row i at position i + Tk - T (a chunk
+    // of T new queries against a cache).  0: Tk = T.
+    int Tk = 0;
 };
 
 // Work-group composition of the query-tile kernels (forward and dQ): each work-group serves

@@ -270,6 +270,25 @@ int ne_attn_decode(const void *q, const void *k_cache, const void *v_cache, cons
                : NE_ERR_HIP;
 }
 
+int ne_attn_prefill(const void *q, const void *k_cache, const void *v_cache, void *o, float *lse,
+                    int B, int Hq, int Hkv, int Tq, int Tk, int D, int dtype, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !o || !lse) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = check_shape(B, Hq, Hkv, Tq, D, 1, dtype, 0.f, s);
+    if (rc != NE_OK) return rc;
+    if (Tk < Tq || Tk > (1 << 24) || (double)B * Hkv * Tk * D > 9.0e15) return NE_ERR_SHAPE;
+    if (any_misaligned({q, k_cache, v_cache, o, lse})) return NE_ERR_ALIGN;
+    s.Tk = Tk;
+    const hipError_t e =
+        dtype == NE_BF16
+            ? ne::launch_fwd_bf16(s, q, k_cache, v_cache, o, lse, stream)
+            : ne::launch_fwd_f32(s, static_cast<const float *>(q),
+                                 static_cast<const float *>(k_cache),
+                                 static_cast<const float *>(v_cache), static_cast<float *>(o), lse,
+                                 stream);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
 size_t ne_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Tc, int D, int dtype) {
     ne::Shape s;
     if (decode_check(B, Hq, Hkv, Tc, D, dtype, s) != NE_OK) return 0;

@@ -159,6 +159,20 @@ int ne_attn_decode(const void *q, const void *k_cache, const void *v_cache, cons
                    void *o, float *lse, void *workspace, int B, int Hq, int Hkv, int Tc, int D,
                    int dtype, hipStream_t stream);
 
+/*
+ * Prefill of a chunk of Tq new queries against a key/value cache of Tk positions (Tq <= Tk) that
+ * already holds the chunk's own keys and values at its end: query row i is at position
+ * i + Tk - Tq and sees keys 0 .. i + Tk - Tq (causal).  With Tq = Tk this is ne_attn_fwd_ex
+ * without RoPE; the chunked form serves generation (the KV cache of the pages, as for
+ * ne_attn_decode).  Any RoPE must already be applied to q and to the cached keys.
+ *
+ * q, o: [B][Hq][Tq][D]; k_cache, v_cache: [B][Hkv][Tk][D]; dtype NE_F32 or NE_BF16 for these
+ * four; lse: [B][Hq][Tq] float32.  No workspace.  Errors as above; NE_ERR_SHAPE also when
+ * Tk < Tq.
+ */
+int ne_attn_prefill(const void *q, const void *k_cache, const void *v_cache, void *o, float *lse,
+                    int B, int Hq, int Hkv, int Tq, int Tk, int D, int dtype, hipStream_t stream);
+
 /* Bytes of the decode workspace: 4 * S * B * Hq * (D + 1) with S = ceil(Tc / 256), in two
  * regions each rounded up to 256 bytes; 0 if the arguments are invalid. */
 size_t ne_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Tc, int D, int dtype);

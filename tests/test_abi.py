@@ -215,3 +215,22 @@ def test_decode_validates(ne, which):
     assert decode_call(ne, B=70000, Hq=1, Hkv=1) == ne.NE_ERR_SHAPE   # grid rows past 65535
     assert decode_call(ne, D=48) == ne.NE_ERR_UNSUPPORTED
     assert decode_call(ne, dtype=3) == ne.NE_ERR_UNSUPPORTED
+
+
+def prefill_call(ne, ptrs=None, B=1, Hq=4, Hkv=2, Tq=16, Tk=40, D=64, dtype=0):
+    L = ne.load()
+    p = ptrs or [A] * 5
+    return L.ne_attn_prefill(*[VP(x) for x in p], B, Hq, Hkv, Tq, Tk, D, dtype, VP(0))
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_prefill_validates(ne, which):
+    p = [A] * 5
+    p[which] = 0
+    assert prefill_call(ne, p) == ne.NE_ERR_NULL
+    p[which] = A + 4
+    assert prefill_call(ne, p) == ne.NE_ERR_ALIGN
+    assert prefill_call(ne, Tq=41) == ne.NE_ERR_SHAPE    # longer than the cache
+    assert prefill_call(ne, Tq=0) == ne.NE_ERR_SHAPE
+    assert prefill_call(ne, Hkv=3) == ne.NE_ERR_SHAPE
+    assert prefill_call(ne, D=128) == ne.NE_ERR_UNSUPPORTED
