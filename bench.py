@@ -19,7 +19,8 @@ sample of the same workload.  Prints one JSON line.
 
     python bench.py --workload decode_gpu_model | decode_long
 
-times instead one decode step against a key/value cache (ne_attn_decode: split kernel then
+(or `--workload prefill_gpu_model | prefill_long`, a chunk of queries against a cache, in
+TFLOP/s of its causal work) times instead one decode step against a key/value cache (ne_attn_decode: split kernel then
 merge kernel): `value` is GB/s of the cache positions actually attended (plus q, o, lse) per
 wall-clock step, and `roofline` compares the same bytes over the HIP-event time of the step
 with the HBM peak.
@@ -239,8 +240,102 @@ def main_decode(a):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_prefill(w, x, min_seconds: float):
+    """The fp64 oracle's prefill on batch elements 0, 1, 2, ... (cycling) for `min_seconds`."""
+    import oracle
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        b = done % w.B
+        sl = slice(b, b + 1)
+        oracle.attn_prefill(x["q"][sl], x["k"][sl], x["v"][sl])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or done >= 64 * w.B:
+            break
+    return {"value": dataclasses.replace(w, B=1).flops() * done / el / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} single-batch-element prefill chunks of {w.name} (B=1 Hq{w.Hq} "
+                      f"Hkv{w.Hkv} Tq{w.Tq} Tk{w.Tk} D{w.D}), {el:.1f} s, fp64"}
+
+
+def main_prefill(a):
+    """Chunked prefill (`--workload prefill_*`): TFLOP/s of the causal work of the chunk."""
+    import numpy as np
+    import torch
+
+    import causal_gqa_flashattention_attn_amd as ne
+    from workloads import PREFILL_WORKLOADS, make_prefill_inputs
+
+    w = PREFILL_WORKLOADS[a.workload]
+    x = make_prefill_inputs(w, a.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(dt).contiguous() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device=dev)
+    code = ne.NE_BF16 if w.dtype == "bf16" else ne.NE_F32
+    L = ne.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = (P(q), P(k), P(v), P(o), P(lse), w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.D, code,
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+
+    def step():
+        rc = L.ne_attn_prefill(*args)
+        if rc != ne.NE_OK:
+            raise ne.NeAttnError(rc, "ne_attn_prefill")
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    gc.disable()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(a.steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    ms_per_step = (t1 - t0) * 1e3 / a.steps
+    ev_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)]))
+    fl = w.flops()
+    peak = MFMA_PEAK[w.dtype]
+    line = {
+        "metric": f"attn prefill TFLOP/s (causal work of the chunk), B{w.B} Hq{w.Hq}/Hkv{w.Hkv} "
+                  f"Tq{w.Tq} Tk{w.Tk} D{w.D} {w.dtype}",
+        "value": round(fl / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq, "Tk": w.Tk,
+                   "D": w.D, "seed": a.seed},
+        "roofline": {"bound": "mfma", "kernel": "forward with a query offset",
+                     "achieved": round(fl / (ev_ms * 1e-3) / 1e12, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(fl / (ev_ms * 1e-3) / 1e12 / peak, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": fl},
+        "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline_prefill(w, x, a.cpu_seconds),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
+    if a.workload.startswith("prefill"):
+        world = int(os.environ.get("WORLD_SIZE", "1"))
+        if a.gpus != 1 or world != 1:
+            print("bench.py measures one GPU only (run with --gpus 1)", file=sys.stderr)
+            sys.exit(2)
+        return main_prefill(a)
     if a.workload.startswith("decode"):
         world = int(os.environ.get("WORLD_SIZE", "1"))
         if a.gpus != 1 or world != 1:

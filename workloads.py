@@ -152,3 +152,45 @@ def make_decode_inputs(w: DecodeWorkload, seed: int = 0) -> dict:
     if w.dtype == "bf16":
         q, k, v = (round_to_bf16(a) for a in (q, k, v))
     return {"q": q, "k": k, "v": v, "lens": lens}
+
+
+# ---------------------------------------------------------------------------- prefill chunks
+
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    """A chunk of Tq new queries at positions Tk-Tq .. Tk-1 against Tk cached keys/values."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Tq: int
+    Tk: int
+    D: int
+    dtype: str = "f32"
+    note: str = ""
+
+    def flops(self) -> float:
+        """QK^T and PV over the keys each query sees (position + 1 of them)."""
+        off = self.Tk - self.Tq
+        seen = self.Tq * off + self.Tq * (self.Tq + 1) / 2
+        return 4.0 * self.B * self.Hq * self.D * seen
+
+
+PREFILL_WORKLOADS = {
+    "prefill_gpu_model": PrefillWorkload("prefill_gpu_model", 16, 12, 4, 128, 512, 64,
+                                         note="GPU-model heads: the last 128 of 512 positions"),
+    "prefill_long": PrefillWorkload("prefill_long", 4, 16, 4, 1024, 8192, 64, dtype="bf16",
+                                    note="wider model, bf16: a 1024-token chunk after 7168"),
+}
+
+
+def make_prefill_inputs(w: PrefillWorkload, seed: int = 0) -> dict:
+    """float32 q [B,Hq,Tq,D], k, v [B,Hkv,Tk,D], i.i.d. N(0,1) in that order (bf16-rounded for
+    bf16)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((w.B, w.Hq, w.Tq, w.D), dtype=np.float32)
+    k = rng.standard_normal((w.B, w.Hkv, w.Tk, w.D), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.Hkv, w.Tk, w.D), dtype=np.float32)
+    if w.dtype == "bf16":
+        q, k, v = (round_to_bf16(a) for a in (q, k, v))
+    return {"q": q, "k": k, "v": v}
