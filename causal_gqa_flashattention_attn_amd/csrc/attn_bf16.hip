@@ -971,6 +971,7 @@ hipError_t launch_b(const void *fn, long long blocks, int threads, size_t lds, h
 
 hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const void *v, void *o,
                            float *lse, hipStream_t st) {
+    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;  // kernels for D = 32, 64
     ArgsB a = make_args_b(s);
     a.q = static_cast<const __bf16 *>(q);
     a.k = static_cast<const __bf16 *>(k);
@@ -987,6 +988,7 @@ hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const v
 hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const void *v,
                           const void *o, const float *lse, const void *dO, void *dq, float *delta,
                           void *qrot, hipStream_t st) {
+    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;  // kernels for D = 32, 64
     ArgsB a = make_args_b(s);
     a.q = static_cast<const __bf16 *>(q);
     a.k = static_cast<const __bf16 *>(k);
@@ -1007,6 +1009,7 @@ hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const vo
 hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const void *v,
                             const float *lse, const void *dO, const float *delta, void *dk,
                             void *dv, hipStream_t st) {
+    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;  // kernels for D = 32, 64
     ArgsB a = make_args_b(s);
     a.q = static_cast<const __bf16 *>(q);
     a.k = static_cast<const __bf16 *>(k);
@@ -1026,6 +1029,7 @@ hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const 
 
 hipError_t launch_rope_bf16(const Shape &s, const void *x, void *y, long long rows,
                             hipStream_t st) {
+    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;  // kernels for D = 32, 64
     const __bf16 *xb = static_cast<const __bf16 *>(x);
     __bf16 *yb = static_cast<__bf16 *>(y);
     RopeTurns rt = rope_turns(s);

@@ -85,12 +85,14 @@ __device__ __forceinline__ T to_elt(float x) {
     return (T)x;
 }
 
-// Sum over each aligned group of N lanes (N = 4, 8 or 16), left in every lane of the group, by
-// DPP moves (plain VALU operations): swaps within quads, then the mirror of each 8- and 16-lane
-// row.
+// Sum over each aligned group of N lanes (N = 1 .. 32, a power of two), left in every lane of the
+// group, by DPP moves (plain VALU operations): swaps within quads, then the mirror of each 8- and
+// 16-lane row; a group of 32 then adds the other 16-lane row by a lane swap (both rows add the
+// same two values, so every lane of the group holds the same sum).
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1 .. 16 lanes");
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32,
+                  "group of 1 .. 32 lanes");
     auto dpp = [](float v, auto ctrl) {
         return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value,
                                                        0xf, 0xf, false));
@@ -99,6 +101,7 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (N >= 4) x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
     if constexpr (N >= 8) x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
     if constexpr (N >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}); // row_mirror
+    if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
     return x;
 }
 
@@ -340,8 +343,13 @@ hipError_t launch_decode(const Shape &s, int bf16, const void *q, const void *k,
     a.G = s.G;
     a.nsplit = decode_splits(s.T);
     a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));
-    if (bf16) return s.D == 64 ? launch_decode_t<64, __bf16>(a, st) : launch_decode_t<32, __bf16>(a, st);
-    return s.D == 64 ? launch_decode_t<64, float>(a, st) : launch_decode_t<32, float>(a, st);
+    if (bf16)
+        return s.D == 128  ? launch_decode_t<128, __bf16>(a, st)
+               : s.D == 64 ? launch_decode_t<64, __bf16>(a, st)
+                           : launch_decode_t<32, __bf16>(a, st);
+    return s.D == 128  ? launch_decode_t<128, float>(a, st)
+           : s.D == 64 ? launch_decode_t<64, float>(a, st)
+                       : launch_decode_t<32, float>(a, st);
 }
 
 }  // namespace ne

@@ -342,7 +342,7 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_FWD_WAVES_PER_EU)))
+__global__ void __launch_bounds__(D == 128 ? 256 : 512) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_FWD_WAVES_PER_EU)))
 fwd_f32(Args a) {
     __shared__ __attribute__((aligned(16))) float sK[2][32 * Cfg<D>::LD];
     __shared__ __attribute__((aligned(16))) float sV[2][32 * Cfg<D>::LD];
@@ -455,7 +455,7 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_DQ_WAVES_PER_EU)))
+__global__ void __launch_bounds__(D == 128 ? 256 : 512) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_DQ_WAVES_PER_EU)))
 dq_f32(Args a) {
     __shared__ __attribute__((aligned(16))) float sK[2][32 * Cfg<D>::LD];
     __shared__ __attribute__((aligned(16))) float sV[2][32 * Cfg<D>::LD];
@@ -610,7 +610,7 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_DKDV_WAVES_PER_EU)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_DKDV_WAVES_PER_EU)))
 dkdv_f32(Args a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int per = a.B * a.Hkv;
@@ -706,7 +706,9 @@ int mirror_step(const Shape &s, const QTileGeom &g, const void *fn) {
 QTileGeom qtile_geometry(const Shape &s, bool pair) {
     QTileGeom g{};
     g.hpw = 1;
-    for (int d = 8; d >= 1; --d)
+    // At D = 128 a wave needs more than 256 registers, so a work-group holds at most 4 waves
+    // (one per SIMD of a compute unit).
+    for (int d = s.D == 128 ? 4 : 8; d >= 1; --d)
         if (s.G % d == 0) {
             g.hpw = d;
             break;
@@ -743,7 +745,9 @@ hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const 
     a.nqt = g.nqt;
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
-    const void *fn = s.D == 64 ? pick_fwd_f32<64>(causal, rope) : pick_fwd_f32<32>(causal, rope);
+    const void *fn = s.D == 128  ? pick_fwd_f32<128>(causal, rope)
+                     : s.D == 64 ? pick_fwd_f32<64>(causal, rope)
+                                 : pick_fwd_f32<32>(causal, rope);
     a.mstep = mirror_step(s, g, fn);
     return launch(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
 }
@@ -767,7 +771,9 @@ hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const f
     a.nqt = g.nqt;
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
-    const void *fn = s.D == 64 ? pick_dq_f32<64>(causal, rope) : pick_dq_f32<32>(causal, rope);
+    const void *fn = s.D == 128  ? pick_dq_f32<128>(causal, rope)
+                     : s.D == 64 ? pick_dq_f32<64>(causal, rope)
+                                 : pick_dq_f32<32>(causal, rope);
     return launch(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
 }
 
@@ -787,9 +793,13 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
     a.paired = g.paired;
     a.nkb = g.nkb;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
-    const size_t lds = (size_t)g.nwaves *
-                       (s.D == 64 ? dkdv_wave_floats<64>() : dkdv_wave_floats<32>()) * sizeof(float);
-    const void *fn = s.D == 64 ? pick_dkdv_f32<64>(causal, rope) : pick_dkdv_f32<32>(causal, rope);
+    const int wf = s.D == 128 ? dkdv_wave_floats<128>()
+                   : s.D == 64 ? dkdv_wave_floats<64>()
+                               : dkdv_wave_floats<32>();
+    const size_t lds = (size_t)g.nwaves * wf * sizeof(float);
+    const void *fn = s.D == 128  ? pick_dkdv_f32<128>(causal, rope)
+                     : s.D == 64 ? pick_dkdv_f32<64>(causal, rope)
+                                 : pick_dkdv_f32<32>(causal, rope);
     return launch(fn, g.nblocks, 64 * g.nwaves, lds, st, a);
 }
 
@@ -801,7 +811,9 @@ hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long r
     const long long per_pos = (long long)T * (s.D / 4);
     const unsigned gx = (unsigned)((per_pos + 255) / 256);
     const long long gy = std::max(1LL, std::min(nbh, std::max(nbh / 8, 2048LL / (long long)gx)));
-    const void *fn = s.D == 64 ? (const void *)rope_rows_f32<64> : (const void *)rope_rows_f32<32>;
+    const void *fn = s.D == 128  ? (const void *)rope_rows_f32<128>
+                     : s.D == 64 ? (const void *)rope_rows_f32<64>
+                                 : (const void *)rope_rows_f32<32>;
     void *params[] = {&x, &y, &nbh, &T, &rt};
     return hipLaunchKernel(fn, dim3(gx, (unsigned)std::min(gy, 65535LL)), dim3(256), params, 0, st);
 }

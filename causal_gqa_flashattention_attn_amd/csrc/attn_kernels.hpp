@@ -89,13 +89,13 @@ hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const 
 
 // Turns per position of each RoPE pair, base^(-2i/D) / (2 pi), evaluated on the host in double.
 struct RopeTurns {
-    double per_pos[32];
+    double per_pos[64];
 };
 
 inline RopeTurns rope_turns(const Shape &s) {
     RopeTurns r{};
     const double lb = s.rope_base > 0.f ? log2((double)s.rope_base) : 0.0;
-    for (int i = 0; i < s.D / 2 && i < 32; ++i)
+    for (int i = 0; i < s.D / 2 && i < 64; ++i)
         r.per_pos[i] = exp2(-(2.0 * i / s.D) * lb) * 0.15915494309189535;
     return r;
 }

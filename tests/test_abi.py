@@ -116,7 +116,8 @@ def test_bad_shapes(ne, kw):
     assert fwd(ne, dtype=0, **kw) == ne.NE_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(D=16), dict(D=128), dict(D=48), dict(dtype=2),
+@pytest.mark.parametrize("kw", [dict(D=16), dict(D=256), dict(D=48), dict(dtype=2),
+                                dict(dtype=1, D=128),
                                 dict(dtype=-1), dict(dtype=0, rope=-1.0),
                                 dict(dtype=0, rope=float("inf")), dict(dtype=0, rope=float("nan"))])
 def test_unsupported(ne, kw):
@@ -152,7 +153,8 @@ def test_backward_passes_validate(ne, which):
     assert dq_pass(ne, p) == ne.NE_ERR_ALIGN
     assert dkdv_pass(ne, p) == ne.NE_ERR_ALIGN
     assert dq_pass(ne, Hkv=3) == ne.NE_ERR_SHAPE
-    assert dkdv_pass(ne, D=128) == ne.NE_ERR_UNSUPPORTED
+    assert dkdv_pass(ne, D=256) == ne.NE_ERR_UNSUPPORTED
+    assert dkdv_pass(ne, D=128, dtype=1) == ne.NE_ERR_UNSUPPORTED  # bf16 tiles: D = 32, 64
 
 
 @pytest.mark.parametrize("which", range(10))
@@ -200,7 +202,10 @@ def test_decode_workspace_bytes(ne):
             up256(4 * S * B * Hq * D) + up256(4 * S * B * Hq))
     assert ne.ne_attn_decode_workspace_bytes(B, Hq, 4, Tc, D, 0) == 0     # Hq % Hkv
     assert ne.ne_attn_decode_workspace_bytes(B, Hq, Hkv, 0, D, 0) == 0    # empty cache
-    assert ne.ne_attn_decode_workspace_bytes(B, Hq, Hkv, Tc, 128, 0) == 0  # unsupported D
+    assert ne.ne_attn_decode_workspace_bytes(B, Hq, Hkv, Tc, 256, 0) == 0  # unsupported D
+    for dtype in (0, 1):  # head size 128 in both dtypes
+        assert ne.ne_attn_decode_workspace_bytes(B, Hq, Hkv, Tc, 128, dtype) == (
+            up256(4 * S * B * Hq * 128) + up256(4 * S * B * Hq))
 
 
 @pytest.mark.parametrize("which", range(7))
@@ -214,6 +219,7 @@ def test_decode_validates(ne, which):
     assert decode_call(ne, Tc=0) == ne.NE_ERR_SHAPE
     assert decode_call(ne, B=70000, Hq=1, Hkv=1) == ne.NE_ERR_SHAPE   # grid rows past 65535
     assert decode_call(ne, D=48) == ne.NE_ERR_UNSUPPORTED
+    assert decode_call(ne, D=256) == ne.NE_ERR_UNSUPPORTED
     assert decode_call(ne, dtype=3) == ne.NE_ERR_UNSUPPORTED
 
 
@@ -233,4 +239,5 @@ def test_prefill_validates(ne, which):
     assert prefill_call(ne, Tq=41) == ne.NE_ERR_SHAPE    # longer than the cache
     assert prefill_call(ne, Tq=0) == ne.NE_ERR_SHAPE
     assert prefill_call(ne, Hkv=3) == ne.NE_ERR_SHAPE
-    assert prefill_call(ne, D=128) == ne.NE_ERR_UNSUPPORTED
+    assert prefill_call(ne, D=256) == ne.NE_ERR_UNSUPPORTED
+    assert prefill_call(ne, D=128, dtype=1) == ne.NE_ERR_UNSUPPORTED  # bf16 tiles: D = 32, 64

@@ -59,6 +59,8 @@ CASES = [
     (1, 10, 1, 300, 64, [300]),               # group of 10: chunks of 8 and 2 heads
     (2, 3, 3, 64, 64, [64, 63]),              # no grouping
     (1, 24, 3, 4097, 64, [4097]),             # group of 8, ragged last split
+    (2, 8, 2, 600, 128, [600, 300]),          # head size 128 (fp32: 32 lanes per row)
+    (1, 16, 2, 1030, 128, [1030]),            # head size 128, group of 8
 ]
 
 

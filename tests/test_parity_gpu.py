@@ -43,6 +43,9 @@ RAGGED = [
     (1, 10, 2, 77, 64), (1, 6, 1, 100, 64), (1, 7, 1, 90, 32), (1, 8, 1, 200, 64),
     # 256 work-groups per tile index: the forward's mirrored tile order with a stride of one row
     (64, 4, 4, 128, 32),
+    # head size 128 (work-groups of at most 4 waves, one wave per SIMD)
+    (1, 4, 2, 64, 128), (1, 3, 1, 77, 128), (2, 12, 4, 130, 128), (1, 8, 1, 100, 128),
+    (1, 2, 2, 33, 128), (1, 16, 2, 257, 128),
 ]
 
 
@@ -60,7 +63,7 @@ def test_non_causal_workloads(ne, oracle_mod, name):
 
 ROPE_CASES = [
     (1, 4, 2, 64, 32, 10000.0), (2, 12, 4, 130, 64, 10000.0), (1, 6, 3, 517, 64, 10000.0),
-    (1, 16, 4, 1024, 64, 10000.0), (1, 4, 4, 33, 32, 500.0),
+    (1, 16, 4, 1024, 64, 10000.0), (1, 4, 4, 33, 32, 500.0), (1, 8, 2, 200, 128, 10000.0),
 ]
 
 
@@ -76,6 +79,13 @@ def test_fp32_fused_rope(ne, oracle_mod, case, causal):
     res = gpu_fwd_bwd(ne, x, causal=causal, rope_base=base)
     ref = oracle_fwd_bwd(oracle_mod, x, causal=causal, rope_base=base)
     assert_f32(res, ref, f"rope {case}")
+
+
+def test_head_size_128_workload(ne, oracle_mod):
+    """The head-size-128 workload at a reduced batch (the oracle's cost), same heads and
+    length."""
+    w = WORKLOADS["d128_f32"]
+    run_case(ne, oracle_mod, w.with_(B=1))
 
 
 def test_fp32_rope_long_positions(ne, oracle_mod):

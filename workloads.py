@@ -76,6 +76,8 @@ WORKLOADS = {
                          note="long context, tile streaming and causal skipping"),
     "bf16_rope": Workload("bf16_rope", 16, 16, 4, 1024, 64, dtype="bf16", rope_base=10000.0,
                           note="bf16 with RoPE applied in the kernel (dim 1024)"),
+    "d128_f32": Workload("d128_f32", 8, 16, 4, 1024, 128,
+                         note="head size 128 (dim 2048), a reading of the planned ~270M scale-up"),
 }
 
 
