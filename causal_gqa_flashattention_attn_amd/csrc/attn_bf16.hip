@@ -191,10 +191,11 @@ struct KVRingB {
     int wave, nw, lpw;  // wave-uniform
     int lrow;           // lane / NCH: the lane's row within a piece
     int chb;            // byte offset of the lane's 16 bytes within its row, even pieces
-    int off0, off1;     // the lane's offset within an even / odd piece
+    int off0, off1;     // the lane's offset within an even / odd piece (D <= 64)
     int offw;           // ... within piece number `wave`
-    static constexpr int PX = 16 * swizzle_piece_xor<D>();  // odd pieces: offset ^ PX
-    static_assert(PPT <= 4 || PPT % 4 == 0, "piece runs are at most four instruction offsets");
+    static constexpr int PX = 16 * swizzle_piece_xor<D>(1);  // D <= 64, odd pieces: offset ^ PX
+    static_assert(PPT <= 4 || PPT % 4 == 0, "piece runs are whole groups of four pieces");
+    static constexpr int MAXRUN = D == 128 ? 8 : 4;  // longest run of pieces per wave and tile
 
     __device__ __forceinline__ void init(int wave_, int nw_, int lane) {
         wave = wave_;
@@ -213,21 +214,28 @@ struct KVRingB {
         const unsigned bytes = (unsigned)T * C::RB;
         const buf_rsrc_t rk = raw_rsrc(kg, bytes), rv = raw_rsrc(vg, bytes);
         const uint32_t sa = opaque_lds_addr(stage);
-        if ((tile + 1) * C::BN <= T && PPT % nw == 0) {
+        if ((tile + 1) * C::BN <= T && PPT % nw == 0 && PPT / nw <= MAXRUN) {
             // No row past the end, and nw divides the pieces of a tensor tile: wave w copies
             // the ppw consecutive pieces w ppw .. of K and of V (the same count, lpw, as below).
             // Consecutive pieces are 1 KB apart in the tensor and in the stage alike: an
-            // instruction offset.  With ppw even, piece parity is that of j; with ppw = 1, of w.
+            // instruction offset (below 4 KB; groups of four pieces step the uniform offsets).
+            // D <= 64: with ppw even, piece parity is that of j; with ppw = 1, of w.  D = 128:
+            // ppw is 4 or 8, so piece p0 + j has p0 + j = j modulo 4.
             const int ppw = PPT / nw;
             const int p0 = wave * ppw;
             const unsigned soff = (unsigned)(tile * TB + p0 * 1024);
             const uint32_t dk = sa + p0 * 1024, dv = sa + TB + p0 * 1024;
-            static_for<(PPT < 4 ? PPT : 4)>([&](auto jc) {
+            static_for<(PPT < MAXRUN ? PPT : MAXRUN)>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 if (j < ppw) {
-                    const unsigned vo = (unsigned)(j == 0 ? (ppw == 1 ? offw : off0) : (j & 1) ? off1 : off0);
-                    dma16_buf_imm_at<j * 1024>(rk, vo, soff, dk);
-                    dma16_buf_imm_at<j * 1024>(rv, vo, soff, dv);
+                    unsigned vo;
+                    if constexpr (D == 128)
+                        vo = (unsigned)(off0 ^ (16 * swizzle_piece_xor<D>(j)));
+                    else
+                        vo = (unsigned)(j == 0 ? (ppw == 1 ? offw : off0) : (j & 1) ? off1 : off0);
+                    constexpr unsigned hi = (unsigned)(j / 4) * 4096u;
+                    dma16_buf_imm_at<(j % 4) * 1024>(rk, vo, soff + hi, dk + hi);
+                    dma16_buf_imm_at<(j % 4) * 1024>(rv, vo, soff + hi, dv + hi);
                 }
             });
             return;
@@ -241,7 +249,8 @@ struct KVRingB {
                 const bool isv = pc >= PPT;
                 const int q = isv ? pc - PPT : pc;
                 const int r = min(tile * C::BN + q * RPP + lrow, T - 1);
-                dma16_buf_at(isv ? rv : rk, (unsigned)((r * C::RB + chb) ^ ((q & 1) * PX)), 0u,
+                dma16_buf_at(isv ? rv : rk,
+                             (unsigned)((r * C::RB + chb) ^ (16 * swizzle_piece_xor<D>(q))), 0u,
                              sa + pc * 1024);
             }
     }
@@ -341,21 +350,17 @@ __device__ __forceinline__ void issue_tr(TrOperand<D> &op, const unsigned char *
 template <int D, int LATER>
 __device__ __forceinline__ void accum_tr(f32x16 (&acc)[CfgB<D>::ND], TrOperand<D> &op,
                                          const bf16x8 (&xb)[2]) {
-    if constexpr (CfgB<D>::ND == 2) {
-        lds_wait_n<LATER + 6>(op.lo[0][0], op.hi[0][0]);
-        acc[0] = mfma32_bf16(join8(op.lo[0][0], op.hi[0][0]), xb[0], acc[0]);
-        lds_wait_n<LATER + 4>(op.lo[0][1], op.hi[0][1]);
-        acc[1] = mfma32_bf16(join8(op.lo[0][1], op.hi[0][1]), xb[0], acc[1]);
-        lds_wait_n<LATER + 2>(op.lo[1][0], op.hi[1][0]);
-        acc[0] = mfma32_bf16(join8(op.lo[1][0], op.hi[1][0]), xb[1], acc[0]);
-        lds_wait_n<LATER>(op.lo[1][1], op.hi[1][1]);
-        acc[1] = mfma32_bf16(join8(op.lo[1][1], op.hi[1][1]), xb[1], acc[1]);
-    } else {
-        lds_wait_n<LATER + 2>(op.lo[0][0], op.hi[0][0]);
-        acc[0] = mfma32_bf16(join8(op.lo[0][0], op.hi[0][0]), xb[0], acc[0]);
-        lds_wait_n<LATER>(op.lo[1][0], op.hi[1][0]);
-        acc[0] = mfma32_bf16(join8(op.lo[1][0], op.hi[1][0]), xb[1], acc[0]);
-    }
+    // The reads were issued in the order (s2, dd), lo then hi: after the pair (s2, dd) came
+    // 2 (ND - 1 - dd) reads of the same s2, and 2 ND more when s2 = 0.
+    constexpr int ND = CfgB<D>::ND;
+    static_for<2>([&](auto s2c) {
+        constexpr int s2 = decltype(s2c)::value;
+        static_for<ND>([&](auto ddc) {
+            constexpr int dd = decltype(ddc)::value;
+            lds_wait_n<LATER + 2 * (ND - 1 - dd) + (s2 == 0 ? 2 * ND : 0)>(op.lo[s2][dd], op.hi[s2][dd]);
+            acc[dd] = mfma32_bf16(join8(op.lo[s2][dd], op.hi[s2][dd]), xb[s2], acc[dd]);
+        });
+    });
 }
 
 // acc (D x 32, transposed) += M_tile[r0 .. r0+31]^T x X, X given as its two bf16 operand halves.
@@ -528,7 +533,8 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
 // NWC: the waves per work-group when known at compile time (4: groups of four query heads),
 // else 0.
 template <int D, bool CAUSAL, bool ROPE, int NWC>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_FWD_WAVES_PER_EU)))
+__global__ void __launch_bounds__(D == 128 ? 256 : 512)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_BF16_FWD_WAVES_PER_EU)))
 fwd_bf16(ArgsB a) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -652,7 +658,8 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
 // NWC: the waves per work-group when known at compile time (4: groups of four query heads),
 // else 0.
 template <int D, bool CAUSAL, bool ROPE, int NWC>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NE_BF16_DQ_WAVES_PER_EU)))
+__global__ void __launch_bounds__(D == 128 ? 256 : 512)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_BF16_DQ_WAVES_PER_EU)))
 dq_bf16(ArgsB a) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -717,11 +724,11 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     const int per_head = nqb - i0;
     const int nitems = a.G * per_head;
 
-    // This lane's 16 bytes of a piece: row lrow of the piece, swizzled chunk (by piece parity).
-    constexpr int PX = 16 * swizzle_piece_xor<D>();
+    // This lane's 16 bytes of a piece: row lrow of the piece, swizzled chunk (piece pc: the
+    // offset XOR 16 swizzle_piece_xor(pc)).
     const int lrow = lane / C::NCH;
     const int chb = 16 * chunk_swizzle<D>(lrow, lane % C::NCH);
-    const int off0 = lrow * C::RB + chb, off1 = off0 ^ PX;
+    const int off0 = lrow * C::RB + chb;
     // Starts the copies of item `it` into `st`, through buffer resources on the head's q and dO.
     // Rows past the end read row T - 1; their lse is replaced by +inf once the item has landed,
     // so their probabilities are 0.
@@ -733,12 +740,15 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         const buf_rsrc_t ro = raw_rsrc(a.dO + bh * T * D, bytes);
         if (i * 32 + 32 <= T) {
             // Piece pc sits 1 KB further on in both the tensor and the stage: an instruction
-            // offset, so the destinations of a stage are two values.
+            // offset (below 4 KB; each group of four pieces steps the uniform offsets), so the
+            // destinations of a stage are two values per group.
             const unsigned soff = (unsigned)(i * 32 * C::RB);
             static_for<S::NPQ>([&](auto pcc) {
                 constexpr int pc = decltype(pcc)::value;
-                dma16_buf_imm<pc * 1024>(rq, (unsigned)((pc & 1) ? off1 : off0), soff, st);
-                dma16_buf_imm<pc * 1024>(ro, (unsigned)((pc & 1) ? off1 : off0), soff, st + S::TBQ);
+                constexpr int hi = (pc / 4) * 4096;
+                const unsigned vo = (unsigned)(off0 ^ (16 * swizzle_piece_xor<D>(pc)));
+                dma16_buf_imm<(pc % 4) * 1024>(rq, vo, soff + hi, st + hi);
+                dma16_buf_imm<(pc % 4) * 1024>(ro, vo, soff + hi, st + S::TBQ + hi);
             });
         } else {
             // Rare (the last item of a head with T % 32 != 0): the stage address is made opaque
@@ -749,7 +759,7 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
 #pragma unroll
             for (int pc = 0; pc < S::NPQ; ++pc) {
                 const int r = min(i * 32 + pc * S::RPP + lrow, T - 1);
-                const unsigned vo = (unsigned)((r * C::RB + chb) ^ ((pc & 1) * PX));
+                const unsigned vo = (unsigned)((r * C::RB + chb) ^ (16 * swizzle_piece_xor<D>(pc)));
                 dma16_buf_at(rq, vo, 0u, sto + pc * 1024);
                 dma16_buf_at(ro, vo, 0u, sto + S::TBQ + pc * 1024);
             }
@@ -870,7 +880,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
 }
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_BF16_DKDV_WAVES_PER_EU)))
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_BF16_DKDV_WAVES_PER_EU)))
 dkdv_bf16(ArgsB a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_b[];
     const int per = a.B * a.Hkv;
@@ -953,13 +964,21 @@ NE_PICK_B(dkdv_bf16, int D, )
 #undef NE_PICK_B
 
 // The query-tile kernel for this shape: four-wave groups get the variant with the count built in.
-template <const void *(*P64_4)(bool, bool), const void *(*P64)(bool, bool),
-          const void *(*P32_4)(bool, bool), const void *(*P32)(bool, bool)>
+template <template <int, int> class P>
 const void *pick_qtile(const Shape &s, int nwaves) {
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
-    if (s.D == 64) return nwaves == 4 ? P64_4(causal, rope) : P64(causal, rope);
-    return nwaves == 4 ? P32_4(causal, rope) : P32(causal, rope);
+    if (s.D == 128) return nwaves == 4 ? P<128, 4>::get(causal, rope) : P<128, 0>::get(causal, rope);
+    if (s.D == 64) return nwaves == 4 ? P<64, 4>::get(causal, rope) : P<64, 0>::get(causal, rope);
+    return nwaves == 4 ? P<32, 4>::get(causal, rope) : P<32, 0>::get(causal, rope);
 }
+template <int D, int NWC>
+struct PickFwd {
+    static const void *get(bool causal, bool rope) { return pick_fwd_bf16<D, NWC>(causal, rope); }
+};
+template <int D, int NWC>
+struct PickDq {
+    static const void *get(bool causal, bool rope) { return pick_dq_bf16<D, NWC>(causal, rope); }
+};
 
 hipError_t launch_b(const void *fn, long long blocks, int threads, size_t lds, hipStream_t st,
                     ArgsB &a) {
@@ -971,7 +990,7 @@ hipError_t launch_b(const void *fn, long long blocks, int threads, size_t lds, h
 
 hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const void *v, void *o,
                            float *lse, hipStream_t st) {
-    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;  // kernels for D = 32, 64
+    if (s.D != 32 && s.D != 64 && s.D != 128) return hipErrorInvalidValue;
     ArgsB a = make_args_b(s);
     a.q = static_cast<const __bf16 *>(q);
     a.k = static_cast<const __bf16 *>(k);
@@ -980,15 +999,14 @@ hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const v
     a.out_lse = lse;
     const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.fwd != 0);
     a.paired = g.paired;
-    const void *fn = pick_qtile<pick_fwd_bf16<64, 4>, pick_fwd_bf16<64, 0>, pick_fwd_bf16<32, 4>,
-                                pick_fwd_bf16<32, 0>>(s, g.nwaves);
+    const void *fn = pick_qtile<PickFwd>(s, g.nwaves);
     return launch_b(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
 }
 
 hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const void *v,
                           const void *o, const float *lse, const void *dO, void *dq, float *delta,
                           void *qrot, hipStream_t st) {
-    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;  // kernels for D = 32, 64
+    if (s.D != 32 && s.D != 64 && s.D != 128) return hipErrorInvalidValue;
     ArgsB a = make_args_b(s);
     a.q = static_cast<const __bf16 *>(q);
     a.k = static_cast<const __bf16 *>(k);
@@ -1001,15 +1019,14 @@ hipError_t launch_dq_bf16(const Shape &s, const void *q, const void *k, const vo
     a.qrot = static_cast<__bf16 *>(qrot);
     const QTileGeom g = qtile_geometry(s, s.causal && kPairBf16.dq != 0);
     a.paired = g.paired;
-    const void *fn = pick_qtile<pick_dq_bf16<64, 4>, pick_dq_bf16<64, 0>, pick_dq_bf16<32, 4>,
-                                pick_dq_bf16<32, 0>>(s, g.nwaves);
+    const void *fn = pick_qtile<PickDq>(s, g.nwaves);
     return launch_b(fn, g.nblocks, 64 * g.nwaves, 0, st, a);
 }
 
 hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const void *v,
                             const float *lse, const void *dO, const float *delta, void *dk,
                             void *dv, hipStream_t st) {
-    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;  // kernels for D = 32, 64
+    if (s.D != 32 && s.D != 64 && s.D != 128) return hipErrorInvalidValue;
     ArgsB a = make_args_b(s);
     a.q = static_cast<const __bf16 *>(q);
     a.k = static_cast<const __bf16 *>(k);
@@ -1022,14 +1039,19 @@ hipError_t launch_dkdv_bf16(const Shape &s, const void *q, const void *k, const 
     const KBlockGeom g = kblock_geometry(s, s.causal && kPairBf16.dkdv != 0);
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = s.rope_base > 0.f;
-    const size_t lds = (size_t)g.nwaves * (s.D == 64 ? dkdv_wave_bytes_b<64>() : dkdv_wave_bytes_b<32>());
-    const void *fn = s.D == 64 ? pick_dkdv_bf16<64>(causal, rope) : pick_dkdv_bf16<32>(causal, rope);
+    const int wb = s.D == 128  ? dkdv_wave_bytes_b<128>()
+                   : s.D == 64 ? dkdv_wave_bytes_b<64>()
+                               : dkdv_wave_bytes_b<32>();
+    const size_t lds = (size_t)g.nwaves * wb;
+    const void *fn = s.D == 128  ? pick_dkdv_bf16<128>(causal, rope)
+                     : s.D == 64 ? pick_dkdv_bf16<64>(causal, rope)
+                                 : pick_dkdv_bf16<32>(causal, rope);
     return launch_b(fn, g.nblocks, 64 * g.nwaves, lds, st, a);
 }
 
 hipError_t launch_rope_bf16(const Shape &s, const void *x, void *y, long long rows,
                             hipStream_t st) {
-    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;  // kernels for D = 32, 64
+    if (s.D != 32 && s.D != 64 && s.D != 128) return hipErrorInvalidValue;
     const __bf16 *xb = static_cast<const __bf16 *>(x);
     __bf16 *yb = static_cast<__bf16 *>(y);
     RopeTurns rt = rope_turns(s);
@@ -1039,7 +1061,9 @@ hipError_t launch_rope_bf16(const Shape &s, const void *x, void *y, long long ro
     const unsigned gx = (unsigned)((per_pos + 255) / 256);
     // About 8 (batch, head) rows per thread when that still leaves enough threads.
     const long long gy = std::max(1LL, std::min(nbh, std::max(nbh / 8, 2048LL / (long long)gx)));
-    const void *fn = s.D == 64 ? (const void *)rope_rows_bf16<64> : (const void *)rope_rows_bf16<32>;
+    const void *fn = s.D == 128  ? (const void *)rope_rows_bf16<128>
+                     : s.D == 64 ? (const void *)rope_rows_bf16<64>
+                                 : (const void *)rope_rows_bf16<32>;
     void *params[] = {&xb, &yb, &nbh, &T, &rt};
     return hipLaunchKernel(fn, dim3(gx, (unsigned)std::min(gy, 65535LL)), dim3(256), params, 0, st);
 }

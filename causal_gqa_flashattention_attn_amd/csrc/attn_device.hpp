@@ -78,35 +78,56 @@ __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 // The LDS serves 256 bytes (64 banks) per cycle and a 16-byte read 16 lanes per cycle, so a
 // pattern is conflict-free when the 16 lanes of each group hit 16 distinct 16-byte slots modulo
 // 256 bytes.  The permutations below make three patterns conflict-free (measured with the LDS
-// bank-conflict counter): 16-byte reads of one chunk from 16 consecutive rows, the transposed
-// read below (32 lanes: 4 consecutive rows x 64 contiguous bytes), and staging writes where 16
-// lanes fill two (D = 64) or four (D = 32) whole rows.
+// bank-conflict counter for D = 32, 64): 16-byte reads of one chunk from 16 consecutive rows,
+// the transposed read below (32 lanes: 4 consecutive rows x 64 contiguous bytes), and staging
+// writes where 16 lanes fill one (D = 128), two (D = 64) or four (D = 32) whole rows.
+//   D = 128 (256-byte rows): chunk c of row r is stored at c ^ (4 (r & 3) + ((r >> 2) & 3)):
+//          16 consecutive rows take 16 distinct values, and the 4 rows of a transposed read
+//          land in 4 distinct groups of 4 chunks.
 //   D = 64 (128-byte rows): chunk c of row r is stored at c ^ f(r),
 //          f(r) = 2 * (((r & 3) + ((r >> 2) & 3)) & 3) + ((r >> 3) & 1).
 //   D = 32 (64-byte rows):  chunk c of row r is stored at c ^ ((r >> 2) & 3).
+// Every permutation repeats every 16 rows.
 template <int D>
 __host__ __device__ __forceinline__ constexpr int chunk_swizzle(int row, int ch) {
-    if constexpr (D == 64) return ch ^ (2 * (((row & 3) + ((row >> 2) & 3)) & 3) + ((row >> 3) & 1));
+    if constexpr (D == 128) return ch ^ (4 * (row & 3) + ((row >> 2) & 3));
+    else if constexpr (D == 64) return ch ^ (2 * (((row & 3) + ((row >> 2) & 3)) & 3) + ((row >> 3) & 1));
     else return ch ^ ((row >> 2) & 3);
 }
 
 // Copies that fill a tile 1024 bytes at a time cover rows [p R, p R + R) with piece p, R = 1024 /
 // (2 D).  The chunk permutation of row p R + r is that of row r XOR'd with a constant that only
-// depends on the parity of p; swizzle_piece_xor gives it (D = 64: 5, D = 32: 0).
+// depends on p; swizzle_piece_xor gives it (D = 128: p & 3; D = 64: 5 for odd p; D = 32: 0).
 template <int D>
-constexpr int swizzle_piece_xor() { return D == 64 ? 5 : 0; }
+__host__ __device__ constexpr int swizzle_piece_xor(int p) {
+    return D == 128 ? (p & 3) : D == 64 ? 5 * (p & 1) : 0;
+}
 template <int D>
 constexpr bool swizzle_piece_xor_holds() {
     constexpr int R = 1024 / (2 * D);
-    for (int p = 0; p < 8; ++p)
+    for (int p = 0; p < 32; ++p)
         for (int r = 0; r < R; ++r)
             for (int c = 0; c < D / 8; ++c)
-                if (chunk_swizzle<D>(p * R + r, c) != (chunk_swizzle<D>(r, c) ^ ((p & 1) * swizzle_piece_xor<D>())))
+                if (chunk_swizzle<D>(p * R + r, c) != (chunk_swizzle<D>(r, c) ^ swizzle_piece_xor<D>(p)))
                     return false;
     return true;
 }
-static_assert(swizzle_piece_xor_holds<64>() && swizzle_piece_xor_holds<32>(),
-              "piece permutation depends on more than the piece's parity");
+// Each row's permutation is a bijection of its chunks.
+template <int D>
+constexpr bool swizzle_is_permutation() {
+    for (int r = 0; r < 16; ++r) {
+        unsigned seen = 0;
+        for (int c = 0; c < D / 8; ++c) seen |= 1u << chunk_swizzle<D>(r, c);
+        if (seen != (D / 8 == 32 ? 0xffffffffu : (1u << (D / 8)) - 1)) return false;
+    }
+    return true;
+}
+static_assert(swizzle_piece_xor_holds<128>() && swizzle_piece_xor_holds<64>() &&
+                  swizzle_piece_xor_holds<32>(),
+              "piece permutation depends on more than swizzle_piece_xor gives");
+static_assert(swizzle_is_permutation<128>() && swizzle_is_permutation<64>() &&
+                  swizzle_is_permutation<32>(),
+              "chunk swizzle is not a permutation");
 
 // Byte offset of element (row, col) in a swizzled tile; col must be a multiple of 4.
 template <int D>
@@ -171,10 +192,12 @@ __device__ __forceinline__ uint32_t tr4_lane_addr(const unsigned char *t, int k0
 
 // s_waitcnt lgkmcnt(N): waits until at most N of this wave's LDS operations are outstanding.
 // They complete in order, so a read followed by N or more later LDS operations of the wave
-// has landed.  a and b pass through the wait, so nothing that uses them moves above it.
+// has landed.  a and b pass through the wait, so nothing that uses them moves above it.  The
+// counter field holds at most 15; a larger N waits for 15, which still covers the read.
 template <int N>
 __device__ __forceinline__ void lds_wait_n(bf16x4 &a, bf16x4 &b) {
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+    static_assert(N >= 0, "negative wait count");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N < 15 ? N : 15));
 }
 
 __device__ __forceinline__ bf16x8 join8(const bf16x4 &lo, const bf16x4 &hi) {

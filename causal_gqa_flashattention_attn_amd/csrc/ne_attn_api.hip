@@ -13,16 +13,13 @@ namespace {
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
-// Checks shared by every entry point; fills `s` on success.  `decode`: the decode step, which
-// has kernels for every supported head size in both dtypes; the tiled bf16 kernels take D = 32
-// or 64 only.
+// Checks shared by every entry point; fills `s` on success.
 int check_shape(int B, int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
-                ne::Shape &s, bool decode = false) {
+                ne::Shape &s) {
     if (B < 1 || Hq < 1 || Hkv < 1 || T < 1) return NE_ERR_SHAPE;
     if (Hq % Hkv != 0) return NE_ERR_SHAPE;
     if (D != 32 && D != 64 && D != 128) return NE_ERR_UNSUPPORTED;
     if (dtype != NE_F32 && dtype != NE_BF16) return NE_ERR_UNSUPPORTED;
-    if (dtype == NE_BF16 && D == 128 && !decode) return NE_ERR_UNSUPPORTED;
     if (!(rope_base >= 0.f) || !isfinite(rope_base)) return NE_ERR_UNSUPPORTED;
     // Element counts and grid sizes must stay far from 64-bit and 31-bit limits.
     const double rows = (double)B * (double)Hq * (double)T;
@@ -192,7 +189,7 @@ DecLayout dec_layout(int B, int Hq, int Tc, int D) {
 }
 
 int decode_check(int B, int Hq, int Hkv, int Tc, int D, int dtype, ne::Shape &s) {
-    const int rc = check_shape(B, Hq, Hkv, Tc, D, 0, dtype, 0.f, s, true);
+    const int rc = check_shape(B, Hq, Hkv, Tc, D, 0, dtype, 0.f, s);
     if (rc != NE_OK) return rc;
     // Work-groups per split: (batch, key/value head, chunk of up to 8 query heads).
     const long long gy = (long long)B * Hkv * ((s.G + 7) / 8);
@@ -308,7 +305,7 @@ const char *ne_attn_strerror(int status) {
         case NE_OK: return "success";
         case NE_ERR_NULL: return "null pointer argument";
         case NE_ERR_SHAPE: return "invalid shape (B, Hq, Hkv, T must be >= 1, Hq a multiple of Hkv, sizes in range)";
-        case NE_ERR_UNSUPPORTED: return "unsupported configuration (D must be 32, 64 or 128 (bf16 forward and backward: 32 or 64), dtype NE_F32 or NE_BF16, rope_base finite and >= 0)";
+        case NE_ERR_UNSUPPORTED: return "unsupported configuration (D must be 32, 64 or 128, dtype NE_F32 or NE_BF16, rope_base finite and >= 0)";
         case NE_ERR_ALIGN: return "pointer not 16-byte aligned";
         case NE_ERR_HIP: return "HIP kernel launch failed";
         default: return "unknown status";

@@ -36,7 +36,7 @@
  * Errors.  Every entry point returns an ne_status.  Argument errors are detected before any
  * launch and nothing is enqueued: NE_ERR_NULL (a null pointer), NE_ERR_SHAPE (B, Hq, Hkv or T
  * below 1, Hq not a multiple of Hkv, sizes whose element count overflows), NE_ERR_UNSUPPORTED
- * (D not 32 or 64, unknown dtype, negative or non-finite rope_base), NE_ERR_ALIGN (a pointer
+ * (D not 32, 64 or 128, unknown dtype, negative or non-finite rope_base), NE_ERR_ALIGN (a pointer
  * not 16-byte aligned).  NE_ERR_HIP reports a failed kernel launch.  No C++ exception crosses
  * this interface.
  */

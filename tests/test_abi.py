@@ -117,7 +117,6 @@ def test_bad_shapes(ne, kw):
 
 
 @pytest.mark.parametrize("kw", [dict(D=16), dict(D=256), dict(D=48), dict(dtype=2),
-                                dict(dtype=1, D=128),
                                 dict(dtype=-1), dict(dtype=0, rope=-1.0),
                                 dict(dtype=0, rope=float("inf")), dict(dtype=0, rope=float("nan"))])
 def test_unsupported(ne, kw):
@@ -154,7 +153,6 @@ def test_backward_passes_validate(ne, which):
     assert dkdv_pass(ne, p) == ne.NE_ERR_ALIGN
     assert dq_pass(ne, Hkv=3) == ne.NE_ERR_SHAPE
     assert dkdv_pass(ne, D=256) == ne.NE_ERR_UNSUPPORTED
-    assert dkdv_pass(ne, D=128, dtype=1) == ne.NE_ERR_UNSUPPORTED  # bf16 tiles: D = 32, 64
 
 
 @pytest.mark.parametrize("which", range(10))
@@ -240,4 +238,3 @@ def test_prefill_validates(ne, which):
     assert prefill_call(ne, Tq=0) == ne.NE_ERR_SHAPE
     assert prefill_call(ne, Hkv=3) == ne.NE_ERR_SHAPE
     assert prefill_call(ne, D=256) == ne.NE_ERR_UNSUPPORTED
-    assert prefill_call(ne, D=128, dtype=1) == ne.NE_ERR_UNSUPPORTED  # bf16 tiles: D = 32, 64

@@ -35,16 +35,25 @@ BF16_CASES = [
     # group sizes 5..8: 5..8 waves share each staged K/V tile, some copying a piece twice
     (1, 10, 2, 77, 64), (1, 6, 1, 100, 64), (1, 7, 1, 90, 32), (1, 8, 1, 200, 64),
     (1, 7, 1, 130, 64),
+    # head size 128: 256-byte rows (their own swizzle), work-groups of at most 4 waves; groups
+    # of 4 (four pieces per wave and tile), 2 (eight), 3 (the general copy path) and 1
+    (1, 4, 1, 64, 128), (2, 8, 2, 130, 128), (1, 6, 3, 200, 128), (1, 3, 1, 150, 128),
+    (1, 2, 2, 77, 128), (1, 8, 1, 257, 128), (1, 4, 4, 1, 128),
 ]
 
 
 @pytest.mark.parametrize("rope", [0.0, 10000.0])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("shape", BF16_CASES)
+@pytest.mark.parametrize("shape", BF16_CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_T{}_D{}".format(*c))
 def test_bf16_shapes(ne, oracle_mod, shape, causal, rope):
     B, Hq, Hkv, T, D = shape
     run_bf16(ne, oracle_mod, Workload("bf16", B, Hq, Hkv, T, D, dtype="bf16"), seed=5,
              causal=causal, rope_base=rope)
+
+
+def test_bf16_head_size_128_workload(ne, oracle_mod):
+    """The head-size-128 bf16 + RoPE workload at a reduced batch (the oracle's cost)."""
+    run_bf16(ne, oracle_mod, WORKLOADS["d128_bf16_rope"].with_(B=1))
 
 
 def test_bf16_gpu_model_shape(ne, oracle_mod):

@@ -50,7 +50,7 @@ RAGGED = [
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("shape", RAGGED)
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda c: "B{}_Hq{}_Hkv{}_T{}_D{}".format(*c))
 def test_ragged_and_odd_shapes(ne, oracle_mod, shape, causal):
     B, Hq, Hkv, T, D = shape
     run_case(ne, oracle_mod, Workload("ragged", B, Hq, Hkv, T, D), seed=7, causal=causal)

@@ -78,6 +78,9 @@ WORKLOADS = {
                           note="bf16 with RoPE applied in the kernel (dim 1024)"),
     "d128_f32": Workload("d128_f32", 8, 16, 4, 1024, 128,
                          note="head size 128 (dim 2048), a reading of the planned ~270M scale-up"),
+    "d128_bf16_rope": Workload("d128_bf16_rope", 8, 16, 4, 1024, 128, dtype="bf16",
+                               rope_base=10000.0,
+                               note="head size 128 in bf16 with RoPE applied in the kernel"),
 }
 
 
