@@ -45,7 +45,10 @@ struct CfgB {
     static constexpr int ND = D / 32;   // 32-wide blocks of D
     static constexpr int NCH = D / 8;   // 16-byte chunks per row
     static constexpr int RB = 2 * D;    // bytes per tile row
-    static constexpr int BN = 64;       // keys per staged K/V tile (two 32-key sub-blocks)
+    // Keys per staged K/V tile: two 32-key sub-blocks, one at D = 128 (so that the three-stage
+    // ring, 48 KB, leaves room for two work-groups per compute unit).
+    static constexpr int BN = D == 128 ? 32 : 64;
+    static constexpr int NSB = BN / 32;  // 32-key sub-blocks per tile
 };
 
 struct ArgsB {
@@ -205,7 +208,14 @@ struct KVRingB {
         chb = 16 * chunk_swizzle<D>(lrow, lane % C::NCH);
         off0 = lrow * C::RB + chb;
         off1 = off0 ^ PX;
-        offw = (wave & 1) ? off1 : off0;
+        if constexpr (D == 128) {
+            // Run of ppw pieces from p0 = wave ppw: piece p0 + j permutes by (p0 & 3) ^ (j & 3)
+            // (ppw is 2, 4 or 8, so p0 & 3 is 0 or 2 and never carries into j).
+            const int ppw = PPT % nw_ == 0 ? PPT / nw_ : 1;
+            offw = off0 ^ (16 * swizzle_piece_xor<D>(wave * ppw));
+        } else {
+            offw = (wave & 1) ? off1 : off0;
+        }
     }
     // Starts the copies of tile `tile` into `stage`.  Addresses are offsets within the head
     // (kg, vg), split into a per-lane part and a wave-uniform part.
@@ -220,7 +230,7 @@ struct KVRingB {
             // Consecutive pieces are 1 KB apart in the tensor and in the stage alike: an
             // instruction offset (below 4 KB; groups of four pieces step the uniform offsets).
             // D <= 64: with ppw even, piece parity is that of j; with ppw = 1, of w.  D = 128:
-            // ppw is 4 or 8, so piece p0 + j has p0 + j = j modulo 4.
+            // the run's first piece sets offw (init).
             const int ppw = PPT / nw;
             const int p0 = wave * ppw;
             const unsigned soff = (unsigned)(tile * TB + p0 * 1024);
@@ -230,7 +240,7 @@ struct KVRingB {
                 if (j < ppw) {
                     unsigned vo;
                     if constexpr (D == 128)
-                        vo = (unsigned)(off0 ^ (16 * swizzle_piece_xor<D>(j)));
+                        vo = (unsigned)(offw ^ (16 * swizzle_piece_xor<D>(j)));
                     else
                         vo = (unsigned)(j == 0 ? (ppw == 1 ? offw : off0) : (j & 1) ? off1 : off0);
                     constexpr unsigned hi = (unsigned)(j / 4) * 4096u;
@@ -433,7 +443,7 @@ __device__ __forceinline__ void fwd_half(const ArgsB &a, FwdState<D> &st, const 
     block_accum_x<D>(st.acc, sV, rt, pb, lane);
 }
 
-// One 64-key tile of the forward: its two 32-key halves one after the other (a half entirely
+// One tile of the forward (BN keys): its 32-key halves one after the other (a half entirely
 // above the diagonal or past the end is skipped, and then so is the second).
 // (r0 is the position of the wave's first query row, T the number of keys.)
 template <int D, bool CAUSAL>
@@ -441,7 +451,7 @@ __device__ __forceinline__ void fwd_step(const ArgsB &a, FwdState<D> &st, const 
                                          const unsigned char *sV, int kt0, int r0, int T,
                                          const bf16x8 (&qv)[CfgB<D>::KS], int lane) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < CfgB<D>::NSB; ++sb) {
         const int kb0 = kt0 + 32 * sb;
         if (!(kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) return;
         fwd_half<D, CAUSAL>(a, st, sK, sV, 32 * sb, kb0, r0, T, qv, lane, 2 * sb);
@@ -534,7 +544,7 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
 // else 0.
 template <int D, bool CAUSAL, bool ROPE, int NWC>
 __global__ void __launch_bounds__(D == 128 ? 256 : 512)
-__attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_BF16_FWD_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : NE_BF16_FWD_WAVES_PER_EU)))
 fwd_bf16(ArgsB a) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -614,7 +624,7 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
         const unsigned char *sK = ring + ST * R::SB;
         const unsigned char *sV = sK + R::TB;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+        for (int sb = 0; sb < C::NSB; ++sb) {
             const int kb0 = j * C::BN + 32 * sb;
             if (!(live && kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) break;  // so is the next
             f32x16 p = block_scores<D>(sK, 32 * sb, qv, col, half);
@@ -659,7 +669,7 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
 // else 0.
 template <int D, bool CAUSAL, bool ROPE, int NWC>
 __global__ void __launch_bounds__(D == 128 ? 256 : 512)
-__attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_BF16_DQ_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : NE_BF16_DQ_WAVES_PER_EU)))
 dq_bf16(ArgsB a) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
