@@ -31,6 +31,11 @@
 #ifndef NE_BF16_DQ_WAVES_PER_EU
 #define NE_BF16_DQ_WAVES_PER_EU 3
 #endif
+// Keys per K/V tile at D = 64.  32 (a 24 KB ring, room for a fourth wave per SIMD in the
+// forward) measured no faster than 64 at T = 1024, and the dQ pass slower.
+#ifndef NE_BF16_BN_D64
+#define NE_BF16_BN_D64 64
+#endif
 #ifndef NE_BF16_DKDV_WAVES_PER_EU
 #define NE_BF16_DKDV_WAVES_PER_EU 2
 #endif
@@ -47,7 +52,7 @@ struct CfgB {
     static constexpr int RB = 2 * D;    // bytes per tile row
     // Keys per staged K/V tile: two 32-key sub-blocks, one at D = 128 (so that the three-stage
     // ring, 48 KB, leaves room for two work-groups per compute unit).
-    static constexpr int BN = D == 128 ? 32 : 64;
+    static constexpr int BN = D == 128 ? 32 : D == 64 ? NE_BF16_BN_D64 : 64;
     static constexpr int NSB = BN / 32;  // 32-key sub-blocks per tile
 };
 
@@ -292,20 +297,7 @@ __device__ __forceinline__ f32x16 block_scores(const unsigned char *tile, int r0
     return s;
 }
 
-// acc (D x 32, transposed) += M_tile[r0 .. r0+31]^T x X, X = the accumulator tile in registers.
-template <int D>
-__device__ __forceinline__ void block_accum(f32x16 (&acc)[CfgB<D>::ND], const unsigned char *tile,
-                                            int r0, const f32x16 &x, int lane) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 b = pack8(x, s2);
-#pragma unroll
-        for (int dd = 0; dd < CfgB<D>::ND; ++dd)
-            acc[dd] = mfma32_bf16(tile_read_tr8<D>(tile, r0 + 16 * s2, 32 * dd, lane), b, acc[dd]);
-    }
-}
-
-// A transposed operand M_tile[r0 .. r0+31]^T (D x 32) in flight: read with tile_read_tr4_asm for
+// A transposed operand M_tile[r0 .. r0+31]^T (D x 32) in flight: read with lds_read_tr4 for
 // tiles that LDS copies may be filling concurrently, so it can be requested well before use.
 template <int D>
 struct TrOperand {
@@ -327,7 +319,8 @@ struct TrAddr {
 };
 
 // Issues the reads of the operand M^T for the 32-row tile at byte offset OFF of the region, in
-// the order accum_tr's waits count on (as issue_tr).
+// the order accum_tr's waits count on: for s2 = 0 then 1, for each 32-column block dd, the
+// reads of rows 8 h .. (h = 0, 1) of the 16-row group s2.
 template <int D, int OFF>
 __device__ __forceinline__ void issue_tr_at(TrOperand<D> &op, const TrAddr<D> &ad) {
     constexpr int G16 = 16 * CfgB<D>::RB;  // bytes of 16 rows
@@ -341,18 +334,6 @@ __device__ __forceinline__ void issue_tr_at(TrOperand<D> &op, const TrAddr<D> &a
         op.lo[1][dd] = lds_read_tr4<OFF + G16>(ad.a[0][dd]);
         op.hi[1][dd] = lds_read_tr4<OFF + G16>(ad.a[1][dd]);
     }
-}
-
-template <int D>
-__device__ __forceinline__ void issue_tr(TrOperand<D> &op, const unsigned char *tile, int r0,
-                                         int lane) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int dd = 0; dd < CfgB<D>::ND; ++dd) {
-            op.lo[s2][dd] = tile_read_tr4_asm<D>(tile, r0 + 16 * s2, 32 * dd, lane);
-            op.hi[s2][dd] = tile_read_tr4_asm<D>(tile, r0 + 16 * s2 + 8, 32 * dd, lane);
-        }
 }
 
 // acc (D x 32, transposed) += op x X, X given as its two bf16 operand halves.  LATER: how many
@@ -373,17 +354,6 @@ __device__ __forceinline__ void accum_tr(f32x16 (&acc)[CfgB<D>::ND], TrOperand<D
     });
 }
 
-// acc (D x 32, transposed) += M_tile[r0 .. r0+31]^T x X, X given as its two bf16 operand halves.
-template <int D>
-__device__ __forceinline__ void block_accum_x(f32x16 (&acc)[CfgB<D>::ND], const unsigned char *tile,
-                                              int r0, const bf16x8 (&xb)[2], int lane) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int dd = 0; dd < CfgB<D>::ND; ++dd)
-            acc[dd] = mfma32_bf16(tile_read_tr8<D>(tile, r0 + 16 * s2, 32 * dd, lane), xb[s2], acc[dd]);
-}
-
 // Online-softmax state of a wave's 32 query rows in the forward: O^T accumulator, reference
 // maximum m (base 2, scaled) and four partial sums of the bf16 probabilities.
 template <int D>
@@ -398,13 +368,19 @@ struct FwdState {
 // halves are processed one after the other, each with its own online-softmax update, so only
 // one 32 x 32 score block is live: that keeps the kernel within the registers of two waves per
 // SIMD with room to spare, which measured faster than one wider update per 64 keys.
-template <int D, bool CAUSAL>
+// OFFV: byte offset of the half's V rows from the ring base, for which `tra` holds the lane
+// addresses.  The transposed V reads are issued as soon as the scores are requested, and in a
+// form the compiler does not track, so it neither waits for the copies of later tiles still in
+// flight into other stages before them nor delays them behind the exponentials.
+template <int D, bool CAUSAL, int OFFV>
 __device__ __forceinline__ void fwd_half(const ArgsB &a, FwdState<D> &st, const unsigned char *sK,
-                                         const unsigned char *sV, int rt, int kb0, int r0, int T,
+                                         const TrAddr<D> &tra, int rt, int kb0, int r0, int T,
                                          const bf16x8 (&qv)[CfgB<D>::KS], int lane, int li) {
     const int half = lane >> 5, col = lane & 31;
     const int qrow = r0 + col;
     f32x16 s = block_scores<D>(sK, rt, qv, col, half);
+    TrOperand<D> tv;
+    issue_tr_at<D, OFFV>(tv, tra);
     if ((CAUSAL && kb0 + 31 > r0) || kb0 + 32 > T) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -440,21 +416,23 @@ __device__ __forceinline__ void fwd_half(const ArgsB &a, FwdState<D> &st, const 
     const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
     st.l4[li] = sum8_bf16(pb[0], st.l4[li]);
     st.l4[li + 1] = sum8_bf16(pb[1], st.l4[li + 1]);
-    block_accum_x<D>(st.acc, sV, rt, pb, lane);
+    accum_tr<D, 0>(st.acc, tv, pb);  // O^T += V^T P^T
 }
 
 // One tile of the forward (BN keys): its 32-key halves one after the other (a half entirely
-// above the diagonal or past the end is skipped, and then so is the second).
+// above the diagonal or past the end is skipped, and then so is the second).  OFFV: byte offset
+// of the tile's V rows from the ring base.
 // (r0 is the position of the wave's first query row, T the number of keys.)
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int OFFV>
 __device__ __forceinline__ void fwd_step(const ArgsB &a, FwdState<D> &st, const unsigned char *sK,
-                                         const unsigned char *sV, int kt0, int r0, int T,
+                                         const TrAddr<D> &tra, int kt0, int r0, int T,
                                          const bf16x8 (&qv)[CfgB<D>::KS], int lane) {
-#pragma unroll
-    for (int sb = 0; sb < CfgB<D>::NSB; ++sb) {
-        const int kb0 = kt0 + 32 * sb;
+    if (!(kt0 < T && (!CAUSAL || kt0 <= r0 + 31))) return;
+    fwd_half<D, CAUSAL, OFFV>(a, st, sK, tra, 0, kt0, r0, T, qv, lane, 0);
+    if constexpr (CfgB<D>::NSB == 2) {
+        const int kb0 = kt0 + 32;
         if (!(kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) return;
-        fwd_half<D, CAUSAL>(a, st, sK, sV, 32 * sb, kb0, r0, T, qv, lane, 2 * sb);
+        fwd_half<D, CAUSAL, OFFV + 32 * CfgB<D>::RB>(a, st, sK, tra, 32, kb0, r0, T, qv, lane, 2);
     }
 }
 
@@ -497,6 +475,8 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
     st.mthr = kNegBig;
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.l4[i] = 0.f;
+    TrAddr<D> tra;  // lane addresses of transposed reads at the ring base; tiles are offsets
+    tra.init(ring, lane);
     // Everything requested so far has landed before the loop, so the compiler places no wait
     // for the row inside it.
     wait_vm_lgkm0(0);
@@ -511,7 +491,7 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
         wait_vm_lgkm0(min(R::PD - 1, ntiles - 1 - j) * kv.lpw);
         __builtin_amdgcn_s_barrier();
         const unsigned char *sK = ring + ST * R::SB;
-        if (live) fwd_step<D, CAUSAL>(a, st, sK, sK + R::TB, j * C::BN, r0 + qo, Tk, qv, lane);
+        if (live) fwd_step<D, CAUSAL, ST * R::SB + R::TB>(a, st, sK, tra, j * C::BN, r0 + qo, Tk, qv, lane);
         // Issued after this tile's reads: the compiler makes transposed LDS reads wait for every
         // copy in flight, and by the next tile's reads these have landed.
         if (j + R::PD < ntiles)
@@ -615,6 +595,8 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
     f32x16 acc[C::ND];
 #pragma unroll
     for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
+    TrAddr<D> tra;  // lane addresses of transposed reads at the ring base, as in the forward
+    tra.init(ring, lane);
     wait_vm_lgkm0(0);  // as in the forward
 
     auto iter = [&](int j, auto stage) {  // unrolled over the stages, as in the forward
@@ -623,12 +605,17 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
         __builtin_amdgcn_s_barrier();
         const unsigned char *sK = ring + ST * R::SB;
         const unsigned char *sV = sK + R::TB;
-#pragma unroll
-        for (int sb = 0; sb < C::NSB; ++sb) {
-            const int kb0 = j * C::BN + 32 * sb;
-            if (!(live && kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) break;  // so is the next
-            f32x16 p = block_scores<D>(sK, 32 * sb, qv, col, half);
-            f32x16 ds = block_scores<D>(sV, 32 * sb, dov, col, half);  // dP^T = V dO^T
+        // One 32-key half (SB) of the tile; false when it lies above the diagonal or past the
+        // end (and so does the next).  The transposed K reads for dQ are issued once both score
+        // products are requested, untracked by the compiler (as in the forward).
+        auto sub = [&](auto sbc) -> bool {
+            constexpr int SB = decltype(sbc)::value;
+            const int kb0 = j * C::BN + 32 * SB;
+            if (!(live && kb0 < T && (!CAUSAL || kb0 <= r0 + 31))) return false;
+            f32x16 p = block_scores<D>(sK, 32 * SB, qv, col, half);
+            f32x16 ds = block_scores<D>(sV, 32 * SB, dov, col, half);  // dP^T = V dO^T
+            TrOperand<D> tk;
+            issue_tr_at<D, ST * R::SB + 32 * SB * C::RB>(tk, tra);
 #pragma unroll
             for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(p[v], a.qscale, -lse2));
             if ((CAUSAL && kb0 + 31 > r0) || kb0 + 32 > T) {  // a block on the diagonal or the end
@@ -641,8 +628,11 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
 #pragma unroll
             for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
             const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
-            block_accum_x<D>(acc, sK, 32 * sb, db, lane);  // dQ^T += K^T dS^T
-        }
+            accum_tr<D, 0>(acc, tk, db);  // dQ^T += K^T dS^T
+            return true;
+        };
+        if (sub(std::integral_constant<int, 0>{}) && C::NSB == 2)
+            sub(std::integral_constant<int, C::NSB - 1>{});
         if (j + R::PD < ntiles)
             kv.issue(kg, vg, j + R::PD, T, ring + ((ST + R::PD) % R::NST) * R::SB);
     };

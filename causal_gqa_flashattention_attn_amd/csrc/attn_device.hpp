@@ -141,36 +141,13 @@ __device__ __forceinline__ bf16x8 tile_read8(const unsigned char *t, int row, in
     return *reinterpret_cast<const bf16x8 *>(t + tile_off<D>(row, col));
 }
 
-// Transposed read of a swizzled tile: lane l receives M[k0 + 4 * (l / 32) + j][c0 + l % 32] for
-// j = 0..3 (ds_read_b64_tr_b16: within each group of 16 lanes, lane i takes element i % 4 of the
-// 8-byte pieces addressed by lanes i / 4 + 4 j).
-template <int D>
-__device__ __forceinline__ bf16x4 tile_read_tr4(const unsigned char *t, int k0, int c0, int lane) {
-    const int row = k0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
-    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)(uintptr_t)(t + tile_off<D>(row, col)));
-}
-
-// The transposed read above, issued as inline assembly.  For tiles that LDS copies (dma16)
-// fill, the compiler makes the intrinsic wait for every copy in flight, since it cannot rule
-// out that they alias; it knows nothing of this form, so the caller must pass the result
-// through lds_wait_n before using it.
-template <int D>
-__device__ __forceinline__ bf16x4 tile_read_tr4_asm(const unsigned char *t, int k0, int c0,
-                                                    int lane) {
-    const int row = k0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
-    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    typedef __attribute__((address_space(3))) const unsigned char lds_u8;
-    const uint32_t addr = (uint32_t)(uintptr_t)(lds_u8 *)(t + tile_off<D>(row, col));
-    bf16x4 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
-    return r;
-}
-
-// The transposed read at LDS byte address addr + OFF (OFF < 65536, an immediate of the
-// instruction), for addresses precomputed by tr4_lane_addr; the same wait rules apply.
+// Transposed read (ds_read_b64_tr_b16) at LDS byte address addr + OFF (OFF < 65536, an
+// immediate of the instruction), for addresses precomputed by tr4_lane_addr: lane l receives
+// M[k0 + 4 * (l / 32) + j][c0 + l % 32] for j = 0..3 (within each group of 16 lanes, lane i
+// takes element i % 4 of the 8-byte pieces addressed by lanes i / 4 + 4 j).  It is issued as
+// inline assembly: for tiles that LDS copies (dma16) fill, the compiler would make the intrinsic
+// wait for every copy in flight, since it cannot rule out that they alias; it knows nothing of
+// this form, so the caller must pass the result through lds_wait_n before using it.
 template <int OFF>
 __device__ __forceinline__ bf16x4 lds_read_tr4(uint32_t addr) {
     static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset out of range");
@@ -201,15 +178,6 @@ __device__ __forceinline__ void lds_wait_n(bf16x4 &a, bf16x4 &b) {
 }
 
 __device__ __forceinline__ bf16x8 join8(const bf16x4 &lo, const bf16x4 &hi) {
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// 8 keys of the transposed operand: (k0 .. +3) from the first read, (k0 + 8 .. +11) from the
-// second, matching the rows held in accumulator registers 8 s .. 8 s + 7 of a lane half.
-template <int D>
-__device__ __forceinline__ bf16x8 tile_read_tr8(const unsigned char *t, int k0, int c0, int lane) {
-    const bf16x4 lo = tile_read_tr4<D>(t, k0, c0, lane);
-    const bf16x4 hi = tile_read_tr4<D>(t, k0 + 8, c0, lane);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
