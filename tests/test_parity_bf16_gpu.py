@@ -56,6 +56,12 @@ def test_bf16_head_size_128_workload(ne, oracle_mod):
     run_bf16(ne, oracle_mod, WORKLOADS["d128_bf16_rope"].with_(B=1))
 
 
+def test_bf16_long_sequence_head_size_128(ne, oracle_mod):
+    """T = 8192 at D = 128 with RoPE (positions up to 8191)."""
+    run_bf16(ne, oracle_mod, Workload("long_d128", 1, 2, 1, 8192, 128, dtype="bf16",
+                                      rope_base=10000.0), seed=3)
+
+
 def test_bf16_gpu_model_shape(ne, oracle_mod):
     """The GPU-model layer shape (boosted query rows) in bf16 without RoPE."""
     run_bf16(ne, oracle_mod, WORKLOADS["gpu_model"].with_(dtype="bf16"))

@@ -88,6 +88,11 @@ def test_head_size_128_workload(ne, oracle_mod):
     run_case(ne, oracle_mod, w.with_(B=1))
 
 
+def test_long_sequence_head_size_128(ne, oracle_mod):
+    """T = 8192 at D = 128: 256 key tiles streamed per query tile, causal skipping at length."""
+    run_case(ne, oracle_mod, Workload("long_d128", 1, 2, 1, 8192, 128), seed=3)
+
+
 def test_fp32_rope_long_positions(ne, oracle_mod):
     """Positions up to 4095: the angle must be reduced accurately at large t."""
     w = Workload("rope_long", 1, 4, 1, 4096, 64, rope_base=10000.0)

@@ -30,6 +30,7 @@ CASES = [
     (1, 8, 1, 77, 333, 32),
     (2, 16, 4, 200, 1000, 64),
     (1, 8, 2, 96, 400, 128),       # head size 128
+    (1, 8, 2, 64, 16384, 128),     # a 64-token chunk after 16,320 cached (head size 128)
 ]
 
 
