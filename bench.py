@@ -286,6 +286,8 @@ def main_prefill(a):
         if rc != ne.NE_OK:
             raise ne.NeAttnError(rc, "ne_attn_prefill")
 
+    if a.copy_mib > 0:
+        calibration_copies(torch, dev, a.copy_mib)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -322,7 +324,8 @@ def main_prefill(a):
         "roofline": {"bound": "mfma", "kernel": "forward with a query offset",
                      "achieved": round(fl / (ev_ms * 1e-3) / 1e12, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(fl / (ev_ms * 1e-3) / 1e12 / peak, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": fl},
+                     "traffic": measured_traffic("prefill", w.name),
+                     "algorithmic_flops_per_launch": fl},
         "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline_prefill(w, x, a.cpu_seconds),
     }
     print(json.dumps(line), flush=True)
