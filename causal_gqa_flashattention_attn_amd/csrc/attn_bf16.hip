@@ -240,18 +240,22 @@ struct KVRingB {
             const int p0 = wave * ppw;
             const unsigned soff = (unsigned)(tile * TB + p0 * 1024);
             const uint32_t dk = sa + p0 * 1024, dv = sa + TB + p0 * 1024;
-            static_for<(PPT < MAXRUN ? PPT : MAXRUN)>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                if (j < ppw) {
-                    unsigned vo;
-                    if constexpr (D == 128)
-                        vo = (unsigned)(offw ^ (16 * swizzle_piece_xor<D>(j)));
-                    else
-                        vo = (unsigned)(j == 0 ? (ppw == 1 ? offw : off0) : (j & 1) ? off1 : off0);
-                    constexpr unsigned hi = (unsigned)(j / 4) * 4096u;
-                    dma16_buf_imm_at<(j % 4) * 1024>(rk, vo, soff + hi, dk + hi);
-                    dma16_buf_imm_at<(j % 4) * 1024>(rv, vo, soff + hi, dv + hi);
-                }
+            // All K pieces, then all V pieces: a run shares one LDS base (the M0 register),
+            // and the scores need K first.
+            static_for<2>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                static_for<(PPT < MAXRUN ? PPT : MAXRUN)>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    if (j < ppw) {
+                        unsigned vo;
+                        if constexpr (D == 128)
+                            vo = (unsigned)(offw ^ (16 * swizzle_piece_xor<D>(j)));
+                        else
+                            vo = (unsigned)(j == 0 ? (ppw == 1 ? offw : off0) : (j & 1) ? off1 : off0);
+                        constexpr unsigned hi = (unsigned)(j / 4) * 4096u;
+                        dma16_buf_imm_at<(j % 4) * 1024>(t ? rv : rk, vo, soff + hi, (t ? dv : dk) + hi);
+                    }
+                });
             });
             return;
         }
@@ -733,7 +737,9 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     // Rows past the end read row T - 1; their lse is replaced by +inf once the item has landed,
     // so their probabilities are 0.
     auto issue = [&](int it, unsigned char *st) {
-        const int hh = it / per_head, i = i0 + it % per_head;
+        // (item indices and counts are non-negative: unsigned division needs no sign fix-ups)
+        const int hh = (int)((unsigned)it / (unsigned)per_head);
+        const int i = i0 + (int)((unsigned)it % (unsigned)per_head);
         const size_t bh = (size_t)b * a.Hq + (size_t)g * a.G + hh;
         const unsigned bytes = (unsigned)T * C::RB;
         const buf_rsrc_t rq = raw_rsrc(a.q + bh * T * D, bytes);
@@ -743,12 +749,15 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
             // offset (below 4 KB; each group of four pieces steps the uniform offsets), so the
             // destinations of a stage are two values per group.
             const unsigned soff = (unsigned)(i * 32 * C::RB);
-            static_for<S::NPQ>([&](auto pcc) {
-                constexpr int pc = decltype(pcc)::value;
-                constexpr int hi = (pc / 4) * 4096;
-                const unsigned vo = (unsigned)(off0 ^ (16 * swizzle_piece_xor<D>(pc)));
-                dma16_buf_imm<(pc % 4) * 1024>(rq, vo, soff + hi, st + hi);
-                dma16_buf_imm<(pc % 4) * 1024>(ro, vo, soff + hi, st + S::TBQ + hi);
+            // All Q pieces, then all dO pieces: a run shares one LDS base (the M0 register).
+            static_for<2>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                static_for<S::NPQ>([&](auto pcc) {
+                    constexpr int pc = decltype(pcc)::value;
+                    constexpr int hi = (pc / 4) * 4096;
+                    const unsigned vo = (unsigned)(off0 ^ (16 * swizzle_piece_xor<D>(pc)));
+                    dma16_buf_imm<(pc % 4) * 1024>(t ? ro : rq, vo, soff + hi, st + t * S::TBQ + hi);
+                });
             });
         } else {
             // Rare (the last item of a head with T % 32 != 0): the stage address is made opaque
@@ -782,7 +791,7 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     // One item in stage ST (compile-time, so that every LDS offset of the item is an immediate).
     auto item = [&](int it, auto stage) {
         constexpr int ST = decltype(stage)::value;
-        const int i = i0 + it % per_head;
+        const int i = i0 + (int)((unsigned)it % (unsigned)per_head);
         unsigned char *st = wbuf + ST * S::SB;
         const unsigned char *sQ = st;
         const unsigned char *sO = st + S::TBQ;
