@@ -87,7 +87,8 @@ def torch_reference(q, k, v, dO, causal):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("shape", [(2, 4, 2, 33, 16), (1, 12, 4, 70, 64), (1, 3, 3, 9, 8),
+@pytest.mark.parametrize("shape", [(2, 4, 2, 33, 16), (1, 12, 4, 70, 64), (1, 4, 2, 40, 128),
+                                   (1, 3, 3, 9, 8),
                                    (1, 8, 1, 17, 32)])
 def test_against_torch_sdpa_fp64(shape, causal):
     q, k, v, dO = qkv(*shape, seed=3)
