@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--copy-mib", type=int, default=0,
                    help="run three plain device-to-device copies of this many MiB before the "
                         "steps (reference dispatches of known size for HBM counter calibration)")
+    p.add_argument("--fused-bwd", action="store_true",
+                   help="time the single-pass backward (ne_attn_bwd_fused: dq by fp32 atomics) "
+                        "instead of the two passes")
     p.add_argument("--graph", action="store_true",
                    help="replay the step from a captured HIP graph instead of eager launches")
     return p.parse_args()
@@ -71,7 +74,7 @@ def kernel_flops(w):
     of the backward's five GEMMs (S, dP, dV, dK); the dQ pass holds dQ = dS K (its recomputed
     S and dP are not algorithmic work)."""
     f = w.flops_fwd()
-    return {"fwd": f, "bwd_dq": 0.5 * f, "bwd_dkdv": 2.0 * f}
+    return {"fwd": f, "bwd_dq": 0.5 * f, "bwd_dkdv": 2.0 * f, "bwd_fused": 2.5 * f}
 
 
 def kernel_bytes(w):
@@ -82,7 +85,8 @@ def kernel_bytes(w):
     nl = w.B * w.Hq * w.T
     return {"fwd": elt * (2 * nq + 2 * nk) + 4 * nl,                 # q,k,v -> o, lse
             "bwd_dq": elt * (4 * nq + 2 * nk) + 4 * 2 * nl,          # q,k,v,o,dO,lse -> dq, delta
-            "bwd_dkdv": elt * (2 * nq + 4 * nk) + 4 * 2 * nl}        # q,k,v,dO,lse,delta -> dk,dv
+            "bwd_dkdv": elt * (2 * nq + 4 * nk) + 4 * 2 * nl,        # q,k,v,dO,lse,delta -> dk,dv
+            "bwd_fused": elt * (4 * nq + 4 * nk) + 4 * nl}           # q,k,v,o,dO,lse -> dq,dk,dv
 
 
 def source_digest() -> str:
@@ -369,7 +373,10 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     c, rb = w.causal, w.rope_base
     ws = ne.workspace(q, k, rb)
-    names = ("fwd", "bwd_dq", "bwd_dkdv")
+    names = ("fwd", "bwd_fused") if a.fused_bwd else ("fwd", "bwd_dq", "bwd_dkdv")
+    if a.fused_bwd and (w.dtype != "f32" or rb > 0 or w.D not in (32, 64)):
+        print("--fused-bwd: float32, no RoPE, D 32 or 64 only", file=sys.stderr)
+        sys.exit(2)
 
     # Arguments are marshalled once: a step is three calls straight into the C entry points
     # (which validate their arguments themselves), so the host stays well ahead of the GPU.
@@ -380,6 +387,10 @@ def main():
         dims = (w.B, w.Hq, w.Hkv, w.T, w.D, int(c),
                 ne.NE_BF16 if w.dtype == "bf16" else ne.NE_F32, ctypes.c_float(rb),
                 ctypes.c_void_p(stream.cuda_stream))
+        if a.fused_bwd:
+            return ((L.ne_attn_fwd_ex, (P(q), P(k), P(v), P(o), P(lse), P(ws)) + dims),
+                    (L.ne_attn_bwd_fused, (P(q), P(k), P(v), P(o), P(lse), P(dO), P(dq), P(dk),
+                                           P(dv), P(ws)) + dims))
         return ((L.ne_attn_fwd_ex, (P(q), P(k), P(v), P(o), P(lse), P(ws)) + dims),
                 (L.ne_attn_bwd_dq_ex, (P(q), P(k), P(v), P(o), P(lse), P(dO), P(dq), P(ws)) + dims),
                 (L.ne_attn_bwd_dkdv_ex, (P(q), P(k), P(v), P(lse), P(dO), P(ws), P(dk), P(dv))
@@ -395,7 +406,7 @@ def main():
             if rc != ne.NE_OK:
                 raise ne.NeAttnError(rc, fn.__name__)
         if ev is not None:
-            ev[3].record()
+            ev[len(names)].record()
 
     if a.copy_mib > 0:
         calibration_copies(torch, dev, a.copy_mib)
@@ -415,7 +426,8 @@ def main():
         graph.replay() if graph is not None else step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(a.steps)]
     torch.cuda.synchronize()
     gc.disable()  # no collector pause while the host enqueues the timed steps
     t0 = time.perf_counter()
@@ -423,7 +435,7 @@ def main():
         if graph is not None:
             events[i][0].record()
             graph.replay()
-            events[i][3].record()
+            events[i][len(names)].record()
         else:
             step(events[i])
     torch.cuda.synchronize()
@@ -469,7 +481,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D,
                    "causal": w.causal, "rope_base": w.rope_base, "seed": a.seed,
-                   "launch": "hip_graph" if graph is not None else "eager"},
+                   "launch": "hip_graph" if graph is not None else "eager",
+                   "backward": "single-pass, dq by fp32 atomics" if a.fused_bwd
+                   else "two passes, atomics-free"},
         "pct_mfma_peak": round(100 * tflops / MFMA_PEAK[w.dtype], 2),
         "kernels": {n: {kk: round(vv, 4) for kk, vv in d.items()} for n, d in kern.items()},
         "roofline": roof,

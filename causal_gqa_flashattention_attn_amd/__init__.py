@@ -2,13 +2,13 @@
 
 The functions named like the C entry points (``ne_attn_fwd``, ``ne_attn_bwd``,
 ``ne_attn_fwd_ex``, ``ne_attn_bwd_ex``, ``ne_attn_bwd_dq_ex``, ``ne_attn_bwd_dkdv_ex``,
-``ne_attn_decode``, ``ne_attn_prefill``, ``ne_attn_workspace_bytes``, ``ne_attn_decode_workspace_bytes``,
+``ne_attn_bwd_fused``, ``ne_attn_decode``, ``ne_attn_prefill``, ``ne_attn_workspace_bytes``, ``ne_attn_decode_workspace_bytes``,
 ``ne_attn_bwd_workspace_bytes``, ``ne_attn_strerror``) only
 marshal arguments: they read sizes from tensor shapes, pass ``data_ptr()`` and the current
 HIP stream, and raise ``NeAttnError`` on a non-zero status.  All arithmetic happens in the HIP
 kernels.  PyTorch provides device memory and streams.
 
-``forward``, ``backward``, ``decode`` and ``prefill`` are conveniences that allocate the outputs and the
+``forward``, ``backward``, ``backward_fused``, ``decode`` and ``prefill`` are conveniences that allocate the outputs and the
 workspace with torch and call the entry points.
 
 Tensor layout: q, o, dO, dq: [B, Hq, T, D]; k, v, dk, dv: [B, Hkv, T, D]; lse: [B, Hq, T]
@@ -24,9 +24,10 @@ import os
 __all__ = [
     "NeAttnError", "library_path", "load", "lib",
     "ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_decode", "ne_attn_prefill",
-    "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes", "ne_attn_bwd_workspace_bytes",
-    "ne_attn_strerror", "forward", "backward", "decode", "prefill", "workspace",
+    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused", "ne_attn_decode",
+    "ne_attn_prefill", "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
+    "ne_attn_bwd_workspace_bytes", "ne_attn_strerror", "forward", "backward", "backward_fused",
+    "decode", "prefill", "workspace",
     "NE_OK", "NE_ERR_NULL", "NE_ERR_SHAPE", "NE_ERR_UNSUPPORTED", "NE_ERR_ALIGN", "NE_ERR_HIP",
     "NE_F32", "NE_BF16", "EXPORTED_SYMBOLS",
 ]
@@ -35,8 +36,8 @@ NE_OK, NE_ERR_NULL, NE_ERR_SHAPE, NE_ERR_UNSUPPORTED, NE_ERR_ALIGN, NE_ERR_HIP =
 NE_F32, NE_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-                    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_decode",
-                    "ne_attn_prefill", "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
+                    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused",
+                    "ne_attn_decode", "ne_attn_prefill", "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
                     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -74,8 +75,9 @@ def load():
     L.ne_attn_bwd_ex.argtypes = [vp] * 10 + [i] * 7 + [f, vp]
     L.ne_attn_bwd_dq_ex.argtypes = [vp] * 8 + [i] * 7 + [f, vp]
     L.ne_attn_bwd_dkdv_ex.argtypes = [vp] * 8 + [i] * 7 + [f, vp]
+    L.ne_attn_bwd_fused.argtypes = [vp] * 10 + [i] * 7 + [f, vp]
     for name in ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-                 "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex"):
+                 "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused"):
         getattr(L, name).restype = i
     L.ne_attn_workspace_bytes.argtypes = [i] * 6 + [f]
     L.ne_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -248,6 +250,18 @@ def ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal: bool = Tr
     _raise(rc, "ne_attn_bwd_ex")
 
 
+def ne_attn_bwd_fused(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal: bool = True,
+                      stream=None):
+    torch = _torch()
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, workspace, 0.0)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_bwd_fused(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
+                                      _p(dk), _p(dv), _p(workspace), B, Hq, Hkv, T, D,
+                                      int(bool(causal)), _dtype_code(q), 0.0,
+                                      _stream(stream, q.device))
+    _raise(rc, "ne_attn_bwd_fused")
+
+
 def ne_attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal: bool = True, stream=None):
     torch = _torch()
     if q.dtype != torch.float32:
@@ -366,6 +380,17 @@ def backward(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0, s
     dv = torch.empty_like(v)
     ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, rope_base), causal=causal,
                    rope_base=rope_base, stream=stream)
+    return dq, dk, dv
+
+
+def backward_fused(q, k, v, o, lse, dO, causal: bool = True, stream=None):
+    """Single-pass backward (float32, no RoPE, D 32 or 64); dq is not bitwise reproducible."""
+    torch = _torch()
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ne_attn_bwd_fused(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, 0.0), causal=causal,
+                      stream=stream)
     return dq, dk, dv
 
 

@@ -38,6 +38,9 @@
 #ifndef NE_DQ_WAVES_PER_EU
 #define NE_DQ_WAVES_PER_EU 2
 #endif
+#ifndef NE_DKDVQ_WAVES_PER_EU
+#define NE_DKDVQ_WAVES_PER_EU 2
+#endif
 #ifndef NE_DKDV_WAVES_PER_EU
 #define NE_DKDV_WAVES_PER_EU 2
 #endif
@@ -472,9 +475,23 @@ dq_f32(Args a) {
 template <int D>
 constexpr int dkdv_wave_floats() { return 2 * 32 * Cfg<D>::LD + 64; }
 
-template <int D, bool CAUSAL, bool ROPE>
+// Single-pass backward: each wave writes its transposed dS tile ([key][query], rows of kLDT
+// floats) over its dO tile, free once the item's dK product has read its last operand; the
+// work-group keeps the block's 32 key rows, unscaled, after the waves' areas.
+constexpr int kLDT = 36;
+static_assert(32 * kLDT <= 32 * Cfg<32>::LD, "the dS^T tile fits in a dO tile");
+template <int D>
+constexpr int dkdvq_lds_floats(int nw) { return nw * dkdv_wave_floats<D>() + 32 * Cfg<D>::LD; }
+
+// FUSED: the single-pass backward.  Besides dK and dV, every item adds its share of dQ,
+// dS K (32 queries x D), into dq with fp32 atomics (dq zeroed beforehand): dS goes through LDS
+// as [key][query] so that the product puts the head dimension on the lanes, and each atomic
+// instruction then touches two 128-byte lines.  The order of the additions into dq varies from
+// run to run, so dq is not bitwise reproducible (dk and dv still are).
+template <int D, bool CAUSAL, bool ROPE, bool FUSED = false>
 __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, float *smem) {
     using C = Cfg<D>;
+    constexpr int WF = dkdv_wave_floats<D>();
     const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -494,13 +511,24 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
         dv[dd] = zero16();
     }
 
-    float *sQ = smem + wave * dkdv_wave_floats<D>();
+    float *sQ = smem + wave * WF;
     float *sO = sQ + 32 * C::LD;  // dO tile
     float *sL = sO + 32 * C::LD;  // lse * log2(e) of the tile's rows
     float *sDl = sL + 32;         // delta of the tile's rows
     const int nqb = (T + 31) / 32;
     const int i0 = CAUSAL ? kb : 0;
     const int c4 = 4 * (lane % C::C4);
+    float *sT = sO;                          // FUSED: this wave's dS^T tile
+    float *sKt = smem + nw * WF;             // FUSED: the block's key rows
+    if constexpr (FUSED) {
+        for (int idx = threadIdx.x; idx < 32 * C::C4; idx += blockDim.x) {
+            const int r = idx / C::C4, cc = 4 * (idx % C::C4);
+            const int row = kb * 32 + r;
+            st4(sKt + r * C::LD + cc,
+                row < T ? ld4(a.k + (bg * T + row) * D + cc) : f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        __syncthreads();
+    }
 
     // The group's (query head, query block) items are dealt round-robin to the waves; each
     // wave stages its own query block and keeps private dK, dV partial sums.
@@ -572,12 +600,42 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
         }
         // dK^T += Q^T dS
         accum_t<D>(dk, sQ, ds, col, half);
+        if constexpr (FUSED) {
+            // dS^T into LDS: lane (key col) writes its 16 queries, four runs of four.
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                st4(sT + col * kLDT + 8 * u + 4 * half,
+                    f32x4{ds[4 * u], ds[4 * u + 1], ds[4 * u + 2], ds[4 * u + 3]});
+            // dQ (32 queries x D) = dS K: step st contracts keys 2 st + half; lane col takes
+            // query col of A and head column col (+ 32 dd) of B.
+            f32x16 aq[C::ND];
+#pragma unroll
+            for (int dd = 0; dd < C::ND; ++dd) aq[dd] = zero16();
+#pragma unroll
+            for (int st = 0; st < 16; ++st) {
+                const int key = 2 * st + half;
+                const float av = sT[key * kLDT + col];
+#pragma unroll
+                for (int dd = 0; dd < C::ND; ++dd)
+                    aq[dd] = mfma32(av, sKt[key * C::LD + dd * 32 + col], aq[dd]);
+            }
+            // Register v holds query acc_row(v, half), head column dd * 32 + col.
+            float *dqh = a.dq + bh * T * D;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int qrow = i * 32 + acc_row(v, half);
+                if (qrow < T)
+#pragma unroll
+                    for (int dd = 0; dd < C::ND; ++dd)
+                        unsafeAtomicAdd(dqh + (size_t)qrow * D + dd * 32 + col, aq[dd][v] * a.scale);
+            }
+        }
     }
 
     // Add the waves' partial dK, dV in LDS (wave order fixed) and write them out.
     __syncthreads();
     {
-        float *R = smem + wave * dkdv_wave_floats<D>();
+        float *R = smem + wave * WF;
 #pragma unroll
         for (int dd = 0; dd < C::ND; ++dd)
 #pragma unroll
@@ -596,7 +654,7 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
         const int r = (idx / C::C4) % 32;
         const int cc = 4 * (idx % C::C4);
         f32x4 sum{0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < nw; ++w) sum += ld4(smem + w * dkdv_wave_floats<D>() + t * 32 * C::LD + r * C::LD + cc);
+        for (int w = 0; w < nw; ++w) sum += ld4(smem + w * WF + t * 32 * C::LD + r * C::LD + cc);
         const int row = kb * 32 + r;
         if (row < T) {
             if (t == 0) {
@@ -622,6 +680,49 @@ dkdv_f32(Args a) {
     if (a.paired && a.nkb - 1 - p > p) {
         __syncthreads();
         dkdv_block<D, CAUSAL, ROPE>(a, b, g, a.nkb - 1 - p, smem);
+    }
+}
+
+// Single-pass backward (no RoPE; D = 32 or 64): as dkdv_f32, plus dQ by atomics.  One wave per
+// SIMD (the dQ product's accumulators come on top of dK, dV).
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_DKDVQ_WAVES_PER_EU)))
+dkdvq_f32(Args a) {
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int per = a.B * a.Hkv;
+    const int p = blockIdx.x / per;
+    const int g = (blockIdx.x % per) % a.Hkv;
+    const int b = (blockIdx.x % per) / a.Hkv;
+    dkdv_block<D, CAUSAL, false, true>(a, b, g, p, smem);
+    if (a.paired && a.nkb - 1 - p > p) {
+        __syncthreads();
+        dkdv_block<D, CAUSAL, false, true>(a, b, g, a.nkb - 1 - p, smem);
+    }
+}
+
+// delta_i = dO_i . o_i for every row, and dq zeroed, for the single-pass backward.  L = D / 4
+// lanes per row, each with 4 columns; the rows' partial sums are added over their L lanes.
+template <int D>
+__global__ void __launch_bounds__(256) delta_zero_f32(const float *o, const float *dO,
+                                                      float *delta, float *dq, long long rows) {
+    constexpr int L = D / 4;
+    const long long n = rows * L;
+    for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx - threadIdx.x < n;
+         idx += (long long)gridDim.x * 256) {
+        const bool in = idx < n;
+        const long long row = idx / L;
+        const int c = 4 * (int)(idx % L);
+        float x = 0.f;
+        if (in) {
+            const f32x4 u = ld4(o + row * D + c), w = ld4(dO + row * D + c);
+            x = (u[0] * w[0] + u[1] * w[1]) + (u[2] * w[2] + u[3] * w[3]);
+        }
+#pragma unroll
+        for (int m = 1; m < L; m <<= 1) x += __shfl_xor(x, m, 64);
+        if (in) {
+            if (c == 0) delta[row] = x;
+            st4(dq + row * D + c, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
     }
 }
 
@@ -801,6 +902,41 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
                      : s.D == 64 ? pick_dkdv_f32<64>(causal, rope)
                                  : pick_dkdv_f32<32>(causal, rope);
     return launch(fn, g.nblocks, 64 * g.nwaves, lds, st, a);
+}
+
+hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, const float *v,
+                                const float *o, const float *lse, const float *dO, float *dq,
+                                float *dk, float *dv, float *delta, hipStream_t st) {
+    // D = 128 would need 171.5 KB of LDS per work-group (160 KB per compute unit).
+    if (s.rope_base > 0.f || (s.D != 32 && s.D != 64)) return hipErrorInvalidValue;
+    const long long rows = (long long)s.B * s.Hq * s.T;
+    {
+        const long long thr = rows * (s.D / 4);
+        const unsigned grid = (unsigned)std::min<long long>((thr + 255) / 256, 1LL << 20);
+        const void *fn = s.D == 64 ? (const void *)delta_zero_f32<64> : (const void *)delta_zero_f32<32>;
+        long long r = rows;
+        void *params[] = {&o, &dO, &delta, &dq, &r};
+        const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), params, 0, st);
+        if (e != hipSuccess) return e;
+    }
+    Args a = make_args(s);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.lse = lse;
+    a.dO = dO;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = delta;
+    const KBlockGeom g = kblock_geometry(s, s.causal && kPairF32.dkdv != 0);
+    a.paired = g.paired;
+    a.nkb = g.nkb;
+    const bool causal = s.causal != 0;
+    const int lf = s.D == 64 ? dkdvq_lds_floats<64>(g.nwaves) : dkdvq_lds_floats<32>(g.nwaves);
+    const void *fn = s.D == 64 ? (causal ? (const void *)dkdvq_f32<64, true> : (const void *)dkdvq_f32<64, false>)
+                               : (causal ? (const void *)dkdvq_f32<32, true> : (const void *)dkdvq_f32<32, false>);
+    return launch(fn, g.nblocks, 64 * g.nwaves, (size_t)lf * sizeof(float), st, a);
 }
 
 hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long rows,

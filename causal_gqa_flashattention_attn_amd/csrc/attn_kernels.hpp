@@ -77,6 +77,12 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
                            const float *lse, const float *dO, const float *delta, float *dk,
                            float *dv, hipStream_t st);
 
+// Single-pass backward (float32, no RoPE): a pre-pass writes delta and zeroes dq, then one
+// key-block pass forms dk, dv and adds dq with fp32 atomics (dq not bitwise reproducible).
+hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, const float *v,
+                                const float *o, const float *lse, const float *dO, float *dq,
+                                float *dk, float *dv, float *delta, hipStream_t st);
+
 // bfloat16 variants: tensors are bf16 (passed untyped), lse and delta fp32.
 hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const void *v, void *o,
                            float *lse, hipStream_t st);

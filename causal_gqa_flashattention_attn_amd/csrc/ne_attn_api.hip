@@ -175,6 +175,23 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
                      stream);
 }
 
+int bwd_fused_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dO, void *dq, void *dk, void *dv, void *ws, int B, int Hq, int Hkv,
+                   int T, int D, int causal, int dtype, float rope_base, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !ws) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (dtype != NE_F32 || s.rope_base > 0.f || D == 128) return NE_ERR_UNSUPPORTED;
+    if (any_misaligned({q, k, v, o, lse, dO, dq, dk, dv, ws})) return NE_ERR_ALIGN;
+    const hipError_t e = ne::launch_bwd_fused_f32(
+        s, static_cast<const float *>(q), static_cast<const float *>(k),
+        static_cast<const float *>(v), static_cast<const float *>(o), lse,
+        static_cast<const float *>(dO), static_cast<float *>(dq), static_cast<float *>(dk),
+        static_cast<float *>(dv), static_cast<float *>(ws), stream);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
 // Decode workspace: the splits' outputs then their lse, each region 256-aligned.
 struct DecLayout {
     size_t part_lse, total;
@@ -244,6 +261,14 @@ int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float
                         hipStream_t stream) {
     return dkdv_impl(q, k, v, lse, dO, workspace, dk, dv, B, Hq, Hkv, T, D, causal, dtype,
                      rope_base, stream);
+}
+
+int ne_attn_bwd_fused(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dO, void *dq, void *dk, void *dv,
+                      void *workspace, int B, int Hq, int Hkv, int T, int D, int causal,
+                      int dtype, float rope_base, hipStream_t stream) {
+    return bwd_fused_impl(q, k, v, o, lse, dO, dq, dk, dv, workspace, B, Hq, Hkv, T, D, causal,
+                          dtype, rope_base, stream);
 }
 
 size_t ne_attn_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int dtype,

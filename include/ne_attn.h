@@ -131,6 +131,26 @@ int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float
                         hipStream_t stream);
 
 /*
+ * Single-pass backward, the alternative to the two passes of ne_attn_bwd_ex.  The pages give no
+ * backward algorithm ("NanoEuler: a GPT-2 hand-built in pure C/CUDA" (openai-hub),
+ * implementation details, and the README translations, section "Verified backward pass",
+ * only require that it be exact); this variant
+ * computes the same gradients without recomputing the scores and dP in a separate dq pass: the
+ * pass over key blocks also forms dS K for dq and adds it with float32 atomics.  A pre-pass
+ * writes delta to the workspace and zeroes dq.  Because the additions into dq happen in an
+ * order that varies from run to run, dq is not bitwise reproducible (dk and dv are); it agrees
+ * with ne_attn_bwd_ex to rounding.
+ *
+ * Arguments, layouts, ownership and errors as for ne_attn_bwd_ex, with these limits:
+ * dtype NE_F32 only, rope_base 0, D 32 or 64 (anything else: NE_ERR_UNSUPPORTED).  The
+ * workspace holds delta only: ne_attn_workspace_bytes(B, Hq, Hkv, T, D, NE_F32, 0) bytes.
+ */
+int ne_attn_bwd_fused(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dO, void *dq, void *dk, void *dv,
+                      void *workspace, int B, int Hq, int Hkv, int T, int D, int causal,
+                      int dtype, float rope_base, hipStream_t stream);
+
+/*
  * Bytes of the workspace of the _ex entry points: the delta region (4 * B * Hq * T) and, when
  * rope_base > 0, room for rotated copies of q and k in the given dtype, each region rounded up
  * to 256 bytes.  0 if the arguments are invalid (the checks of the entry points).

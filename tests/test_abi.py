@@ -238,3 +238,29 @@ def test_prefill_validates(ne, which):
     assert prefill_call(ne, Tq=0) == ne.NE_ERR_SHAPE
     assert prefill_call(ne, Hkv=3) == ne.NE_ERR_SHAPE
     assert prefill_call(ne, D=256) == ne.NE_ERR_UNSUPPORTED
+
+
+def fused(ne, ptrs=None, **kw):
+    L = ne.load()
+    p = ptrs or [A] * 10
+    a = dict(B=1, Hq=4, Hkv=2, T=64, D=32, causal=1, dtype=0, rope=0.0)
+    a.update(kw)
+    return L.ne_attn_bwd_fused(*[VP(x) for x in p], a["B"], a["Hq"], a["Hkv"], a["T"], a["D"],
+                               a["causal"], a["dtype"], a["rope"], VP(0))
+
+
+@pytest.mark.parametrize("which", range(10))
+def test_fused_backward_validates(ne, which):
+    p = [A] * 10
+    p[which] = 0
+    assert fused(ne, p) == ne.NE_ERR_NULL
+    p[which] = A + 4
+    assert fused(ne, p) == ne.NE_ERR_ALIGN
+    assert fused(ne, Hkv=3) == ne.NE_ERR_SHAPE
+    assert fused(ne, T=0) == ne.NE_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=1), dict(rope=10000.0), dict(D=128), dict(D=48)])
+def test_fused_backward_limits(ne, kw):
+    """float32 only, no RoPE, D 32 or 64."""
+    assert fused(ne, **kw) == ne.NE_ERR_UNSUPPORTED
