@@ -251,13 +251,13 @@ def ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal: bool = Tr
 
 
 def ne_attn_bwd_fused(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal: bool = True,
-                      stream=None):
+                      rope_base: float = 0.0, stream=None):
     torch = _torch()
-    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, workspace, 0.0)
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, workspace, rope_base)
     with torch.cuda.device(q.device):
         rc = load().ne_attn_bwd_fused(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
                                       _p(dk), _p(dv), _p(workspace), B, Hq, Hkv, T, D,
-                                      int(bool(causal)), _dtype_code(q), 0.0,
+                                      int(bool(causal)), _dtype_code(q), float(rope_base),
                                       _stream(stream, q.device))
     _raise(rc, "ne_attn_bwd_fused")
 
@@ -383,14 +383,15 @@ def backward(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0, s
     return dq, dk, dv
 
 
-def backward_fused(q, k, v, o, lse, dO, causal: bool = True, stream=None):
-    """Single-pass backward (float32, no RoPE, D 32 or 64); dq is not bitwise reproducible."""
+def backward_fused(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0,
+                   stream=None):
+    """Single-pass backward (float32, D 32 or 64); dq is not bitwise reproducible."""
     torch = _torch()
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    ne_attn_bwd_fused(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, 0.0), causal=causal,
-                      stream=stream)
+    ne_attn_bwd_fused(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, rope_base),
+                      causal=causal, rope_base=rope_base, stream=stream)
     return dq, dk, dv
 
 

@@ -683,9 +683,9 @@ dkdv_f32(Args a) {
     }
 }
 
-// Single-pass backward (no RoPE; D = 32 or 64): as dkdv_f32, plus dQ by atomics.  One wave per
-// SIMD (the dQ product's accumulators come on top of dK, dV).
-template <int D, bool CAUSAL>
+// Single-pass backward (D = 32 or 64): as dkdv_f32, plus dQ by atomics.  With RoPE, q and k
+// arrive rotated and dq is accumulated in the rotated frame (rotated back afterwards).
+template <int D, bool CAUSAL, bool ROPE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_DKDVQ_WAVES_PER_EU)))
 dkdvq_f32(Args a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -693,10 +693,10 @@ dkdvq_f32(Args a) {
     const int p = blockIdx.x / per;
     const int g = (blockIdx.x % per) % a.Hkv;
     const int b = (blockIdx.x % per) / a.Hkv;
-    dkdv_block<D, CAUSAL, false, true>(a, b, g, p, smem);
+    dkdv_block<D, CAUSAL, ROPE, true>(a, b, g, p, smem);
     if (a.paired && a.nkb - 1 - p > p) {
         __syncthreads();
-        dkdv_block<D, CAUSAL, false, true>(a, b, g, a.nkb - 1 - p, smem);
+        dkdv_block<D, CAUSAL, ROPE, true>(a, b, g, a.nkb - 1 - p, smem);
     }
 }
 
@@ -731,7 +731,8 @@ __global__ void __launch_bounds__(256) delta_zero_f32(const float *o, const floa
 // it evaluates the two sines and cosines once and applies them to the rows of every (batch,
 // head) it visits.  The attention kernels that stream a tensor through LDS many times read this
 // rotated copy instead of rotating every staged tile again.
-template <int D>
+// INV: the transpose R^T (a gradient rotated back), in place when x == y.
+template <int D, bool INV>
 __global__ void __launch_bounds__(256) rope_rows_f32(const float *x, float *y, long long nbh, int T,
                                                      RopeTurns rt) {
     const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -747,8 +748,12 @@ __global__ void __launch_bounds__(256) rope_rows_f32(const float *x, float *y, l
     for (long long bh = blockIdx.y; bh < nbh; bh += gridDim.y) {
         const size_t off = ((size_t)bh * T + t) * D + c;
         const f32x4 v = ld4(x + off);
-        st4(y + off, f32x4{v[0] * cs[0] - v[1] * sn[0], v[0] * sn[0] + v[1] * cs[0],
-                           v[2] * cs[1] - v[3] * sn[1], v[2] * sn[1] + v[3] * cs[1]});
+        if (INV)
+            st4(y + off, f32x4{v[0] * cs[0] + v[1] * sn[0], v[1] * cs[0] - v[0] * sn[0],
+                               v[2] * cs[1] + v[3] * sn[1], v[3] * cs[1] - v[2] * sn[1]});
+        else
+            st4(y + off, f32x4{v[0] * cs[0] - v[1] * sn[0], v[0] * sn[0] + v[1] * cs[0],
+                               v[2] * cs[1] - v[3] * sn[1], v[2] * sn[1] + v[3] * cs[1]});
     }
 }
 
@@ -906,10 +911,20 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
 
 hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, const float *v,
                                 const float *o, const float *lse, const float *dO, float *dq,
-                                float *dk, float *dv, float *delta, hipStream_t st) {
+                                float *dk, float *dv, float *delta, float *qrot, float *krot,
+                                hipStream_t st) {
     // D = 128 would need 171.5 KB of LDS per work-group (160 KB per compute unit).
-    if (s.rope_base > 0.f || (s.D != 32 && s.D != 64)) return hipErrorInvalidValue;
+    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;
+    const bool rope = s.rope_base > 0.f;
     const long long rows = (long long)s.B * s.Hq * s.T;
+    if (rope) {  // q and k rotated once into the workspace
+        if (!qrot || !krot) return hipErrorInvalidValue;
+        hipError_t e = launch_rope_f32(s, q, qrot, rows, st, false);
+        if (e == hipSuccess) e = launch_rope_f32(s, k, krot, (long long)s.B * s.Hkv * s.T, st, false);
+        if (e != hipSuccess) return e;
+        q = qrot;
+        k = krot;
+    }
     {
         const long long thr = rows * (s.D / 4);
         const unsigned grid = (unsigned)std::min<long long>((thr + 255) / 256, 1LL << 20);
@@ -934,22 +949,30 @@ hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, 
     a.nkb = g.nkb;
     const bool causal = s.causal != 0;
     const int lf = s.D == 64 ? dkdvq_lds_floats<64>(g.nwaves) : dkdvq_lds_floats<32>(g.nwaves);
-    const void *fn = s.D == 64 ? (causal ? (const void *)dkdvq_f32<64, true> : (const void *)dkdvq_f32<64, false>)
-                               : (causal ? (const void *)dkdvq_f32<32, true> : (const void *)dkdvq_f32<32, false>);
-    return launch(fn, g.nblocks, 64 * g.nwaves, (size_t)lf * sizeof(float), st, a);
+    const void *k64[2][2] = {{(const void *)dkdvq_f32<64, false, false>, (const void *)dkdvq_f32<64, false, true>},
+                             {(const void *)dkdvq_f32<64, true, false>, (const void *)dkdvq_f32<64, true, true>}};
+    const void *k32[2][2] = {{(const void *)dkdvq_f32<32, false, false>, (const void *)dkdvq_f32<32, false, true>},
+                             {(const void *)dkdvq_f32<32, true, false>, (const void *)dkdvq_f32<32, true, true>}};
+    const void *fn = (s.D == 64 ? k64 : k32)[causal][rope];
+    hipError_t e = launch(fn, g.nblocks, 64 * g.nwaves, (size_t)lf * sizeof(float), st, a);
+    if (e == hipSuccess && rope) e = launch_rope_f32(s, dq, dq, rows, st, true);  // dq = R^T dq'
+    return e;
 }
 
 hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long rows,
-                           hipStream_t st) {
+                           hipStream_t st, bool inv) {
     RopeTurns rt = rope_turns(s);
     long long nbh = rows / s.T;
     int T = s.T;
     const long long per_pos = (long long)T * (s.D / 4);
     const unsigned gx = (unsigned)((per_pos + 255) / 256);
     const long long gy = std::max(1LL, std::min(nbh, std::max(nbh / 8, 2048LL / (long long)gx)));
-    const void *fn = s.D == 128  ? (const void *)rope_rows_f32<128>
-                     : s.D == 64 ? (const void *)rope_rows_f32<64>
-                                 : (const void *)rope_rows_f32<32>;
+    const void *fn = inv ? (s.D == 128  ? (const void *)rope_rows_f32<128, true>
+                            : s.D == 64 ? (const void *)rope_rows_f32<64, true>
+                                        : (const void *)rope_rows_f32<32, true>)
+                         : (s.D == 128  ? (const void *)rope_rows_f32<128, false>
+                            : s.D == 64 ? (const void *)rope_rows_f32<64, false>
+                                        : (const void *)rope_rows_f32<32, false>);
     void *params[] = {&x, &y, &nbh, &T, &rt};
     return hipLaunchKernel(fn, dim3(gx, (unsigned)std::min(gy, 65535LL)), dim3(256), params, 0, st);
 }

@@ -77,11 +77,14 @@ hipError_t launch_dkdv_f32(const Shape &s, const float *q, const float *k, const
                            const float *lse, const float *dO, const float *delta, float *dk,
                            float *dv, hipStream_t st);
 
-// Single-pass backward (float32, no RoPE): a pre-pass writes delta and zeroes dq, then one
-// key-block pass forms dk, dv and adds dq with fp32 atomics (dq not bitwise reproducible).
+// Single-pass backward (float32): a pre-pass writes delta and zeroes dq, then one key-block
+// pass forms dk, dv and adds dq with fp32 atomics (dq not bitwise reproducible).  With RoPE,
+// q and k are first rotated into qrot, krot ([B][Hq][T][D], [B][Hkv][T][D]) and dq is rotated
+// back at the end.
 hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, const float *v,
                                 const float *o, const float *lse, const float *dO, float *dq,
-                                float *dk, float *dv, float *delta, hipStream_t st);
+                                float *dk, float *dv, float *delta, float *qrot, float *krot,
+                                hipStream_t st);
 
 // bfloat16 variants: tensors are bf16 (passed untyped), lse and delta fp32.
 hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const void *v, void *o,
@@ -108,7 +111,7 @@ inline RopeTurns rope_turns(const Shape &s) {
 
 // RoPE applied to a whole tensor [rows / T][T][D] (s.rope_base > 0), x -> y.
 hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long rows,
-                           hipStream_t st);
+                           hipStream_t st, bool inv = false);
 hipError_t launch_rope_bf16(const Shape &s, const void *x, void *y, long long rows,
                             hipStream_t st);
 

@@ -182,13 +182,18 @@ int bwd_fused_impl(const void *q, const void *k, const void *v, const void *o, c
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
-    if (dtype != NE_F32 || s.rope_base > 0.f || D == 128) return NE_ERR_UNSUPPORTED;
+    if (dtype != NE_F32 || D == 128) return NE_ERR_UNSUPPORTED;
     if (any_misaligned({q, k, v, o, lse, dO, dq, dk, dv, ws})) return NE_ERR_ALIGN;
+    const WsLayout L = ws_layout(s, dtype);  // delta; with RoPE the rotated k and q
+    char *w = static_cast<char *>(ws);
+    const bool rope = s.rope_base > 0.f;
     const hipError_t e = ne::launch_bwd_fused_f32(
         s, static_cast<const float *>(q), static_cast<const float *>(k),
         static_cast<const float *>(v), static_cast<const float *>(o), lse,
         static_cast<const float *>(dO), static_cast<float *>(dq), static_cast<float *>(dk),
-        static_cast<float *>(dv), static_cast<float *>(ws), stream);
+        static_cast<float *>(dv), reinterpret_cast<float *>(w + L.delta),
+        rope ? reinterpret_cast<float *>(w + L.qr) : nullptr,
+        rope ? reinterpret_cast<float *>(w + L.kr) : nullptr, stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 

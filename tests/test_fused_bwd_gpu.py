@@ -1,4 +1,5 @@
-"""Single-pass backward (ne_attn_bwd_fused: dq added with fp32 atomics) against the fp64 oracle.
+"""Single-pass backward (ne_attn_bwd_fused: dq added with fp32 atomics) against the fp64 oracle,
+with and without RoPE.
 
 Same bar as the two-pass backward: normwise relative error max |g - g_ref| / max |g_ref| <= 1e-4
 on dq, dk, dv.  dk and dv are bitwise reproducible; dq is not (atomic order) and is compared
@@ -16,13 +17,14 @@ pytestmark = pytest.mark.gpu
 def run_fused(ne, oracle_mod, w, seed=0, causal=True):
     import torch
     x = make_inputs(w, seed)
+    rb = w.rope_base
     print(f"\n[case] fused bwd {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} T{w.T} D{w.D} "
-          f"causal={causal} seed={seed}", flush=True)
+          f"causal={causal} rope={rb} seed={seed}", flush=True)
     q, k, v, dO = (torch.from_numpy(x[n]).cuda() for n in ("q", "k", "v", "dO"))
-    o, lse = ne.forward(q, k, v, causal=causal)
-    dq, dk, dv = ne.backward_fused(q, k, v, o, lse, dO, causal=causal)
+    o, lse = ne.forward(q, k, v, causal=causal, rope_base=rb)
+    dq, dk, dv = ne.backward_fused(q, k, v, o, lse, dO, causal=causal, rope_base=rb)
     torch.cuda.synchronize()
-    ref = oracle_fwd_bwd(oracle_mod, x, causal=causal)
+    ref = oracle_fwd_bwd(oracle_mod, x, causal=causal, rope_base=rb)
     got = {"dq": dq, "dk": dk, "dv": dv}
     for n in ("dq", "dk", "dv"):
         e = normwise(got[n].cpu().double().numpy(), ref[n])
@@ -48,6 +50,18 @@ SHAPES = [
 def test_fused_shapes(ne, oracle_mod, shape, causal):
     B, Hq, Hkv, T, D = shape
     run_fused(ne, oracle_mod, Workload("fused", B, Hq, Hkv, T, D), seed=7, causal=causal)
+
+
+ROPE_SHAPES = [(1, 4, 2, 64, 32), (2, 12, 4, 130, 64), (1, 6, 3, 517, 64), (1, 8, 1, 1024, 64)]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", ROPE_SHAPES, ids=lambda c: "B{}_Hq{}_Hkv{}_T{}_D{}".format(*c))
+def test_fused_rope(ne, oracle_mod, shape, causal):
+    """RoPE (base 10000): dq summed in the rotated frame, then rotated back."""
+    B, Hq, Hkv, T, D = shape
+    run_fused(ne, oracle_mod, Workload("fused_rope", B, Hq, Hkv, T, D, rope_base=10000.0),
+              seed=11, causal=causal)
 
 
 def test_fused_matches_two_pass_and_dkdv_is_reproducible(ne, oracle_mod):
