@@ -385,7 +385,7 @@ def backward(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0, s
 
 def backward_fused(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0,
                    stream=None):
-    """Single-pass backward (float32, D 32 or 64); dq is not bitwise reproducible."""
+    """Single-pass backward (float32); dq is not bitwise reproducible."""
     torch = _torch()
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)

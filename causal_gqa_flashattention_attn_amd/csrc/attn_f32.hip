@@ -480,6 +480,8 @@ constexpr int dkdv_wave_floats() { return 2 * 32 * Cfg<D>::LD + 64; }
 // work-group keeps the block's 32 key rows, unscaled, after the waves' areas.
 constexpr int kLDT = 36;
 static_assert(32 * kLDT <= 32 * Cfg<32>::LD, "the dS^T tile fits in a dO tile");
+static_assert(4 * 4 * (2 * 32 * Cfg<128>::LD + 64) + 4 * 32 * Cfg<128>::LD <= 160 * 1024,
+              "four D = 128 waves and the key rows fit in 160 KB of LDS");
 template <int D>
 constexpr int dkdvq_lds_floats(int nw) { return nw * dkdv_wave_floats<D>() + 32 * Cfg<D>::LD; }
 
@@ -683,10 +685,11 @@ dkdv_f32(Args a) {
     }
 }
 
-// Single-pass backward (D = 32 or 64): as dkdv_f32, plus dQ by atomics.  With RoPE, q and k
+// Single-pass backward: as dkdv_f32, plus dQ by atomics.  With RoPE, q and k
 // arrive rotated and dq is accumulated in the rotated frame (rotated back afterwards).
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_DKDVQ_WAVES_PER_EU)))
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_DKDVQ_WAVES_PER_EU)))
 dkdvq_f32(Args a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int per = a.B * a.Hkv;
@@ -913,8 +916,8 @@ hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, 
                                 const float *o, const float *lse, const float *dO, float *dq,
                                 float *dk, float *dv, float *delta, float *qrot, float *krot,
                                 hipStream_t st) {
-    // D = 128 would need 171.5 KB of LDS per work-group (160 KB per compute unit).
-    if (s.D != 32 && s.D != 64) return hipErrorInvalidValue;
+    // D = 128: 153 KB of LDS per work-group, one per compute unit.
+    if (s.D != 32 && s.D != 64 && s.D != 128) return hipErrorInvalidValue;
     const bool rope = s.rope_base > 0.f;
     const long long rows = (long long)s.B * s.Hq * s.T;
     if (rope) {  // q and k rotated once into the workspace
@@ -928,7 +931,9 @@ hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, 
     {
         const long long thr = rows * (s.D / 4);
         const unsigned grid = (unsigned)std::min<long long>((thr + 255) / 256, 1LL << 20);
-        const void *fn = s.D == 64 ? (const void *)delta_zero_f32<64> : (const void *)delta_zero_f32<32>;
+        const void *fn = s.D == 128  ? (const void *)delta_zero_f32<128>
+                         : s.D == 64 ? (const void *)delta_zero_f32<64>
+                                     : (const void *)delta_zero_f32<32>;
         long long r = rows;
         void *params[] = {&o, &dO, &delta, &dq, &r};
         const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), params, 0, st);
@@ -948,12 +953,16 @@ hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, 
     a.paired = g.paired;
     a.nkb = g.nkb;
     const bool causal = s.causal != 0;
-    const int lf = s.D == 64 ? dkdvq_lds_floats<64>(g.nwaves) : dkdvq_lds_floats<32>(g.nwaves);
+    const int lf = s.D == 128  ? dkdvq_lds_floats<128>(g.nwaves)
+                   : s.D == 64 ? dkdvq_lds_floats<64>(g.nwaves)
+                               : dkdvq_lds_floats<32>(g.nwaves);
     const void *k64[2][2] = {{(const void *)dkdvq_f32<64, false, false>, (const void *)dkdvq_f32<64, false, true>},
                              {(const void *)dkdvq_f32<64, true, false>, (const void *)dkdvq_f32<64, true, true>}};
     const void *k32[2][2] = {{(const void *)dkdvq_f32<32, false, false>, (const void *)dkdvq_f32<32, false, true>},
                              {(const void *)dkdvq_f32<32, true, false>, (const void *)dkdvq_f32<32, true, true>}};
-    const void *fn = (s.D == 64 ? k64 : k32)[causal][rope];
+    const void *k128[2][2] = {{(const void *)dkdvq_f32<128, false, false>, (const void *)dkdvq_f32<128, false, true>},
+                              {(const void *)dkdvq_f32<128, true, false>, (const void *)dkdvq_f32<128, true, true>}};
+    const void *fn = (s.D == 128 ? k128 : s.D == 64 ? k64 : k32)[causal][rope];
     hipError_t e = launch(fn, g.nblocks, 64 * g.nwaves, (size_t)lf * sizeof(float), st, a);
     if (e == hipSuccess && rope) e = launch_rope_f32(s, dq, dq, rows, st, true);  // dq = R^T dq'
     return e;

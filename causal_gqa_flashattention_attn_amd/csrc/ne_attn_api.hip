@@ -182,7 +182,7 @@ int bwd_fused_impl(const void *q, const void *k, const void *v, const void *o, c
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
-    if (dtype != NE_F32 || D == 128) return NE_ERR_UNSUPPORTED;
+    if (dtype != NE_F32) return NE_ERR_UNSUPPORTED;
     if (any_misaligned({q, k, v, o, lse, dO, dq, dk, dv, ws})) return NE_ERR_ALIGN;
     const WsLayout L = ws_layout(s, dtype);  // delta; with RoPE the rotated k and q
     char *w = static_cast<char *>(ws);

@@ -142,7 +142,7 @@ int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float
  * with ne_attn_bwd_ex to rounding.
  *
  * Arguments, layouts, ownership and errors as for ne_attn_bwd_ex, with these limits:
- * dtype NE_F32 only, D 32 or 64 (anything else: NE_ERR_UNSUPPORTED).  The workspace is that of
+ * dtype NE_F32 only (NE_BF16: NE_ERR_UNSUPPORTED).  The workspace is that of
  * ne_attn_bwd_ex, ne_attn_workspace_bytes(B, Hq, Hkv, T, D, NE_F32, rope_base) bytes: delta and,
  * with RoPE, the rotated q and k (dq is summed in the rotated frame and rotated back).
  */

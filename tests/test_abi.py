@@ -260,8 +260,8 @@ def test_fused_backward_validates(ne, which):
     assert fused(ne, T=0) == ne.NE_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=1), dict(dtype=1, rope=10000.0), dict(D=128),
+@pytest.mark.parametrize("kw", [dict(dtype=1), dict(dtype=1, rope=10000.0), dict(D=256),
                                 dict(D=48), dict(rope=-1.0)])
 def test_fused_backward_limits(ne, kw):
-    """float32 only, D 32 or 64."""
+    """float32 only; D 32, 64 or 128."""
     assert fused(ne, **kw) == ne.NE_ERR_UNSUPPORTED

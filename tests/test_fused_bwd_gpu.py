@@ -42,6 +42,8 @@ SHAPES = [
     (1, 4, 2, 1, 32), (1, 3, 1, 17, 64), (2, 4, 4, 37, 32), (1, 6, 2, 65, 64),
     (2, 12, 4, 255, 64), (1, 16, 2, 33, 64), (1, 5, 5, 96, 32), (1, 8, 1, 200, 64),
     (1, 10, 2, 77, 64), (3, 2, 2, 7, 64),
+    # head size 128: one work-group (four waves, one per SIMD) per compute unit
+    (1, 4, 2, 64, 128), (2, 12, 4, 130, 128), (1, 8, 1, 257, 128),
 ]
 
 
@@ -52,7 +54,8 @@ def test_fused_shapes(ne, oracle_mod, shape, causal):
     run_fused(ne, oracle_mod, Workload("fused", B, Hq, Hkv, T, D), seed=7, causal=causal)
 
 
-ROPE_SHAPES = [(1, 4, 2, 64, 32), (2, 12, 4, 130, 64), (1, 6, 3, 517, 64), (1, 8, 1, 1024, 64)]
+ROPE_SHAPES = [(1, 4, 2, 64, 32), (2, 12, 4, 130, 64), (1, 6, 3, 517, 64), (1, 8, 1, 1024, 64),
+               (1, 8, 2, 200, 128)]
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -62,6 +65,11 @@ def test_fused_rope(ne, oracle_mod, shape, causal):
     B, Hq, Hkv, T, D = shape
     run_fused(ne, oracle_mod, Workload("fused_rope", B, Hq, Hkv, T, D, rope_base=10000.0),
               seed=11, causal=causal)
+
+
+def test_fused_head_size_128_workload(ne, oracle_mod):
+    """The head-size-128 workload at a reduced batch (the oracle's cost)."""
+    run_fused(ne, oracle_mod, WORKLOADS["d128_f32"].with_(B=1))
 
 
 def test_fused_matches_two_pass_and_dkdv_is_reproducible(ne, oracle_mod):
