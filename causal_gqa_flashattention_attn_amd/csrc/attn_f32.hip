@@ -785,6 +785,7 @@ Args make_args(const Shape &s) {
 NE_PICK(fwd_f32)
 NE_PICK(dq_f32)
 NE_PICK(dkdv_f32)
+NE_PICK(dkdvq_f32)
 #undef NE_PICK
 
 hipError_t launch(const void *fn, long long blocks, int threads, size_t lds, hipStream_t st, Args &a) {
@@ -956,13 +957,9 @@ hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, 
     const int lf = s.D == 128  ? dkdvq_lds_floats<128>(g.nwaves)
                    : s.D == 64 ? dkdvq_lds_floats<64>(g.nwaves)
                                : dkdvq_lds_floats<32>(g.nwaves);
-    const void *k64[2][2] = {{(const void *)dkdvq_f32<64, false, false>, (const void *)dkdvq_f32<64, false, true>},
-                             {(const void *)dkdvq_f32<64, true, false>, (const void *)dkdvq_f32<64, true, true>}};
-    const void *k32[2][2] = {{(const void *)dkdvq_f32<32, false, false>, (const void *)dkdvq_f32<32, false, true>},
-                             {(const void *)dkdvq_f32<32, true, false>, (const void *)dkdvq_f32<32, true, true>}};
-    const void *k128[2][2] = {{(const void *)dkdvq_f32<128, false, false>, (const void *)dkdvq_f32<128, false, true>},
-                              {(const void *)dkdvq_f32<128, true, false>, (const void *)dkdvq_f32<128, true, true>}};
-    const void *fn = (s.D == 128 ? k128 : s.D == 64 ? k64 : k32)[causal][rope];
+    const void *fn = s.D == 128  ? pick_dkdvq_f32<128>(causal, rope)
+                     : s.D == 64 ? pick_dkdvq_f32<64>(causal, rope)
+                                 : pick_dkdvq_f32<32>(causal, rope);
     hipError_t e = launch(fn, g.nblocks, 64 * g.nwaves, (size_t)lf * sizeof(float), st, a);
     if (e == hipSuccess && rope) e = launch_rope_f32(s, dq, dq, rows, st, true);  // dq = R^T dq'
     return e;
