@@ -17,6 +17,11 @@ around every launch of the timed steps.  The `roofline` object describes the ker
 largest average duration; `cpu_baseline` times the fp64 oracle on the host cores on a bounded
 sample of the same workload.  Prints one JSON line.
 
+    python bench.py --workload block_gpu_model
+
+times instead the attention sub-block x + attn(rmsnorm(x)) of the GPU model, forward and
+backward (ne_attn_block_fwd, ne_attn_block_bwd), in TFLOP/s of its products.
+
     python bench.py --workload decode_gpu_model | decode_long
 
 (or `--workload prefill_gpu_model | prefill_long`, a chunk of queries against a cache, in
@@ -335,8 +340,120 @@ def main_prefill(a):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_block(w, x, min_seconds: float):
+    """The sub-block oracle (numpy fp64 products + the C attention oracle) on single batch
+    elements of the same inputs, forward + backward, until `min_seconds` have passed."""
+    import dataclasses
+
+    import oracle
+    from oracle.block import block_bwd
+    one = dataclasses.replace(w, B=1)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        b = done % w.B
+        block_bwd(x["x"][b:b + 1], x["gamma"], x["w_qkv"], x["w_o"], x["dy"][b:b + 1], w.Hq,
+                  w.Hkv, w.D, w.eps, w.rope_base)  # runs the forward too
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": one.flops() * done / el / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} single-batch-element sub-block forward + backward calls of "
+                      f"{w.name} (B=1 T{w.T} Hq{w.Hq} Hkv{w.Hkv} D{w.D}), {el:.1f} s, fp64"}
+
+
+def main_block(a):
+    """The attention sub-block x + attn(rmsnorm(x)), forward + backward (`--workload block_*`):
+    TFLOP/s of its products (three projection GEMMs per pass pair and the attention)."""
+    import numpy as np
+    import torch
+
+    import causal_gqa_flashattention_attn_amd as ne
+    from workloads import BLOCK_WORKLOADS, make_block_inputs
+
+    w = BLOCK_WORKLOADS[a.workload]
+    x = make_block_inputs(w, a.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = {n: torch.from_numpy(v).to(dev).contiguous() for n, v in x.items()}
+    y = torch.empty_like(t["x"])
+    dx, dgamma = torch.empty_like(t["x"]), torch.empty_like(t["gamma"])
+    dwq, dwo = torch.empty_like(t["w_qkv"]), torch.empty_like(t["w_o"])
+    ws = torch.empty(ne.ne_attn_block_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.rope_base),
+                     dtype=torch.uint8, device=dev)
+    L = ne.lib()
+    P = lambda v: ctypes.c_void_p(v.data_ptr())  # noqa: E731
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    dims = (w.B, w.T, w.Hq, w.Hkv, w.D, ctypes.c_float(w.eps), ctypes.c_float(w.rope_base), st)
+    fa = (P(t["x"]), P(t["gamma"]), P(t["w_qkv"]), P(t["w_o"]), P(y), P(ws)) + dims
+    ba = (P(t["x"]), P(t["gamma"]), P(t["w_qkv"]), P(t["w_o"]), P(t["dy"]), P(dx), P(dgamma),
+          P(dwq), P(dwo), P(ws)) + dims
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record()
+        rc = L.ne_attn_block_fwd(*fa)
+        if rc != ne.NE_OK:
+            raise ne.NeAttnError(rc, "ne_attn_block_fwd")
+        if e is not None:
+            e[1].record()
+        rc = L.ne_attn_block_bwd(*ba)
+        if rc != ne.NE_OK:
+            raise ne.NeAttnError(rc, "ne_attn_block_bwd")
+        if e is not None:
+            e[2].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    gc.disable()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    ms = (t1 - t0) * 1e3 / a.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    fl = w.flops()
+    line = {
+        "metric": f"attention sub-block fwd+bwd TFLOP/s (rmsnorm, QKV and output projections, "
+                  f"causal GQA attention with RoPE), B{w.B} T{w.T} Hq{w.Hq}/Hkv{w.Hkv} D{w.D} f32",
+        "value": round(fl / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "rope_base": w.rope_base, "eps": w.eps, "seed": a.seed},
+        "kernels": {"block_fwd": {"avg_ms": fwd_ms}, "block_bwd": {"avg_ms": bwd_ms}},
+        "roofline": {"bound": "mfma", "kernel": "sub-block forward + backward",
+                     "achieved": round(fl / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 3),
+                     "peak": MFMA_PEAK["f32"], "unit": "TFLOP/s",
+                     "frac": round(fl / ((fwd_ms + bwd_ms) * 1e-3) / 1e12 / MFMA_PEAK["f32"], 4),
+                     "traffic": None, "algorithmic_flops_per_launch": fl},
+        "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline_block(w, x, a.cpu_seconds),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
+    if a.workload.startswith("block"):
+        world = int(os.environ.get("WORLD_SIZE", "1"))
+        if a.gpus != 1 or world != 1:
+            print("bench.py measures one GPU only (run with --gpus 1)", file=sys.stderr)
+            sys.exit(2)
+        return main_block(a)
     if a.workload.startswith("prefill"):
         world = int(os.environ.get("WORLD_SIZE", "1"))
         if a.gpus != 1 or world != 1:

@@ -27,7 +27,8 @@ __all__ = [
     "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused", "ne_attn_decode",
     "ne_attn_prefill", "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror", "forward", "backward", "backward_fused",
-    "decode", "prefill", "workspace",
+    "decode", "prefill", "workspace", "ne_attn_block_fwd", "ne_attn_block_bwd",
+    "ne_attn_block_workspace_bytes", "block_forward", "block_backward",
     "NE_OK", "NE_ERR_NULL", "NE_ERR_SHAPE", "NE_ERR_UNSUPPORTED", "NE_ERR_ALIGN", "NE_ERR_HIP",
     "NE_F32", "NE_BF16", "EXPORTED_SYMBOLS",
 ]
@@ -38,7 +39,8 @@ NE_F32, NE_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
                     "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused",
                     "ne_attn_decode", "ne_attn_prefill", "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
-                    "ne_attn_bwd_workspace_bytes", "ne_attn_strerror")
+                    "ne_attn_bwd_workspace_bytes", "ne_attn_strerror", "ne_attn_block_fwd",
+                    "ne_attn_block_bwd", "ne_attn_block_workspace_bytes")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -87,6 +89,12 @@ def load():
     L.ne_attn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.ne_attn_bwd_workspace_bytes.argtypes = [i, i, i]
     L.ne_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.ne_attn_block_workspace_bytes.argtypes = [i] * 5 + [f]
+    L.ne_attn_block_workspace_bytes.restype = ctypes.c_size_t
+    L.ne_attn_block_fwd.argtypes = [vp] * 6 + [i] * 5 + [f, f, vp]
+    L.ne_attn_block_fwd.restype = i
+    L.ne_attn_block_bwd.argtypes = [vp] * 10 + [i] * 5 + [f, f, vp]
+    L.ne_attn_block_bwd.restype = i
     L.ne_attn_strerror.argtypes = [i]
     L.ne_attn_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -417,3 +425,76 @@ def prefill(q, k_cache, v_cache, stream=None):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     ne_attn_prefill(q, k_cache, v_cache, o, lse, stream=stream)
     return o, lse
+
+
+# ----------------------------------------------------------------------- attention sub-block
+
+def ne_attn_block_workspace_bytes(B: int, T: int, Hq: int, Hkv: int, D: int,
+                                  rope_base: float = 0.0) -> int:
+    return int(load().ne_attn_block_workspace_bytes(int(B), int(T), int(Hq), int(Hkv), int(D),
+                                                    float(rope_base)))
+
+
+def _block_check(x, gamma, w_qkv, w_o, Hq, Hkv, D):
+    torch = _torch()
+    B, T, C = x.shape
+    if C != Hq * D or tuple(gamma.shape) != (C,) or tuple(w_qkv.shape) != (C, (Hq + 2 * Hkv) * D) \
+            or tuple(w_o.shape) != (Hq * D, C):
+        raise ValueError("sub-block shapes: x [B,T,Hq*D], gamma [C], w_qkv [C,(Hq+2Hkv)D], "
+                         "w_o [Hq*D,C]")
+    for name, t in (("x", x), ("gamma", gamma), ("w_qkv", w_qkv), ("w_o", w_o)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    return B, T
+
+
+def ne_attn_block_fwd(x, gamma, w_qkv, w_o, y, workspace, Hq, Hkv, D, eps=1e-5, rope_base=0.0,
+                      stream=None):
+    torch = _torch()
+    B, T = _block_check(x, gamma, w_qkv, w_o, Hq, Hkv, D)
+    _ws_check(workspace, ne_attn_block_workspace_bytes(B, T, Hq, Hkv, D, rope_base), x.device)
+    _check_tensors(dict(x=x, gamma=gamma, w_qkv=w_qkv, w_o=w_o, y=y), x.device)
+    with torch.cuda.device(x.device):
+        rc = load().ne_attn_block_fwd(_p(x), _p(gamma), _p(w_qkv), _p(w_o), _p(y), _p(workspace),
+                                      B, T, Hq, Hkv, D, float(eps), float(rope_base),
+                                      _stream(stream, x.device))
+    _raise(rc, "ne_attn_block_fwd")
+
+
+def ne_attn_block_bwd(x, gamma, w_qkv, w_o, dy, dx, dgamma, dw_qkv, dw_o, workspace, Hq, Hkv, D,
+                      eps=1e-5, rope_base=0.0, stream=None):
+    torch = _torch()
+    B, T = _block_check(x, gamma, w_qkv, w_o, Hq, Hkv, D)
+    _ws_check(workspace, ne_attn_block_workspace_bytes(B, T, Hq, Hkv, D, rope_base), x.device)
+    _check_tensors(dict(x=x, gamma=gamma, w_qkv=w_qkv, w_o=w_o, dy=dy, dx=dx, dgamma=dgamma,
+                        dw_qkv=dw_qkv, dw_o=dw_o), x.device)
+    with torch.cuda.device(x.device):
+        rc = load().ne_attn_block_bwd(_p(x), _p(gamma), _p(w_qkv), _p(w_o), _p(dy), _p(dx),
+                                      _p(dgamma), _p(dw_qkv), _p(dw_o), _p(workspace), B, T, Hq,
+                                      Hkv, D, float(eps), float(rope_base),
+                                      _stream(stream, x.device))
+    _raise(rc, "ne_attn_block_bwd")
+
+
+def block_forward(x, gamma, w_qkv, w_o, Hq, Hkv, D, eps=1e-5, rope_base=0.0, stream=None):
+    """Allocates y and the sub-block workspace and runs the forward; returns (y, workspace)."""
+    torch = _torch()
+    B, T = _block_check(x, gamma, w_qkv, w_o, Hq, Hkv, D)
+    n = ne_attn_block_workspace_bytes(B, T, Hq, Hkv, D, rope_base)
+    if n == 0:
+        raise ValueError("invalid shape for a sub-block workspace")
+    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    y = torch.empty_like(x)
+    ne_attn_block_fwd(x, gamma, w_qkv, w_o, y, ws, Hq, Hkv, D, eps, rope_base, stream)
+    return y, ws
+
+
+def block_backward(x, gamma, w_qkv, w_o, dy, workspace, Hq, Hkv, D, eps=1e-5, rope_base=0.0,
+                   stream=None):
+    """Runs the sub-block backward after block_forward; returns (dx, dgamma, dw_qkv, dw_o)."""
+    torch = _torch()
+    dx, dgamma = torch.empty_like(x), torch.empty_like(gamma)
+    dw_qkv, dw_o = torch.empty_like(w_qkv), torch.empty_like(w_o)
+    ne_attn_block_bwd(x, gamma, w_qkv, w_o, dy, dx, dgamma, dw_qkv, dw_o, workspace, Hq, Hkv, D,
+                      eps, rope_base, stream)
+    return dx, dgamma, dw_qkv, dw_o

@@ -50,8 +50,8 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
     tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
-                   check=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
+                    "-L/opt/rocm/lib", "-lrocblas"], check=True)
     os.replace(tmp, LIB)
     return LIB
 

@@ -86,6 +86,18 @@ hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, 
                                 float *dk, float *dv, float *delta, float *qrot, float *krot,
                                 hipStream_t st);
 
+// Attention sub-block helpers (attn_block.hip), float32, row-major.
+hipError_t gemm_rm(hipStream_t st, bool ta, bool tb, int M, int N, int K, const float *A,
+                   const float *Bm, float *Cm, float beta);
+hipError_t launch_rmsnorm_fwd(const float *x, const float *gamma, float *xn, float *rstd,
+                              long long rows, int C, float eps, hipStream_t st);
+int rmsnorm_bwd_blocks(long long rows);
+hipError_t launch_rmsnorm_bwd(const float *x, const float *gamma, const float *rstd,
+                              const float *dxn, const float *dy, float *dx, float *part,
+                              float *dgamma, long long rows, int C, hipStream_t st);
+hipError_t launch_rows_heads(float *rows_, float *heads, int B, int T, int W, int h0, int H,
+                             int D, bool to_heads, hipStream_t st);
+
 // bfloat16 variants: tensors are bf16 (passed untyped), lse and delta fp32.
 hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const void *v, void *o,
                            float *lse, hipStream_t st);

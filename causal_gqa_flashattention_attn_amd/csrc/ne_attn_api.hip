@@ -197,6 +197,49 @@ int bwd_fused_impl(const void *q, const void *k, const void *v, const void *o, c
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
+// Attention sub-block workspace (float32): what the forward saves for the backward, then
+// scratch of either pass, each region 256-aligned.
+struct BlkLayout {
+    size_t xn, rstd, q, k, v, o, lse, attn, rows_a, rows_b, hq, hk, hv, hd, part, total;
+};
+
+BlkLayout blk_layout(const ne::Shape &s) {
+    const size_t N = (size_t)s.B * s.T, C = (size_t)s.Hq * s.D;
+    const size_t W = (size_t)(s.Hq + 2 * s.Hkv) * s.D;
+    const size_t nq = N * C, nk = N * (size_t)s.Hkv * s.D;
+    BlkLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t at = off; off += up256(bytes); return at; };
+    L.xn = take(4 * nq);
+    L.rstd = take(4 * N);
+    L.q = take(4 * nq);
+    L.k = take(4 * nk);
+    L.v = take(4 * nk);
+    L.o = take(4 * nq);
+    L.lse = take(4 * N * s.Hq);
+    L.attn = take(ws_layout(s, NE_F32).total);
+    L.rows_a = take(4 * N * W);   // qkv rows; in the backward dqkv rows
+    L.rows_b = take(4 * nq);      // o rows; in the backward also d(o rows) and dxn
+    L.hq = take(4 * nq);          // backward: dO, then dq
+    L.hk = take(4 * nk);          // backward: dk
+    L.hv = take(4 * nk);          // backward: dv
+    L.hd = take(4 * nq);          // backward: o rows
+    L.part = take(4 * (size_t)ne::rmsnorm_bwd_blocks((long long)N) * C);
+    L.total = off;
+    return L;
+}
+
+int blk_check(int B, int T, int Hq, int Hkv, int D, float eps, float rope_base, ne::Shape &s) {
+    const int rc = check_shape(B, Hq, Hkv, T, D, 1, NE_F32, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (!(eps > 0.f) || !isfinite(eps)) return NE_ERR_UNSUPPORTED;
+    const long long C = (long long)Hq * D, W = (long long)(Hq + 2 * Hkv) * D;
+    const long long N = (long long)B * T;
+    if (C > 16384 || W > 0x7fffffffLL / 4 || N > 0x7fffffffLL || N * W > (1LL << 40))
+        return NE_ERR_SHAPE;
+    return NE_OK;
+}
+
 // Decode workspace: the splits' outputs then their lse, each region 256-aligned.
 struct DecLayout {
     size_t part_lse, total;
@@ -274,6 +317,77 @@ int ne_attn_bwd_fused(const void *q, const void *k, const void *v, const void *o
                       int dtype, float rope_base, hipStream_t stream) {
     return bwd_fused_impl(q, k, v, o, lse, dO, dq, dk, dv, workspace, B, Hq, Hkv, T, D, causal,
                           dtype, rope_base, stream);
+}
+
+size_t ne_attn_block_workspace_bytes(int B, int T, int Hq, int Hkv, int D, float rope_base) {
+    ne::Shape s;
+    if (blk_check(B, T, Hq, Hkv, D, 1e-5f, rope_base, s) != NE_OK) return 0;
+    return blk_layout(s).total;
+}
+
+int ne_attn_block_fwd(const float *x, const float *gamma, const float *w_qkv, const float *w_o,
+                      float *y, void *workspace, int B, int T, int Hq, int Hkv, int D, float eps,
+                      float rope_base, hipStream_t stream) {
+    if (!x || !gamma || !w_qkv || !w_o || !y || !workspace) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = blk_check(B, T, Hq, Hkv, D, eps, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (any_misaligned({x, gamma, w_qkv, w_o, y, workspace})) return NE_ERR_ALIGN;
+    const BlkLayout L = blk_layout(s);
+    char *w = static_cast<char *>(workspace);
+    auto F = [&](size_t off) { return reinterpret_cast<float *>(w + off); };
+    const long long N = (long long)B * T;
+    const int C = Hq * D, W = (Hq + 2 * Hkv) * D;
+    hipError_t e = ne::launch_rmsnorm_fwd(x, gamma, F(L.xn), F(L.rstd), N, C, eps, stream);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, false, false, (int)N, W, C, F(L.xn), w_qkv, F(L.rows_a), 0.f);
+    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.q), B, T, W, 0, Hq, D, true, stream);
+    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.k), B, T, W, Hq, Hkv, D, true, stream);
+    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.v), B, T, W, Hq + Hkv, Hkv, D, true, stream);
+    if (e != hipSuccess) return NE_ERR_HIP;
+    const int ra = fwd_impl(F(L.q), F(L.k), F(L.v), F(L.o), F(L.lse), w + L.attn, B, Hq, Hkv, T, D,
+                            1, NE_F32, rope_base, stream);
+    if (ra != NE_OK) return ra;
+    e = ne::launch_rows_heads(F(L.rows_b), F(L.o), B, T, C, 0, Hq, D, false, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(y, x, sizeof(float) * (size_t)N * C, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, false, false, (int)N, C, C, F(L.rows_b), w_o, y, 1.f);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+int ne_attn_block_bwd(const float *x, const float *gamma, const float *w_qkv, const float *w_o,
+                      const float *dy, float *dx, float *dgamma, float *dw_qkv, float *dw_o,
+                      void *workspace, int B, int T, int Hq, int Hkv, int D, float eps,
+                      float rope_base, hipStream_t stream) {
+    if (!x || !gamma || !w_qkv || !w_o || !dy || !dx || !dgamma || !dw_qkv || !dw_o || !workspace)
+        return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = blk_check(B, T, Hq, Hkv, D, eps, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (any_misaligned({x, gamma, w_qkv, w_o, dy, dx, dgamma, dw_qkv, dw_o, workspace}))
+        return NE_ERR_ALIGN;
+    const BlkLayout L = blk_layout(s);
+    char *w = static_cast<char *>(workspace);
+    auto F = [&](size_t off) { return reinterpret_cast<float *>(w + off); };
+    const long long N = (long long)B * T;
+    const int C = Hq * D, W = (Hq + 2 * Hkv) * D;
+    // d(o rows) = dy Wo^T;  dWo = (o rows)^T dy
+    hipError_t e = ne::gemm_rm(stream, false, true, (int)N, C, C, dy, w_o, F(L.rows_b), 0.f);
+    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.hd), F(L.o), B, T, C, 0, Hq, D, false, stream);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, true, false, C, C, (int)N, F(L.hd), dy, dw_o, 0.f);
+    // dO heads, then the attention backward (two passes) into dq, dk, dv heads
+    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_b), F(L.hd), B, T, C, 0, Hq, D, true, stream);
+    if (e != hipSuccess) return NE_ERR_HIP;
+    const int ra = bwd_impl(F(L.q), F(L.k), F(L.v), F(L.o), F(L.lse), F(L.hd), F(L.hq), F(L.hk),
+                            F(L.hv), w + L.attn, B, Hq, Hkv, T, D, 1, NE_F32, rope_base, stream);
+    if (ra != NE_OK) return ra;
+    // dqkv rows; dWqkv = xn^T dqkv; dxn = dqkv Wqkv^T; RMSNorm backward
+    e = ne::launch_rows_heads(F(L.rows_a), F(L.hq), B, T, W, 0, Hq, D, false, stream);
+    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.hk), B, T, W, Hq, Hkv, D, false, stream);
+    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.hv), B, T, W, Hq + Hkv, Hkv, D, false, stream);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, true, false, C, W, (int)N, F(L.xn), F(L.rows_a), dw_qkv, 0.f);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, false, true, (int)N, C, W, F(L.rows_a), w_qkv, F(L.rows_b), 0.f);
+    if (e == hipSuccess)
+        e = ne::launch_rmsnorm_bwd(x, gamma, F(L.rstd), F(L.rows_b), dy, dx, F(L.part), dgamma, N, C, stream);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
 size_t ne_attn_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int dtype,

@@ -194,6 +194,34 @@ int ne_attn_decode(const void *q, const void *k_cache, const void *v_cache, cons
 int ne_attn_prefill(const void *q, const void *k_cache, const void *v_cache, void *o, float *lse,
                     int B, int Hq, int Hkv, int Tq, int Tk, int D, int dtype, hipStream_t stream);
 
+/*
+ * The attention sub-block around the kernel, float32: the pre-norm residual branch of a
+ * NanoEuler block, y = x + attn(rmsnorm(x)) ("NanoEuler -- Show HN" Japanese README translation,
+ * section "Architecture": RMSNorm pre-normalisation without bias, RoPE on queries and keys,
+ * grouped-query attention, x = x + attn(rmsnorm(x))):
+ *   r = (mean_c x^2 + eps)^(-1/2),  xn = x r gamma,  [q | k | v] = xn w_qkv,
+ *   o = causal GQA attention (RoPE when rope_base > 0),  y = x + o w_o.
+ * x, y: [B][T][C] with C = Hq * D; gamma: [C]; w_qkv: [C][(Hq + 2 Hkv) D], columns ordered
+ * q heads, then k heads, then v heads, D per head; w_o: [Hq D][C]; all float32, row-major,
+ * device memory, 16-byte aligned.  The products run in rocBLAS (a handle per device, created on
+ * the first call and kept); the rest in the library's kernels.
+ *
+ * workspace: caller-owned, ne_attn_block_workspace_bytes(...) bytes.  ne_attn_block_fwd leaves
+ * in it what ne_attn_block_bwd needs, so the backward must follow a forward with the same
+ * inputs and workspace (same stream, or an event).  ne_attn_block_bwd writes dx (including the
+ * residual dy), dgamma, dw_qkv and dw_o, all overwritten; results are bitwise reproducible
+ * given rocBLAS's own determinism.  Errors as above; NE_ERR_UNSUPPORTED also for eps <= 0,
+ * NE_ERR_SHAPE for C above 16384.
+ */
+size_t ne_attn_block_workspace_bytes(int B, int T, int Hq, int Hkv, int D, float rope_base);
+int ne_attn_block_fwd(const float *x, const float *gamma, const float *w_qkv, const float *w_o,
+                      float *y, void *workspace, int B, int T, int Hq, int Hkv, int D, float eps,
+                      float rope_base, hipStream_t stream);
+int ne_attn_block_bwd(const float *x, const float *gamma, const float *w_qkv, const float *w_o,
+                      const float *dy, float *dx, float *dgamma, float *dw_qkv, float *dw_o,
+                      void *workspace, int B, int T, int Hq, int Hkv, int D, float eps,
+                      float rope_base, hipStream_t stream);
+
 /* Bytes of the decode workspace: 4 * S * B * Hq * (D + 1) with S = ceil(Tc / 256), in two
  * regions each rounded up to 256 bytes; 0 if the arguments are invalid. */
 size_t ne_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Tc, int D, int dtype);

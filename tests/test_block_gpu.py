@@ -1,0 +1,48 @@
+"""The attention sub-block x + attn(rmsnorm(x)) (ne_attn_block_fwd / _bwd) against its fp64
+oracle (oracle/block.py): normwise relative error max |g - g_ref| / max |g_ref| <= 1e-4 on y, dx,
+dgamma, dw_qkv and dw_o (float32 products over up to 8192 rows)."""
+import numpy as np
+import pytest
+
+from helpers import normwise
+from workloads import BLOCK_WORKLOADS, BlockWorkload, make_block_inputs
+
+pytestmark = pytest.mark.gpu
+BAR = 1e-4
+
+
+def run_block(ne, w, seed=0):
+    import torch
+    from oracle.block import block_bwd, block_fwd
+    print(f"\n[case] block B{w.B} T{w.T} Hq{w.Hq} Hkv{w.Hkv} D{w.D} rope={w.rope_base}", flush=True)
+    x = make_block_inputs(w, seed)
+    dev = {n: torch.from_numpy(a).cuda() for n, a in x.items()}
+    y, ws = ne.block_forward(dev["x"], dev["gamma"], dev["w_qkv"], dev["w_o"], w.Hq, w.Hkv, w.D,
+                             w.eps, w.rope_base)
+    grads = ne.block_backward(dev["x"], dev["gamma"], dev["w_qkv"], dev["w_o"], dev["dy"], ws,
+                              w.Hq, w.Hkv, w.D, w.eps, w.rope_base)
+    torch.cuda.synchronize()
+    ry, _ = block_fwd(x["x"], x["gamma"], x["w_qkv"], x["w_o"], w.Hq, w.Hkv, w.D, w.eps,
+                      w.rope_base)
+    rg = block_bwd(x["x"], x["gamma"], x["w_qkv"], x["w_o"], x["dy"], w.Hq, w.Hkv, w.D, w.eps,
+                   w.rope_base)
+    for name, a, r in zip(("y", "dx", "dgamma", "dw_qkv", "dw_o"), (y,) + tuple(grads),
+                          (ry,) + tuple(rg)):
+        e = normwise(a.double().cpu().numpy(), r)
+        print(f"  {name}_rel={e:.2e}")
+        assert e <= BAR, (name, e)
+
+
+@pytest.mark.parametrize("shape,rope", [((1, 37, 4, 2, 32), 0.0), ((1, 37, 4, 2, 32), 10000.0),
+                                        ((2, 130, 12, 4, 64), 10000.0), ((1, 65, 8, 1, 128), 500.0),
+                                        ((2, 100, 6, 6, 64), 0.0)],
+                         ids=lambda v: str(v))
+def test_block_shapes(ne, shape, rope):
+    B, T, Hq, Hkv, D = shape
+    run_block(ne, BlockWorkload("block", B, T, Hq, Hkv, D, rope_base=rope), seed=3)
+
+
+def test_block_gpu_model_shape(ne):
+    """The GPU model's sub-block (dim 768, 12/4 heads, T 512) at B = 2 (the oracle's cost)."""
+    from dataclasses import replace
+    run_block(ne, replace(BLOCK_WORKLOADS["block_gpu_model"], B=2))

@@ -199,3 +199,52 @@ def make_prefill_inputs(w: PrefillWorkload, seed: int = 0) -> dict:
     if w.dtype == "bf16":
         q, k, v = (round_to_bf16(a) for a in (q, k, v))
     return {"q": q, "k": k, "v": v}
+
+
+# ----------------------------------------------------------------------- attention sub-block
+
+@dataclasses.dataclass(frozen=True)
+class BlockWorkload:
+    """The attention sub-block x + attn(rmsnorm(x)) at one layer's shape: x [B, T, C],
+    C = Hq D; gamma [C]; w_qkv [C, (Hq + 2 Hkv) D]; w_o [Hq D, C]."""
+    name: str
+    B: int
+    T: int
+    Hq: int
+    Hkv: int
+    D: int
+    rope_base: float = 10000.0
+    eps: float = 1e-5
+    note: str = ""
+
+    @property
+    def C(self) -> int:
+        return self.Hq * self.D
+
+    def flops(self) -> float:
+        """Forward + backward: the three projection GEMMs of each pass (forward 2 products,
+        backward 4) plus the attention's 7 B Hq T^2 D (causal)."""
+        n = self.B * self.T
+        w = (self.Hq + 2 * self.Hkv) * self.D
+        gemm_fwd = 2.0 * n * self.C * w + 2.0 * n * self.Hq * self.D * self.C
+        return 3.0 * gemm_fwd + 3.5 * 2.0 * self.B * self.Hq * self.T * self.T * self.D
+
+
+BLOCK_WORKLOADS = {
+    "block_gpu_model": BlockWorkload("block_gpu_model", 16, 512, 12, 4, 64,
+                                     note="the GPU model's attention sub-block (dim 768)"),
+}
+
+
+def make_block_inputs(w: BlockWorkload, seed: int = 0) -> dict:
+    """Draws, in order, x ~ N(0, 1), gamma = 1 + 0.1 N(0, 1), w_qkv and w_o ~ N(0, 1 / C),
+    dy ~ N(0, 1), float32."""
+    rng = np.random.default_rng(seed)
+    C, W = w.C, (w.Hq + 2 * w.Hkv) * w.D
+    f = np.float32
+    x = rng.standard_normal((w.B, w.T, C), dtype=f)
+    gamma = (1.0 + 0.1 * rng.standard_normal(C, dtype=f)).astype(f)
+    w_qkv = (rng.standard_normal((C, W), dtype=f) / np.sqrt(C)).astype(f)
+    w_o = (rng.standard_normal((w.Hq * w.D, C), dtype=f) / np.sqrt(C)).astype(f)
+    dy = rng.standard_normal((w.B, w.T, C), dtype=f)
+    return {"x": x, "gamma": gamma, "w_qkv": w_qkv, "w_o": w_o, "dy": dy}
