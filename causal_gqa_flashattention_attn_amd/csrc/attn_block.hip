@@ -82,13 +82,24 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_f32(const float *x, const flo
         pb[c] = (red[c] + red[C + c]) + (red[2 * C + c] + red[3 * C + c]);
 }
 
-// dgamma[c] = sum over blocks of part[block][c], in block order.
+// dgamma[c] = sum over blocks of part[block][c]: 32 columns per work-group, eight groups of
+// partial rows (g, g + 8, ...) summed in order, then the eight group sums added in order, so
+// the result does not depend on scheduling.
 __global__ void __launch_bounds__(256) colsum_f32(const float *part, float *out, int nblk, int C) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= C) return;
+    __shared__ float red[8][32];
+    const int cg = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const int c = blockIdx.x * 32 + cg;
     float s = 0.f;
-    for (int b = 0; b < nblk; ++b) s += part[(size_t)b * C + c];
-    out[c] = s;
+    if (c < C)
+        for (int b = g; b < nblk; b += 8) s += part[(size_t)b * C + c];
+    red[g][cg] = s;
+    __syncthreads();
+    if (g == 0 && c < C) {
+        float t = red[0][cg];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) t += red[k][cg];
+        out[c] = t;
+    }
 }
 
 // Rows [B T][W] (W = heads_total D) <-> heads [B][H][T][D] for the heads h0 .. h0 + H - 1 of a
@@ -152,12 +163,15 @@ hipError_t launch_rmsnorm_fwd(const float *x, const float *gamma, float *xn, flo
                            dim3(256), p, 0, st);
 }
 
-int rmsnorm_bwd_blocks(long long rows) { return (int)((rows + 63) / 64); }
+// Rows per rmsnorm_bwd work-group: four per wave, enough work-groups to stream the rows.
+constexpr int kNormRows = 16;
+
+int rmsnorm_bwd_blocks(long long rows) { return (int)((rows + kNormRows - 1) / kNormRows); }
 
 hipError_t launch_rmsnorm_bwd(const float *x, const float *gamma, const float *rstd,
                               const float *dxn, const float *dy, float *dx, float *part,
                               float *dgamma, long long rows, int C, hipStream_t st) {
-    int rpb = 64;
+    int rpb = kNormRows;
     const int nblk = rmsnorm_bwd_blocks(rows);
     void *p[] = {&x, &gamma, &rstd, &dxn, &dy, &dx, &part, &rows, &C, &rpb};
     hipError_t e = hipLaunchKernel((const void *)rmsnorm_bwd_f32, dim3((unsigned)nblk), dim3(256),
@@ -165,7 +179,7 @@ hipError_t launch_rmsnorm_bwd(const float *x, const float *gamma, const float *r
     if (e != hipSuccess) return e;
     int nb = nblk;
     void *q[] = {&part, &dgamma, &nb, &C};
-    return hipLaunchKernel((const void *)colsum_f32, dim3((unsigned)((C + 255) / 256)), dim3(256),
+    return hipLaunchKernel((const void *)colsum_f32, dim3((unsigned)((C + 31) / 32)), dim3(256),
                            q, 0, st);
 }
 
