@@ -265,3 +265,37 @@ def test_fused_backward_validates(ne, which):
 def test_fused_backward_limits(ne, kw):
     """float32 only; D 32, 64 or 128."""
     assert fused(ne, **kw) == ne.NE_ERR_UNSUPPORTED
+
+
+def block_call(ne, which, ptrs=None, B=1, T=16, Hq=4, Hkv=2, D=32, eps=1e-5, rope=0.0):
+    L = ne.load()
+    if which == "fwd":
+        p = ptrs or [A] * 6
+        return L.ne_attn_block_fwd(*[VP(x) for x in p], B, T, Hq, Hkv, D, eps, rope, VP(0))
+    p = ptrs or [A] * 10
+    return L.ne_attn_block_bwd(*[VP(x) for x in p], B, T, Hq, Hkv, D, eps, rope, VP(0))
+
+
+@pytest.mark.parametrize("which,n", [("fwd", 6), ("bwd", 10)])
+def test_block_validates(ne, which, n):
+    for j in range(n):
+        p = [A] * n
+        p[j] = 0
+        assert block_call(ne, which, p) == ne.NE_ERR_NULL
+        p[j] = A + 4
+        assert block_call(ne, which, p) == ne.NE_ERR_ALIGN
+    assert block_call(ne, which, Hkv=3) == ne.NE_ERR_SHAPE
+    assert block_call(ne, which, T=0) == ne.NE_ERR_SHAPE
+    assert block_call(ne, which, D=48) == ne.NE_ERR_UNSUPPORTED
+    assert block_call(ne, which, eps=0.0) == ne.NE_ERR_UNSUPPORTED
+    assert block_call(ne, which, eps=float("nan")) == ne.NE_ERR_UNSUPPORTED
+    assert block_call(ne, which, rope=-1.0) == ne.NE_ERR_UNSUPPORTED
+
+
+def test_block_workspace_bytes(ne):
+    n = ne.ne_attn_block_workspace_bytes(2, 64, 4, 2, 32, 0.0)
+    n_rope = ne.ne_attn_block_workspace_bytes(2, 64, 4, 2, 32, 10000.0)
+    C, N = 4 * 32, 2 * 64
+    assert n > 4 * N * C * 4 and n_rope > n          # RoPE adds the rotated q, k
+    assert ne.ne_attn_block_workspace_bytes(2, 64, 4, 3, 32, 0.0) == 0  # Hq % Hkv
+    assert ne.ne_attn_block_workspace_bytes(2, 64, 4, 2, 48, 0.0) == 0  # unsupported D
