@@ -117,3 +117,44 @@ def test_graph_replays_decode(ne):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, eo) and torch.equal(lse, el)
+
+
+def test_graph_replays_block(ne):
+    """The attention sub-block (its rocBLAS products included) captured forward + backward."""
+    import torch
+    from workloads import BlockWorkload, make_block_inputs
+    print("\n[case] graph sub-block", flush=True)
+    w = BlockWorkload("graph", 2, 96, 4, 2, 32)
+    x = {n: torch.from_numpy(a).cuda() for n, a in make_block_inputs(w, 4).items()}
+    y = torch.empty_like(x["x"])
+    dx, dg = torch.empty_like(x["x"]), torch.empty_like(x["gamma"])
+    dwq, dwo = torch.empty_like(x["w_qkv"]), torch.empty_like(x["w_o"])
+    ws = torch.empty(ne.ne_attn_block_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.rope_base),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        ne.ne_attn_block_fwd(x["x"], x["gamma"], x["w_qkv"], x["w_o"], y, ws, w.Hq, w.Hkv, w.D,
+                             w.eps, w.rope_base)
+        ne.ne_attn_block_bwd(x["x"], x["gamma"], x["w_qkv"], x["w_o"], x["dy"], dx, dg, dwq, dwo,
+                             ws, w.Hq, w.Hkv, w.D, w.eps, w.rope_base)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (y, dx, dg, dwq, dwo)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        for t in (y, dx, dg, dwq, dwo):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((y, dx, dg, dwq, dwo), eager):
+            assert torch.equal(a, b)
