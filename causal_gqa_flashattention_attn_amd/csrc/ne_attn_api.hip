@@ -235,7 +235,8 @@ int blk_check(int B, int T, int Hq, int Hkv, int D, float eps, float rope_base, 
     if (!(eps > 0.f) || !isfinite(eps)) return NE_ERR_UNSUPPORTED;
     const long long C = (long long)Hq * D, W = (long long)(Hq + 2 * Hkv) * D;
     const long long N = (long long)B * T;
-    if (C > 16384 || W > 0x7fffffffLL / 4 || N > 0x7fffffffLL || N * W > (1LL << 40))
+    // C <= 8192: the RMSNorm backward keeps four rows of C floats in LDS (128 KB).
+    if (C > 8192 || W > 0x7fffffffLL / 4 || N > 0x7fffffffLL || N * W > (1LL << 40))
         return NE_ERR_SHAPE;
     return NE_OK;
 }

@@ -211,7 +211,7 @@ int ne_attn_prefill(const void *q, const void *k_cache, const void *v_cache, voi
  * inputs and workspace (same stream, or an event).  ne_attn_block_bwd writes dx (including the
  * residual dy), dgamma, dw_qkv and dw_o, all overwritten; results are bitwise reproducible
  * given rocBLAS's own determinism.  Errors as above; NE_ERR_UNSUPPORTED also for eps <= 0,
- * NE_ERR_SHAPE for C above 16384.
+ * NE_ERR_SHAPE for C above 8192.
  */
 size_t ne_attn_block_workspace_bytes(int B, int T, int Hq, int Hkv, int D, float rope_base);
 int ne_attn_block_fwd(const float *x, const float *gamma, const float *w_qkv, const float *w_o,

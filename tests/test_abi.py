@@ -290,6 +290,7 @@ def test_block_validates(ne, which, n):
     assert block_call(ne, which, eps=0.0) == ne.NE_ERR_UNSUPPORTED
     assert block_call(ne, which, eps=float("nan")) == ne.NE_ERR_UNSUPPORTED
     assert block_call(ne, which, rope=-1.0) == ne.NE_ERR_UNSUPPORTED
+    assert block_call(ne, which, Hq=130, Hkv=2, D=64) == ne.NE_ERR_SHAPE  # C = 8320 > 8192
 
 
 def test_block_workspace_bytes(ne):
