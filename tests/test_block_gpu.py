@@ -46,3 +46,9 @@ def test_block_gpu_model_shape(ne):
     """The GPU model's sub-block (dim 768, 12/4 heads, T 512) at B = 2 (the oracle's cost)."""
     from dataclasses import replace
     run_block(ne, replace(BLOCK_WORKLOADS["block_gpu_model"], B=2))
+
+
+def test_block_widest_rows(ne):
+    """The widest rows the entry points accept, C = Hq D = 8192 (64 query heads of 128): the
+    RMSNorm backward then keeps four rows of C floats, 128 KB, in LDS.  T = 40 is ragged."""
+    run_block(ne, BlockWorkload("block", 1, 40, 64, 8, 128, rope_base=10000.0), seed=5)
