@@ -448,10 +448,19 @@ def _block_check(x, gamma, w_qkv, w_o, Hq, Hkv, D):
     return B, T
 
 
+def _like_check(**pairs):
+    """Each (tensor, model) pair: the tensor must be float32 with the model's shape."""
+    torch = _torch()
+    for name, (t, m) in pairs.items():
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(m.shape):
+            raise ValueError(f"{name} must be float32 of shape {tuple(m.shape)}")
+
+
 def ne_attn_block_fwd(x, gamma, w_qkv, w_o, y, workspace, Hq, Hkv, D, eps=1e-5, rope_base=0.0,
                       stream=None):
     torch = _torch()
     B, T = _block_check(x, gamma, w_qkv, w_o, Hq, Hkv, D)
+    _like_check(y=(y, x))
     _ws_check(workspace, ne_attn_block_workspace_bytes(B, T, Hq, Hkv, D, rope_base), x.device)
     _check_tensors(dict(x=x, gamma=gamma, w_qkv=w_qkv, w_o=w_o, y=y), x.device)
     with torch.cuda.device(x.device):
@@ -465,6 +474,8 @@ def ne_attn_block_bwd(x, gamma, w_qkv, w_o, dy, dx, dgamma, dw_qkv, dw_o, worksp
                       eps=1e-5, rope_base=0.0, stream=None):
     torch = _torch()
     B, T = _block_check(x, gamma, w_qkv, w_o, Hq, Hkv, D)
+    _like_check(dy=(dy, x), dx=(dx, x), dgamma=(dgamma, gamma), dw_qkv=(dw_qkv, w_qkv),
+                dw_o=(dw_o, w_o))
     _ws_check(workspace, ne_attn_block_workspace_bytes(B, T, Hq, Hkv, D, rope_base), x.device)
     _check_tensors(dict(x=x, gamma=gamma, w_qkv=w_qkv, w_o=w_o, dy=dy, dx=dx, dgamma=dgamma,
                         dw_qkv=dw_qkv, dw_o=dw_o), x.device)

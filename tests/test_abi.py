@@ -300,3 +300,28 @@ def test_block_workspace_bytes(ne):
     assert n > 4 * N * C * 4 and n_rope > n          # RoPE adds the rotated q, k
     assert ne.ne_attn_block_workspace_bytes(2, 64, 4, 3, 32, 0.0) == 0  # Hq % Hkv
     assert ne.ne_attn_block_workspace_bytes(2, 64, 4, 2, 48, 0.0) == 0  # unsupported D
+
+
+def test_block_binding_checks_output_shapes(ne):
+    """The binding rejects outputs whose shape or dtype differs from what the entry points write
+    (before any device call, so host tensors serve)."""
+    import torch
+    B, T, Hq, Hkv, D = 1, 16, 4, 2, 32
+    C, W = Hq * D, (Hq + 2 * Hkv) * D
+    x, g = torch.zeros(B, T, C), torch.zeros(C)
+    wqkv, wo = torch.zeros(C, W), torch.zeros(C, C)
+    ws = torch.zeros(1, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="y must be"):
+        ne.ne_attn_block_fwd(x, g, wqkv, wo, torch.zeros(B, T - 1, C), ws, Hq, Hkv, D)
+    with pytest.raises(ValueError, match="y must be"):
+        ne.ne_attn_block_fwd(x, g, wqkv, wo, torch.zeros(B, T, C, dtype=torch.float64), ws, Hq,
+                             Hkv, D)
+    good = dict(dy=x, dx=torch.zeros_like(x), dgamma=torch.zeros_like(g),
+                dw_qkv=torch.zeros_like(wqkv), dw_o=torch.zeros_like(wo))
+    for name, bad in (("dy", torch.zeros(B, T, C + 4)), ("dx", torch.zeros(B * T, C)),
+                      ("dgamma", torch.zeros(C + 1)), ("dw_qkv", torch.zeros(W, C)),
+                      ("dw_o", torch.zeros(C, C, dtype=torch.float16))):
+        args = dict(good, **{name: bad})
+        with pytest.raises(ValueError, match=f"{name} must be"):
+            ne.ne_attn_block_bwd(x, g, wqkv, wo, args["dy"], args["dx"], args["dgamma"],
+                                 args["dw_qkv"], args["dw_o"], ws, Hq, Hkv, D)
