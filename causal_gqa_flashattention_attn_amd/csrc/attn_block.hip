@@ -129,14 +129,18 @@ unsigned grid_for(long long n) {
 
 }  // namespace
 
+namespace {
+// Guards the handles: their creation, and the stream a handle is bound to between setting it
+// and enqueueing a product on it (host threads share a device's handle).
+std::mutex blas_mu;
+}  // namespace
+
 // rocBLAS handle per device, created on first use (rocBLAS allocates its own workspace then)
-// and kept for the life of the process.
+// and kept for the life of the process.  The caller holds blas_mu.
 rocblas_handle blas_handle() {
-    static std::mutex mu;
     static rocblas_handle h[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
     if (!h[dev] && rocblas_create_handle(&h[dev]) != rocblas_status_success) h[dev] = nullptr;
     return h[dev];
 }
@@ -146,6 +150,7 @@ rocblas_handle blas_handle() {
 // C^T = op(B)^T op(A)^T.
 hipError_t gemm_rm(hipStream_t st, bool ta, bool tb, int M, int N, int K, const float *A,
                    const float *Bm, float *Cm, float beta) {
+    std::lock_guard<std::mutex> lock(blas_mu);  // set_stream + sgemm only enqueue: held briefly
     rocblas_handle h = blas_handle();
     if (!h || rocblas_set_stream(h, st) != rocblas_status_success) return hipErrorUnknown;
     const float alpha = 1.f;

@@ -52,3 +52,43 @@ def test_block_widest_rows(ne):
     """The widest rows the entry points accept, C = Hq D = 8192 (64 query heads of 128): the
     RMSNorm backward then keeps four rows of C floats, 128 KB, in LDS.  T = 40 is ragged."""
     run_block(ne, BlockWorkload("block", 1, 40, 64, 8, 128, rope_base=10000.0), seed=5)
+
+
+def test_block_two_host_threads(ne):
+    """Two host threads, each on a stream of its own, run the sub-block forward at once: the
+    products share the device's rocBLAS handle, whose stream each call binds under a lock, so
+    every result is bitwise the one computed alone."""
+    import threading
+    import torch
+    w = BlockWorkload("block", 2, 130, 12, 4, 64, rope_base=10000.0)
+    print("\n[case] block forward from two host threads", flush=True)
+    dev = [{n: torch.from_numpy(a).cuda() for n, a in make_block_inputs(w, s).items()}
+           for s in (11, 12)]
+    args = lambda d: (d["x"], d["gamma"], d["w_qkv"], d["w_o"], w.Hq, w.Hkv, w.D, w.eps,
+                      w.rope_base)
+    ref = [ne.block_forward(*args(d))[0] for d in dev]
+    torch.cuda.synchronize()
+    reps = 8
+    out = [[None] * reps for _ in dev]
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for r in range(reps):
+                    out[i][r] = ne.block_forward(*args(dev[i]), stream=s)[0]
+            s.synchronize()
+        except Exception as e:  # surfaced in the main thread below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(dev))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in range(len(dev)):
+        for r in range(reps):
+            assert torch.equal(out[i][r], ref[i]), (i, r)
