@@ -26,7 +26,8 @@
  *
  * Ownership and memory.  Every pointer is a device pointer owned by the caller; the library
  * allocates and frees nothing, keeps no state and is thread-safe (calls that share a workspace
- * must be ordered).  Outputs (o, lse, dq, dk, dv,
+ * must be ordered).  The one exception is the sub-block, whose products keep a rocBLAS handle
+ * per device (see ne_attn_block_fwd).  Outputs (o, lse, dq, dk, dv,
  * delta) are fully overwritten; inputs are never written.  Inputs and outputs must not alias.
  * Pointers must be 16-byte aligned.
  *
