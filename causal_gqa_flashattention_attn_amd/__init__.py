@@ -8,8 +8,11 @@ marshal arguments: they read sizes from tensor shapes, pass ``data_ptr()`` and t
 HIP stream, and raise ``NeAttnError`` on a non-zero status.  All arithmetic happens in the HIP
 kernels.  PyTorch provides device memory and streams.
 
-``forward``, ``backward``, ``backward_fused``, ``decode`` and ``prefill`` are conveniences that allocate the outputs and the
-workspace with torch and call the entry points.
+``forward``, ``backward``, ``backward_fused``, ``decode``, ``prefill``, ``block_forward`` and
+``block_backward`` are conveniences that allocate the outputs and the workspace with torch and
+call the entry points.  They allocate on the stream the kernels run on (``stream``, else the
+current stream), so torch's caching allocator never hands a workspace that is dropped on return
+to other work while the kernels may still use it; the outputs belong to that stream too.
 
 Tensor layout: q, o, dO, dq: [B, Hq, T, D]; k, v, dk, dv: [B, Hkv, T, D]; lse: [B, Hq, T]
 float32; all contiguous on one GPU; float32, or bfloat16 through the ``_ex`` entry points.
@@ -18,6 +21,7 @@ Prefill: q, o: [B, Hq, Tq, D]; k_cache, v_cache: [B, Hkv, Tk, D]; lse: [B, Hq, T
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -164,6 +168,17 @@ def _stream(stream, dev):
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _alloc_on(stream, dev):
+    """Context in which the conveniences allocate: `stream` made current (a torch stream, or a
+    raw HIP stream handle wrapped as an external stream), or nothing when stream is None."""
+    torch = _torch()
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream, device=dev)
+    return torch.cuda.stream(stream)
 
 
 def _p(t):
@@ -373,21 +388,23 @@ def forward(q, k, v, causal: bool = True, rope_base: float = 0.0, stream=None):
     """Allocates o, lse (and with RoPE the workspace) and runs the forward pass; returns
     (o, lse)."""
     torch = _torch()
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    ws = workspace(q, k, rope_base) if rope_base > 0 else None
-    ne_attn_fwd_ex(q, k, v, o, lse, ws, causal=causal, rope_base=rope_base, stream=stream)
+    with _alloc_on(stream, q.device):
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        ws = workspace(q, k, rope_base) if rope_base > 0 else None
+        ne_attn_fwd_ex(q, k, v, o, lse, ws, causal=causal, rope_base=rope_base, stream=stream)
     return o, lse
 
 
 def backward(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 0.0, stream=None):
     """Allocates dq, dk, dv and the workspace and runs the backward pass."""
     torch = _torch()
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
-    ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, rope_base), causal=causal,
-                   rope_base=rope_base, stream=stream)
+    with _alloc_on(stream, q.device):
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        ne_attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, rope_base),
+                       causal=causal, rope_base=rope_base, stream=stream)
     return dq, dk, dv
 
 
@@ -395,11 +412,12 @@ def backward_fused(q, k, v, o, lse, dO, causal: bool = True, rope_base: float = 
                    stream=None):
     """Single-pass backward (float32); dq is not bitwise reproducible."""
     torch = _torch()
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
-    ne_attn_bwd_fused(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, rope_base),
-                      causal=causal, rope_base=rope_base, stream=stream)
+    with _alloc_on(stream, q.device):
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        ne_attn_bwd_fused(q, k, v, o, lse, dO, dq, dk, dv, workspace(q, k, rope_base),
+                          causal=causal, rope_base=rope_base, stream=stream)
     return dq, dk, dv
 
 
@@ -411,19 +429,21 @@ def decode(q, k_cache, v_cache, lens, stream=None):
                                        _dtype_code(q))
     if n == 0:
         raise ValueError("invalid shape for a decode workspace")
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
-    ne_attn_decode(q, k_cache, v_cache, lens, o, lse, ws, stream=stream)
+    with _alloc_on(stream, q.device):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+        ne_attn_decode(q, k_cache, v_cache, lens, o, lse, ws, stream=stream)
     return o, lse
 
 
 def prefill(q, k_cache, v_cache, stream=None):
     """Allocates o, lse and runs a prefill chunk; returns (o, lse)."""
     torch = _torch()
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    ne_attn_prefill(q, k_cache, v_cache, o, lse, stream=stream)
+    with _alloc_on(stream, q.device):
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        ne_attn_prefill(q, k_cache, v_cache, o, lse, stream=stream)
     return o, lse
 
 
@@ -494,9 +514,10 @@ def block_forward(x, gamma, w_qkv, w_o, Hq, Hkv, D, eps=1e-5, rope_base=0.0, str
     n = ne_attn_block_workspace_bytes(B, T, Hq, Hkv, D, rope_base)
     if n == 0:
         raise ValueError("invalid shape for a sub-block workspace")
-    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
-    y = torch.empty_like(x)
-    ne_attn_block_fwd(x, gamma, w_qkv, w_o, y, ws, Hq, Hkv, D, eps, rope_base, stream)
+    with _alloc_on(stream, x.device):
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+        y = torch.empty_like(x)
+        ne_attn_block_fwd(x, gamma, w_qkv, w_o, y, ws, Hq, Hkv, D, eps, rope_base, stream)
     return y, ws
 
 
@@ -504,8 +525,9 @@ def block_backward(x, gamma, w_qkv, w_o, dy, workspace, Hq, Hkv, D, eps=1e-5, ro
                    stream=None):
     """Runs the sub-block backward after block_forward; returns (dx, dgamma, dw_qkv, dw_o)."""
     torch = _torch()
-    dx, dgamma = torch.empty_like(x), torch.empty_like(gamma)
-    dw_qkv, dw_o = torch.empty_like(w_qkv), torch.empty_like(w_o)
-    ne_attn_block_bwd(x, gamma, w_qkv, w_o, dy, dx, dgamma, dw_qkv, dw_o, workspace, Hq, Hkv, D,
-                      eps, rope_base, stream)
+    with _alloc_on(stream, x.device):
+        dx, dgamma = torch.empty_like(x), torch.empty_like(gamma)
+        dw_qkv, dw_o = torch.empty_like(w_qkv), torch.empty_like(w_o)
+        ne_attn_block_bwd(x, gamma, w_qkv, w_o, dy, dx, dgamma, dw_qkv, dw_o, workspace, Hq, Hkv,
+                          D, eps, rope_base, stream)
     return dx, dgamma, dw_qkv, dw_o

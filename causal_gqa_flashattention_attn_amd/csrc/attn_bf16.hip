@@ -10,8 +10,10 @@
 //
 // RoPE: the pair (x[2i], x[2i+1]) at position t is rotated by t * base^(-2i/D) in fp32 when q
 // and k are loaded; the rotated values are rounded to bf16 before they enter the matrix cores.
-// dq and dk are rotated back (transpose) in fp32 before rounding, so they are gradients with
-// respect to the caller's un-rotated q and k.
+// The angle is formed and reduced modulo one turn in double precision (per-pair turn rates are
+// evaluated on the host in double), so it is exact to float rounding at every position.  dq and
+// dk are rotated back (transpose) in fp32 before rounding, so they are gradients with respect to
+// the caller's un-rotated q and k.
 //
 // Layout in LDS: K, V, Q and dO tiles stay row-major as in HBM (16-byte chunks XOR-swizzled per
 // row).  Products that contract over the tile's rows (P V, dS K, dO^T P, Q^T dS) read their
@@ -69,26 +71,35 @@ struct ArgsB {
     int Tk, qoff;   // forward: key length and position of query row 0 (Tk = T, 0 usually)
     float qscale;   // scale * log2(e)
     float scale;    // 1 / sqrt(D)
-    float rope_lb;  // log2(rope base)
+    RopeTurns rt;        // turns per position of each RoPE pair (double)
+    double rope_shift4;  // base^(-8/D): per_pos[i + 4] / per_pos[i]
+    double rope_shift2;  // base^(-4/D): per_pos[i + 2] / per_pos[i]
+    double rope_lb;      // log2(base)
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
 
-// Turns per position of pair i: base^(-2i/D) / (2 pi).
-template <int D>
-__device__ __forceinline__ float rope_rate(int i, float lb) {
-    return exp2f(-(2.0f * (float)i / (float)D) * lb) * 0.15915494309189535f;
+// RoPE angles in turns.  Pair i of a row at position t turns by t * per_pos[i], per_pos[i] =
+// base^(-2i/D) / (2 pi) evaluated on the host in double.  A lane's pairs are i0 + p for a
+// compile-time i0, offset by a whole number of pairs j on the second half-wave; since
+// per_pos[i0 + j + p] = per_pos[i0 + p] * base^(-2j/D), the lane folds that factor into its
+// position once (tpos, double) and every angle is tpos times a scalar rate, formed and reduced
+// modulo one turn in double, then rounded once to float: exact to float rounding at any position.
+__device__ __forceinline__ float rope_frac(double tpos, double rate) {
+    const double turns = tpos * rate;
+    return (float)(turns - rint(turns));
 }
 
-// Rotates the pairs (x[2p], x[2p+1]), p < N/2, of a row at position t; rates[p] is the turn
-// rate of pair p.  The fractional turn goes to the hardware sine/cosine (input in turns).
+// Rotates the pairs (x[2p], x[2p+1]), p < N/2, by tpos * rt.per_pos[i0 + p] turns (the
+// transpose when inv).  The reduced angle goes to the hardware sine/cosine (input in turns).
 template <int N>
-__device__ __forceinline__ void rope_rotate(float (&x)[N], int t, const float *rates, bool inv) {
+__device__ __forceinline__ void rope_rotate(float (&x)[N], double tpos, const RopeTurns &rt,
+                                            int i0, bool inv) {
 #pragma unroll
     for (int p = 0; p < N / 2; ++p) {
-        const float fr = __builtin_amdgcn_fractf((float)t * rates[p]);
+        const float fr = rope_frac(tpos, rt.per_pos[i0 + p]);
         const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
         const float a = x[2 * p], b = x[2 * p + 1];
         if (!inv) {
@@ -113,28 +124,27 @@ __device__ __forceinline__ bf16x8 round8(const float (&x)[8]) {
 }
 
 // 8 elements (row, c0 .. c0+7) from HBM, rotated when ROPE (rates of the 4 pairs given).
+// (With ROPE: tpos, rt and i0 give the angles of its four pairs, as for rope_rotate.)
 template <int D, bool ROPE>
 __device__ __forceinline__ bf16x8 load_row8(const __bf16 *base, int row, int T, int c0,
-                                            const float *rates) {
+                                            double tpos, const RopeTurns &rt, int i0) {
     const int r = min(row, T - 1);
     bf16x8 v = *reinterpret_cast<const bf16x8 *>(base + (size_t)r * D + c0);
     if (ROPE) {
         float x[8];
         unpack8(v, x);
-        rope_rotate<8>(x, row, rates, false);
+        rope_rotate<8>(x, tpos, rt, i0, false);
         v = round8(x);
     }
     return v;
 }
 
-// Stores four fp32 values (row, c0 .. c0+3) as bf16, optionally rotating them back first.
+// Stores four fp32 values (row, c0 .. c0+3) as bf16, optionally rotating them back first (the
+// two pairs' angles from tpos, rt and i0, as for rope_rotate).
 template <int D, bool ROPE_INV>
 __device__ __forceinline__ void store_row4(__bf16 *base, int row, int c0, float (&x)[4],
-                                           float lb) {
-    if (ROPE_INV) {
-        const float rates[2] = {rope_rate<D>(c0 / 2, lb), rope_rate<D>(c0 / 2 + 1, lb)};
-        rope_rotate<4>(x, row, rates, true);
-    }
+                                           double tpos, const RopeTurns &rt, int i0) {
+    if (ROPE_INV) rope_rotate<4>(x, tpos, rt, i0, true);
     bf16x4 r{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
     *reinterpret_cast<bf16x4 *>(base + (size_t)row * D + c0) = r;
 }
@@ -276,18 +286,15 @@ struct KVRingB {
 };
 
 // This lane's query (or key) row as KS operand chunks: chunk s holds columns 16 s + 8 half ..+7.
+// With ROPE the row is rotated: chunk s holds pairs 8 s + 4 half + p (p < 4), so the second
+// half-wave's pairs are 4 further on (rope_shift4 = base^(-8/D) folded into its position).
 template <int D, bool ROPE>
 __device__ __forceinline__ void load_operand_row(bf16x8 (&dst)[CfgB<D>::KS], const __bf16 *base,
-                                                 int row, int T, int half, float lb) {
+                                                 int row, int T, int half, const ArgsB &a) {
+    const double tpos = ROPE ? (double)row * (half ? a.rope_shift4 : 1.0) : 0.0;
 #pragma unroll
-    for (int s = 0; s < CfgB<D>::KS; ++s) {
-        const int c0 = 16 * s + 8 * half;
-        float rates[4];
-        if (ROPE)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) rates[p] = rope_rate<D>(c0 / 2 + p, lb);
-        dst[s] = load_row8<D, ROPE>(base, row, T, c0, rates);
-    }
+    for (int s = 0; s < CfgB<D>::KS; ++s)
+        dst[s] = load_row8<D, ROPE>(base, row, T, 16 * s + 8 * half, tpos, a.rt, 8 * s);
 }
 
 // S^T block (32 keys of the tile from row r0 x this wave's 32 rows) = M_tile x X^T.
@@ -470,7 +477,7 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
     for (int t = 0; t < R::PD; ++t)
         if (t < ntiles) kv.issue(kg, vg, t, Tk, ring + t * R::SB);
     bf16x8 qv[C::KS];
-    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
+    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a);
 
     FwdState<D> st;
 #pragma unroll
@@ -518,7 +525,7 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
             for (int u = 0; u < 4; ++u) {
                 float x[4] = {st.acc[dd][4 * u] * inv, st.acc[dd][4 * u + 1] * inv,
                               st.acc[dd][4 * u + 2] * inv, st.acc[dd][4 * u + 3] * inv};
-                store_row4<D, false>(orow, qrow, 32 * dd + 8 * u + 4 * half, x, 0.f);
+                store_row4<D, false>(orow, qrow, 32 * dd + 8 * u + 4 * half, x, 0.0, a.rt, 0);
             }
         if (half == 0) a.out_lse[bh * T + qrow] = st.m * kLn2 + logf(l);
     }
@@ -567,19 +574,19 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
     for (int t = 0; t < R::PD; ++t)
         if (t < ntiles) kv.issue(kg, vg, t, T, ring + t * R::SB);
     bf16x8 qv[C::KS], dov[C::KS];
-    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a.rope_lb);
+    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a);
     if (ROPE && qrow < T) {  // each query row is loaded by exactly one wave: keep its rotation
 #pragma unroll
         for (int st = 0; st < C::KS; ++st)
             *reinterpret_cast<bf16x8 *>(a.qrot + (bh * T + qrow) * D + 16 * st + 8 * half) = qv[st];
     }
-    load_operand_row<D, false>(dov, a.dO + bh * T * D, qrow, T, half, 0.f);
+    load_operand_row<D, false>(dov, a.dO + bh * T * D, qrow, T, half, a);
 
     // delta_i = sum_d dO_id o_id over this row (fp32), written once for the dK/dV pass.
     float delta;
     {
         bf16x8 ov[C::KS];
-        load_operand_row<D, false>(ov, a.o + bh * T * D, qrow, T, half, 0.f);
+        load_operand_row<D, false>(ov, a.o + bh * T * D, qrow, T, half, a);
         float part = 0.f;
 #pragma unroll
         for (int s = 0; s < C::KS; ++s)
@@ -648,13 +655,16 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
 
     if (qrow < T) {
         __bf16 *drow = a.dq + bh * T * D;
+        const double tpos2 = ROPE ? (double)qrow * (half ? a.rope_shift2 : 1.0) : 0.0;
 #pragma unroll
         for (int dd = 0; dd < C::ND; ++dd)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 float x[4] = {acc[dd][4 * u] * a.scale, acc[dd][4 * u + 1] * a.scale,
                               acc[dd][4 * u + 2] * a.scale, acc[dd][4 * u + 3] * a.scale};
-                store_row4<D, ROPE>(drow, qrow, 32 * dd + 8 * u + 4 * half, x, a.rope_lb);
+                // pairs 16 dd + 4 u + 2 half + p: the second half-wave's are 2 further on
+                store_row4<D, ROPE>(drow, qrow, 32 * dd + 8 * u + 4 * half, x, tpos2, a.rt,
+                                    16 * dd + 4 * u);
             }
     }
 }
@@ -783,8 +793,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     if (wave < nitems) issue(wave, wbuf);
     if (wave + nw < nitems) issue(wave + nw, wbuf + S::SB);
     bf16x8 kv[C::KS], vv[C::KS];
-    load_operand_row<D, false>(kv, a.k + bg * T * D, krow, T, half, a.rope_lb);
-    load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, 0.f);
+    load_operand_row<D, false>(kv, a.k + bg * T * D, krow, T, half, a);
+    load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, a);
     wait_vm_lgkm0(0);
     TrAddr<D> tra;  // transposed reads of the stage-0 Q tile; other tiles are immediate offsets
     tra.init(wbuf, lane);
@@ -880,10 +890,13 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         const int row = kb * 32 + r;
         if (row < T) {
             float x[4] = {sum[0], sum[1], sum[2], sum[3]};
-            if (t == 0)
-                store_row4<D, ROPE>(a.dk + bg * T * D, row, cc, x, a.rope_lb);
-            else
-                store_row4<D, false>(a.dv + bg * T * D, row, cc, x, 0.f);
+            if (t == 0) {
+                // pairs cc / 2 + p: per_pos[cc / 2 + p] = per_pos[p] * base^(-cc/D)
+                const double tpos = ROPE ? (double)row * exp2(-(double)cc / D * a.rope_lb) : 0.0;
+                store_row4<D, ROPE>(a.dk + bg * T * D, row, cc, x, tpos, a.rt, 0);
+            } else {
+                store_row4<D, false>(a.dv + bg * T * D, row, cc, x, 0.0, a.rt, 0);
+            }
         }
     }
 }
@@ -947,7 +960,11 @@ ArgsB make_args_b(const Shape &s) {
     a.G = s.G;
     a.scale = (float)(1.0 / sqrt((double)s.D));
     a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));
-    a.rope_lb = s.rope_base > 0.f ? (float)log2((double)s.rope_base) : 0.f;
+    a.rt = rope_turns(s);
+    const double lb = s.rope_base > 0.f ? log2((double)s.rope_base) : 0.0;
+    a.rope_shift4 = exp2(-8.0 / s.D * lb);
+    a.rope_shift2 = exp2(-4.0 / s.D * lb);
+    a.rope_lb = lb;
     const QTileGeom g = qtile_geometry(s, false);
     a.hpw = g.hpw;
     a.rb = g.rb;

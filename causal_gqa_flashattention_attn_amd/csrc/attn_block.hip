@@ -130,13 +130,13 @@ unsigned grid_for(long long n) {
 }  // namespace
 
 namespace {
-// Guards the handles: their creation, and the stream a handle is bound to between setting it
-// and enqueueing a product on it (host threads share a device's handle).
+// Guards the handles: their creation, and the stream and workspace a handle is bound to between
+// binding them and enqueueing a product on it (host threads share a device's handle).
 std::mutex blas_mu;
 }  // namespace
 
-// rocBLAS handle per device, created on first use (rocBLAS allocates its own workspace then)
-// and kept for the life of the process.  The caller holds blas_mu.
+// rocBLAS handle per device, created on first use and kept for the life of the process.  The
+// caller holds blas_mu.
 rocblas_handle blas_handle() {
     static rocblas_handle h[64] = {};
     int dev = 0;
@@ -147,12 +147,16 @@ rocblas_handle blas_handle() {
 
 // Row-major C[M][N] = alpha op(A) op(B) + beta C with op(A) [M][K], op(B) [K][N]; ta / tb: the
 // stored matrix is the transpose ([K][M] / [N][K]).  rocBLAS is column-major, so it computes
-// C^T = op(B)^T op(A)^T.
-hipError_t gemm_rm(hipStream_t st, bool ta, bool tb, int M, int N, int K, const float *A,
-                   const float *Bm, float *Cm, float beta) {
-    std::lock_guard<std::mutex> lock(blas_mu);  // set_stream + sgemm only enqueue: held briefly
+// C^T = op(B)^T op(A)^T.  The product runs on `st` with `ws` (ws_bytes, owned by the caller) as
+// its rocBLAS workspace: a launch takes its workspace address when it is enqueued, so products
+// of calls with distinct workspaces never share scratch memory, whatever their streams.
+hipError_t gemm_rm(hipStream_t st, void *ws, size_t ws_bytes, bool ta, bool tb, int M, int N,
+                   int K, const float *A, const float *Bm, float *Cm, float beta) {
+    std::lock_guard<std::mutex> lock(blas_mu);  // binding + sgemm only enqueue: held briefly
     rocblas_handle h = blas_handle();
-    if (!h || rocblas_set_stream(h, st) != rocblas_status_success) return hipErrorUnknown;
+    if (!h || rocblas_set_stream(h, st) != rocblas_status_success ||
+        rocblas_set_workspace(h, ws, ws_bytes) != rocblas_status_success)
+        return hipErrorUnknown;
     const float alpha = 1.f;
     const rocblas_status s = rocblas_sgemm(
         h, tb ? rocblas_operation_transpose : rocblas_operation_none,

@@ -87,8 +87,10 @@ hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, 
                                 hipStream_t st);
 
 // Attention sub-block helpers (attn_block.hip), float32, row-major.
-hipError_t gemm_rm(hipStream_t st, bool ta, bool tb, int M, int N, int K, const float *A,
-                   const float *Bm, float *Cm, float beta);
+// rocBLAS workspace of the sub-block's products: a region of the caller's block workspace.
+constexpr size_t kBlasWorkspaceBytes = (size_t)32 << 20;
+hipError_t gemm_rm(hipStream_t st, void *ws, size_t ws_bytes, bool ta, bool tb, int M, int N,
+                   int K, const float *A, const float *Bm, float *Cm, float beta);
 hipError_t launch_rmsnorm_fwd(const float *x, const float *gamma, float *xn, float *rstd,
                               long long rows, int C, float eps, hipStream_t st);
 int rmsnorm_bwd_blocks(long long rows);

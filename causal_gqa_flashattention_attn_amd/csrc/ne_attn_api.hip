@@ -13,6 +13,10 @@ namespace {
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// The bf16 kernels address one head's T x D tensor through buffer resources, whose byte count
+// and offsets are 32-bit: a head must span at most 2^31 bytes (T <= 2^23 at D = 128).
+bool bf16_head_fits(long long T, int D) { return T * D * 2 <= (1LL << 31); }
+
 // Checks shared by every entry point; fills `s` on success.
 int check_shape(int B, int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
                 ne::Shape &s) {
@@ -24,6 +28,7 @@ int check_shape(int B, int Hq, int Hkv, int T, int D, int causal, int dtype, flo
     // Element counts and grid sizes must stay far from 64-bit and 31-bit limits.
     const double rows = (double)B * (double)Hq * (double)T;
     if (rows * D > 9.0e15 || T > (1 << 24)) return NE_ERR_SHAPE;
+    if (dtype == NE_BF16 && !bf16_head_fits(T, D)) return NE_ERR_SHAPE;
     s.B = B;
     s.Hq = Hq;
     s.Hkv = Hkv;
@@ -200,7 +205,7 @@ int bwd_fused_impl(const void *q, const void *k, const void *v, const void *o, c
 // Attention sub-block workspace (float32): what the forward saves for the backward, then
 // scratch of either pass, each region 256-aligned.
 struct BlkLayout {
-    size_t xn, rstd, q, k, v, o, lse, attn, rows_a, rows_b, hq, hk, hv, hd, part, total;
+    size_t xn, rstd, q, k, v, o, lse, attn, rows_a, rows_b, hq, hk, hv, hd, part, blas, total;
 };
 
 BlkLayout blk_layout(const ne::Shape &s) {
@@ -225,6 +230,7 @@ BlkLayout blk_layout(const ne::Shape &s) {
     L.hv = take(4 * nk);          // backward: dv
     L.hd = take(4 * nq);          // backward: o rows
     L.part = take(4 * (size_t)ne::rmsnorm_bwd_blocks((long long)N) * C);
+    L.blas = take(ne::kBlasWorkspaceBytes);  // rocBLAS workspace of the projections
     L.total = off;
     return L;
 }
@@ -340,7 +346,7 @@ int ne_attn_block_fwd(const float *x, const float *gamma, const float *w_qkv, co
     const long long N = (long long)B * T;
     const int C = Hq * D, W = (Hq + 2 * Hkv) * D;
     hipError_t e = ne::launch_rmsnorm_fwd(x, gamma, F(L.xn), F(L.rstd), N, C, eps, stream);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, false, false, (int)N, W, C, F(L.xn), w_qkv, F(L.rows_a), 0.f);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, false, false, (int)N, W, C, F(L.xn), w_qkv, F(L.rows_a), 0.f);
     if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.q), B, T, W, 0, Hq, D, true, stream);
     if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.k), B, T, W, Hq, Hkv, D, true, stream);
     if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.v), B, T, W, Hq + Hkv, Hkv, D, true, stream);
@@ -350,7 +356,7 @@ int ne_attn_block_fwd(const float *x, const float *gamma, const float *w_qkv, co
     if (ra != NE_OK) return ra;
     e = ne::launch_rows_heads(F(L.rows_b), F(L.o), B, T, C, 0, Hq, D, false, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(y, x, sizeof(float) * (size_t)N * C, hipMemcpyDeviceToDevice, stream);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, false, false, (int)N, C, C, F(L.rows_b), w_o, y, 1.f);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, false, false, (int)N, C, C, F(L.rows_b), w_o, y, 1.f);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
@@ -371,9 +377,9 @@ int ne_attn_block_bwd(const float *x, const float *gamma, const float *w_qkv, co
     const long long N = (long long)B * T;
     const int C = Hq * D, W = (Hq + 2 * Hkv) * D;
     // d(o rows) = dy Wo^T;  dWo = (o rows)^T dy
-    hipError_t e = ne::gemm_rm(stream, false, true, (int)N, C, C, dy, w_o, F(L.rows_b), 0.f);
+    hipError_t e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, false, true, (int)N, C, C, dy, w_o, F(L.rows_b), 0.f);
     if (e == hipSuccess) e = ne::launch_rows_heads(F(L.hd), F(L.o), B, T, C, 0, Hq, D, false, stream);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, true, false, C, C, (int)N, F(L.hd), dy, dw_o, 0.f);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, true, false, C, C, (int)N, F(L.hd), dy, dw_o, 0.f);
     // dO heads, then the attention backward (two passes) into dq, dk, dv heads
     if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_b), F(L.hd), B, T, C, 0, Hq, D, true, stream);
     if (e != hipSuccess) return NE_ERR_HIP;
@@ -384,8 +390,8 @@ int ne_attn_block_bwd(const float *x, const float *gamma, const float *w_qkv, co
     e = ne::launch_rows_heads(F(L.rows_a), F(L.hq), B, T, W, 0, Hq, D, false, stream);
     if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.hk), B, T, W, Hq, Hkv, D, false, stream);
     if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.hv), B, T, W, Hq + Hkv, Hkv, D, false, stream);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, true, false, C, W, (int)N, F(L.xn), F(L.rows_a), dw_qkv, 0.f);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, false, true, (int)N, C, W, F(L.rows_a), w_qkv, F(L.rows_b), 0.f);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, true, false, C, W, (int)N, F(L.xn), F(L.rows_a), dw_qkv, 0.f);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, false, true, (int)N, C, W, F(L.rows_a), w_qkv, F(L.rows_b), 0.f);
     if (e == hipSuccess)
         e = ne::launch_rmsnorm_bwd(x, gamma, F(L.rstd), F(L.rows_b), dy, dx, F(L.part), dgamma, N, C, stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
@@ -422,6 +428,7 @@ int ne_attn_prefill(const void *q, const void *k_cache, const void *v_cache, voi
     const int rc = check_shape(B, Hq, Hkv, Tq, D, 1, dtype, 0.f, s);
     if (rc != NE_OK) return rc;
     if (Tk < Tq || Tk > (1 << 24) || (double)B * Hkv * Tk * D > 9.0e15) return NE_ERR_SHAPE;
+    if (dtype == NE_BF16 && !bf16_head_fits(Tk, D)) return NE_ERR_SHAPE;
     if (any_misaligned({q, k_cache, v_cache, o, lse})) return NE_ERR_ALIGN;
     s.Tk = Tk;
     const hipError_t e =

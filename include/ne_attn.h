@@ -205,9 +205,10 @@ int ne_attn_prefill(const void *q, const void *k_cache, const void *v_cache, voi
  * x, y: [B][T][C] with C = Hq * D; gamma: [C]; w_qkv: [C][(Hq + 2 Hkv) D], columns ordered
  * q heads, then k heads, then v heads, D per head; w_o: [Hq D][C]; all float32, row-major,
  * device memory, 16-byte aligned.  The products run in rocBLAS (a handle per device, created on
- * the first call and kept); the rest in the library's kernels.  Host threads may call these
- * entry points at once, on streams of their own: each product binds the shared handle to the
- * caller's stream and is enqueued under one lock.
+ * the first call and kept); the rest in the library's kernels.  Each product binds the shared
+ * handle to the caller's stream and to a 32 MiB region of the caller's workspace as rocBLAS
+ * scratch, and is enqueued under one lock, so host threads may call these entry points at once,
+ * on streams of their own, each with its own workspace.
  *
  * workspace: caller-owned, ne_attn_block_workspace_bytes(...) bytes.  ne_attn_block_fwd leaves
  * in it what ne_attn_block_bwd needs, so the backward must follow a forward with the same

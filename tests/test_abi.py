@@ -116,6 +116,21 @@ def test_bad_shapes(ne, kw):
     assert fwd(ne, dtype=0, **kw) == ne.NE_ERR_SHAPE
 
 
+def test_bf16_head_limit(ne):
+    """The bf16 kernels address a head through 32-bit buffer offsets: a head of more than 2^31
+    bytes is refused before any launch (T above 2^23 at D = 128), in every entry point."""
+    T = (1 << 23) + 1
+    assert fwd(ne, dtype=1, T=T, D=128) == ne.NE_ERR_SHAPE
+    assert fwd(ne, dtype=1, T=T, D=128, rope=10000.0) == ne.NE_ERR_SHAPE
+    assert bwd(ne, dtype=1, T=T, D=128) == ne.NE_ERR_SHAPE
+    assert ne.ne_attn_workspace_bytes(1, 4, 2, T, 128, 1, 0.0) == 0
+    assert ne.ne_attn_decode_workspace_bytes(1, 4, 2, T, 128, 1) == 0
+    assert prefill_call(ne, Tq=16, Tk=T, D=128, dtype=1) == ne.NE_ERR_SHAPE
+    # the same sizes are fine for shapes the bound does not reach (checked without launching)
+    assert ne.ne_attn_workspace_bytes(1, 4, 2, T, 128, 0, 0.0) > 0
+    assert ne.ne_attn_workspace_bytes(1, 4, 2, 1 << 24, 64, 1, 0.0) > 0
+
+
 @pytest.mark.parametrize("kw", [dict(D=16), dict(D=256), dict(D=48), dict(dtype=2),
                                 dict(dtype=-1), dict(dtype=0, rope=-1.0),
                                 dict(dtype=0, rope=float("inf")), dict(dtype=0, rope=float("nan"))])

@@ -43,9 +43,15 @@ def test_block_shapes(ne, shape, rope):
 
 
 def test_block_gpu_model_shape(ne):
-    """The GPU model's sub-block (dim 768, 12/4 heads, T 512) at B = 2 (the oracle's cost)."""
+    """The GPU model's sub-block (dim 768, 12/4 heads, T 512) at B = 2."""
     from dataclasses import replace
     run_block(ne, replace(BLOCK_WORKLOADS["block_gpu_model"], B=2))
+
+
+def test_block_gpu_model_bench_batch(ne):
+    """The sub-block at the batch it is timed at (B = 16, 8192 rows): the attention kernels then
+    take their mirrored tile order and rocBLAS its kernels for that many rows."""
+    run_block(ne, BLOCK_WORKLOADS["block_gpu_model"])
 
 
 def test_block_widest_rows(ne):
@@ -56,8 +62,9 @@ def test_block_widest_rows(ne):
 
 def test_block_two_host_threads(ne):
     """Two host threads, each on a stream of its own, run the sub-block forward at once: the
-    products share the device's rocBLAS handle, whose stream each call binds under a lock, so
-    every result is bitwise the one computed alone."""
+    products share the device's rocBLAS handle, whose stream and scratch (a region of the
+    call's own workspace) each call binds under a lock, so every result is bitwise the one
+    computed alone."""
     import threading
     import torch
     w = BlockWorkload("block", 2, 130, 12, 4, 64, rope_base=10000.0)

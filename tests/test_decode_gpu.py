@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import BF16_REL, F32_ABS_O, normwise
+from helpers import BF16_ABS_LSE, BF16_REL, F32_ABS_O, normwise
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,7 @@ def run_case(ne, B, Hq, Hkv, Tc, D, lens, bf16, seed=0):
     if bf16:
         assert normwise(o[full], o_ref[full]) <= BF16_REL
         assert normwise(lse[full], lse_ref[full]) <= BF16_REL
+        assert np.abs(lse[full] - lse_ref[full]).max() <= BF16_ABS_LSE
     else:
         assert np.abs(o[full] - o_ref[full]).max() <= F32_ABS_O
         assert np.abs(lse[full] - lse_ref[full]).max() <= F32_ABS_O

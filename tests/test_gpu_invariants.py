@@ -180,3 +180,34 @@ def test_split_backward_passes_match_combined(ne, dtype_name, rope):
     torch.cuda.synchronize()
     for a_, b_ in ((o, o2), (lse, lse2), (dq, dq2), (dk, dk2), (dv, dv2)):
         assert torch.equal(a_, b_)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conveniences_allocate_on_the_kernel_stream(ne, dtype):
+    """backward(..., stream=s) with s not made current: its workspace (dropped when the call
+    returns) and its outputs come from s's memory, so the default stream can take and overwrite
+    memory while the kernels on s still run without touching what they read or write."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, Hq, Hkv, T, D, base = 2, 8, 2, 2048, 64, 10000.0
+    x = qkvd(B, Hq, Hkv, T, D, 60)
+    q, k, v, dO = (torch.from_numpy(x[n]).cuda().to(tdt) for n in ("q", "k", "v", "dO"))
+    print(f"\n[case] conveniences on a side stream {dtype}", flush=True)
+    o, lse = ne.forward(q, k, v, rope_base=base)
+    ref = ne.backward(q, k, v, o, lse, dO, rope_base=base)
+    torch.cuda.synchronize()
+    nws = ne.ne_attn_workspace_bytes(B, Hq, Hkv, T, D, ne.NE_BF16 if dtype == "bf16" else ne.NE_F32,
+                                     base)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        got = ne.backward(q, k, v, o, lse, dO, rope_base=base, stream=s)
+        # the default stream takes blocks of the workspace's and the outputs' sizes and fills
+        # them with NaN while the backward may still be running on s
+        junk = [torch.full((nws,), 255, dtype=torch.uint8, device="cuda")]
+        junk += [torch.full_like(t, float("nan")) for t in got]
+        s.synchronize()
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep
+        del junk

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import BF16_REL, F32_ABS_O, normwise
+from helpers import BF16_ABS_LSE, BF16_REL, F32_ABS_O, normwise
 from workloads import (DECODE_WORKLOADS, PREFILL_WORKLOADS, make_decode_inputs,
                        make_prefill_inputs)
 
@@ -24,6 +24,7 @@ def check(o, lse, o_ref, lse_ref, bf16, label):
     if bf16:
         assert normwise(o, o_ref) <= BF16_REL, label
         assert normwise(lse, lse_ref) <= BF16_REL, label
+        assert np.abs(lse - lse_ref).max() <= BF16_ABS_LSE, label
     else:
         assert np.abs(o - o_ref).max() <= F32_ABS_O, label
         assert np.abs(lse - lse_ref).max() <= F32_ABS_O, label

@@ -30,7 +30,7 @@ def test_workload_parity(ne, oracle_mod, name):
 
 
 @pytest.mark.parametrize("seed", [1, 2])
-@pytest.mark.parametrize("name", ["tiny", "cpu_model"])
+@pytest.mark.parametrize("name", ["tiny", "cpu_model", "gpu_model", "long_ctx"])
 def test_workload_parity_other_seeds(ne, oracle_mod, name, seed):
     run_case(ne, oracle_mod, WORKLOADS[name], seed=seed)
 
@@ -82,10 +82,8 @@ def test_fp32_fused_rope(ne, oracle_mod, case, causal):
 
 
 def test_head_size_128_workload(ne, oracle_mod):
-    """The head-size-128 workload at a reduced batch (the oracle's cost), same heads and
-    length."""
-    w = WORKLOADS["d128_f32"]
-    run_case(ne, oracle_mod, w.with_(B=1))
+    """The head-size-128 workload at the batch it is timed at (B = 8)."""
+    run_case(ne, oracle_mod, WORKLOADS["d128_f32"])
 
 
 def test_long_sequence_head_size_128(ne, oracle_mod):

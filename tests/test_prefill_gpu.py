@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import BF16_REL, F32_ABS_O, normwise
+from helpers import BF16_ABS_LSE, BF16_REL, F32_ABS_O, normwise
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +47,7 @@ def test_prefill_parity(ne, case, bf16):
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
     if bf16:
         assert normwise(o, o_ref) <= BF16_REL and normwise(lse, lse_ref) <= BF16_REL
+        assert np.abs(lse - lse_ref).max() <= BF16_ABS_LSE
     else:
         assert np.abs(o - o_ref).max() <= F32_ABS_O and np.abs(lse - lse_ref).max() <= F32_ABS_O
 
