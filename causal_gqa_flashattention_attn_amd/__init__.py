@@ -2,8 +2,9 @@
 
 The functions named like the C entry points (``ne_attn_fwd``, ``ne_attn_bwd``,
 ``ne_attn_fwd_ex``, ``ne_attn_bwd_ex``, ``ne_attn_bwd_dq_ex``, ``ne_attn_bwd_dkdv_ex``,
-``ne_attn_bwd_fused``, ``ne_attn_decode``, ``ne_attn_prefill``, ``ne_attn_workspace_bytes``, ``ne_attn_decode_workspace_bytes``,
-``ne_attn_bwd_workspace_bytes``, ``ne_attn_strerror``) only
+``ne_attn_bwd_fused``, ``ne_attn_bwd_noalloc``, ``ne_attn_decode``, ``ne_attn_prefill``,
+``ne_attn_workspace_bytes``, ``ne_attn_decode_workspace_bytes``, ``ne_attn_bwd_workspace_bytes``,
+``ne_attn_strerror``) only
 marshal arguments: they read sizes from tensor shapes, pass ``data_ptr()`` and the current
 HIP stream, and raise ``NeAttnError`` on a non-zero status.  All arithmetic happens in the HIP
 kernels.  PyTorch provides device memory and streams.
@@ -28,20 +29,23 @@ import os
 __all__ = [
     "NeAttnError", "library_path", "load", "lib",
     "ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused", "ne_attn_decode",
+    "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused", "ne_attn_bwd_noalloc",
+    "ne_attn_decode",
     "ne_attn_prefill", "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror", "forward", "backward", "backward_fused",
     "decode", "prefill", "workspace", "ne_attn_block_fwd", "ne_attn_block_bwd",
     "ne_attn_block_workspace_bytes", "block_forward", "block_backward",
     "NE_OK", "NE_ERR_NULL", "NE_ERR_SHAPE", "NE_ERR_UNSUPPORTED", "NE_ERR_ALIGN", "NE_ERR_HIP",
-    "NE_F32", "NE_BF16", "EXPORTED_SYMBOLS",
+    "NE_ERR_SCRATCH", "NE_F32", "NE_BF16", "EXPORTED_SYMBOLS",
 ]
 
-NE_OK, NE_ERR_NULL, NE_ERR_SHAPE, NE_ERR_UNSUPPORTED, NE_ERR_ALIGN, NE_ERR_HIP = range(6)
+(NE_OK, NE_ERR_NULL, NE_ERR_SHAPE, NE_ERR_UNSUPPORTED, NE_ERR_ALIGN, NE_ERR_HIP,
+ NE_ERR_SCRATCH) = range(7)
 NE_F32, NE_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
                     "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused",
+                    "ne_attn_bwd_noalloc",
                     "ne_attn_decode", "ne_attn_prefill", "ne_attn_workspace_bytes", "ne_attn_decode_workspace_bytes",
                     "ne_attn_bwd_workspace_bytes", "ne_attn_strerror", "ne_attn_block_fwd",
                     "ne_attn_block_bwd", "ne_attn_block_workspace_bytes")
@@ -82,8 +86,10 @@ def load():
     L.ne_attn_bwd_dq_ex.argtypes = [vp] * 8 + [i] * 7 + [f, vp]
     L.ne_attn_bwd_dkdv_ex.argtypes = [vp] * 8 + [i] * 7 + [f, vp]
     L.ne_attn_bwd_fused.argtypes = [vp] * 10 + [i] * 7 + [f, vp]
+    L.ne_attn_bwd_noalloc.argtypes = [vp] * 9 + [i] * 7 + [f, vp]
     for name in ("ne_attn_fwd", "ne_attn_bwd", "ne_attn_fwd_ex", "ne_attn_bwd_ex",
-                 "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused"):
+                 "ne_attn_bwd_dq_ex", "ne_attn_bwd_dkdv_ex", "ne_attn_bwd_fused",
+                 "ne_attn_bwd_noalloc"):
         getattr(L, name).restype = i
     L.ne_attn_workspace_bytes.argtypes = [i] * 6 + [f]
     L.ne_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -236,9 +242,9 @@ def ne_attn_fwd(q, k, v, o, lse, causal: bool = True, stream=None):
     _raise(rc, "ne_attn_fwd")
 
 
-def _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, ws, rope_base=None):
+def _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, ws, rope_base=None, need_ws=True):
     """rope_base None: ws is the float32 delta workspace of ne_attn_bwd; otherwise the
-    workspace of the _ex entry points for that RoPE setting."""
+    workspace of the _ex entry points for that RoPE setting.  need_ws False: no workspace."""
     torch = _torch()
     B, Hq, Hkv, T, D = _dims(q, k, v)
     for name, t in (("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk),
@@ -251,14 +257,18 @@ def _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, ws, rope_base=None):
         raise ValueError("dk, dv must match k")
     if tuple(lse.shape) != (B, Hq, T) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [B, Hq, T]")
-    if rope_base is None:
+    ts = dict(q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv)
+    if not need_ws:
+        pass
+    elif rope_base is None:
         if ws.dtype != torch.float32 or ws.numel() * 4 < ne_attn_bwd_workspace_bytes(B, Hq, T):
             raise ValueError("delta_ws must be float32 with at least B*Hq*T elements")
+        ts["ws"] = ws
     else:
         _ws_check(ws, ne_attn_workspace_bytes(B, Hq, Hkv, T, D, _dtype_code(q), rope_base),
                   q.device)
-    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse, dO=dO, dq=dq, dk=dk, dv=dv, ws=ws),
-                   q.device)
+        ts["ws"] = ws
+    _check_tensors(ts, q.device)
     return B, Hq, Hkv, T, D
 
 
@@ -283,6 +293,21 @@ def ne_attn_bwd_fused(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal: bool =
                                       int(bool(causal)), _dtype_code(q), float(rope_base),
                                       _stream(stream, q.device))
     _raise(rc, "ne_attn_bwd_fused")
+
+
+def ne_attn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, causal: bool = True,
+                        rope_base: float = 0.0, stream=None):
+    """ne_attn_bwd_ex with the library's static scratch instead of a workspace: allocates
+    nothing; calls that overlap on one GPU must be ordered by the caller."""
+    torch = _torch()
+    B, Hq, Hkv, T, D = _bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, None, rope_base,
+                                   need_ws=False)
+    with torch.cuda.device(q.device):
+        rc = load().ne_attn_bwd_noalloc(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
+                                        _p(dk), _p(dv), B, Hq, Hkv, T, D, int(bool(causal)),
+                                        _dtype_code(q), float(rope_base),
+                                        _stream(stream, q.device))
+    _raise(rc, "ne_attn_bwd_noalloc")
 
 
 def ne_attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal: bool = True, stream=None):

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/ne_attn.h"
 #include "attn_kernels.hpp"
@@ -202,6 +203,48 @@ int bwd_fused_impl(const void *q, const void *k, const void *v, const void *o, c
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
+// Scratch of ne_attn_bwd_noalloc: a file-scope device array (each device that runs it holds its
+// own copy until the process ends) standing in for the workspace of ne_attn_bwd_ex.  In host
+// code `scratch` names a host-side stand-in, never the device memory: kernels get the address
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex scratch_mu;
+void *scratch_dev[64] = {};
+
+// Device address of the current device's copy of `scratch`, looked up once per device (with
+// that device current) and kept; nullptr if the lookup fails.
+void *scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_dev[dev] = p;
+    }
+    return scratch_dev[dev];
+}
+
+int bwd_noalloc_impl(const void *q, const void *k, const void *v, const void *o,
+                     const float *lse, const void *dO, void *dq, void *dk, void *dv, int B, int Hq,
+                     int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                     hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return NE_ERR_NULL;
+    ne::Shape s;
+    const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
+    if (rc != NE_OK) return rc;
+    if (ws_layout(s, dtype).total > kNoAllocScratchBytes) return NE_ERR_SCRATCH;
+    if (any_misaligned({q, k, v, o, lse, dO, dq, dk, dv})) return NE_ERR_ALIGN;
+    void *ws = scratch_ptr();
+    if (!ws) return NE_ERR_HIP;
+    // Every byte of the scratch that the passes read is written first by the dQ pass (delta,
+    // rotated q) or the RoPE pre-pass before it (rotated k): nothing needs clearing.
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, ws, B, Hq, Hkv, T, D, causal, dtype,
+                    rope_base, stream);
+}
+
 // Attention sub-block workspace (float32): what the forward saves for the backward, then
 // scratch of either pass, each region 256-aligned.
 struct BlkLayout {
@@ -316,6 +359,14 @@ int ne_attn_bwd_dkdv_ex(const void *q, const void *k, const void *v, const float
                         hipStream_t stream) {
     return dkdv_impl(q, k, v, lse, dO, workspace, dk, dv, B, Hq, Hkv, T, D, causal, dtype,
                      rope_base, stream);
+}
+
+int ne_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                        const float *lse, const void *dO, void *dq, void *dk, void *dv, int B,
+                        int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                        hipStream_t stream) {
+    return bwd_noalloc_impl(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, T, D, causal, dtype,
+                            rope_base, stream);
 }
 
 int ne_attn_bwd_fused(const void *q, const void *k, const void *v, const void *o,
@@ -460,6 +511,7 @@ const char *ne_attn_strerror(int status) {
         case NE_ERR_UNSUPPORTED: return "unsupported configuration (D must be 32, 64 or 128, dtype NE_F32 or NE_BF16, rope_base finite and >= 0)";
         case NE_ERR_ALIGN: return "pointer not 16-byte aligned";
         case NE_ERR_HIP: return "HIP kernel launch failed";
+        case NE_ERR_SCRATCH: return "the shape needs more scratch than the library's static buffer holds (64 MiB)";
         default: return "unknown status";
     }
 }

@@ -36,7 +36,8 @@
  *
  * Errors.  Every entry point returns an ne_status.  Argument errors are detected before any
  * launch and nothing is enqueued: NE_ERR_NULL (a null pointer), NE_ERR_SHAPE (B, Hq, Hkv or T
- * below 1, Hq not a multiple of Hkv, sizes whose element count overflows), NE_ERR_UNSUPPORTED
+ * below 1, Hq not a multiple of Hkv, sizes whose element count overflows, a bf16 head -- T x D
+ * elements of one (batch, head) -- of more than 2^31 bytes), NE_ERR_UNSUPPORTED
  * (D not 32, 64 or 128, unknown dtype, negative or non-finite rope_base), NE_ERR_ALIGN (a pointer
  * not 16-byte aligned).  NE_ERR_HIP reports a failed kernel launch.  No C++ exception crosses
  * this interface.
@@ -59,7 +60,8 @@ enum ne_status {
     NE_ERR_SHAPE = 2,
     NE_ERR_UNSUPPORTED = 3,
     NE_ERR_ALIGN = 4,
-    NE_ERR_HIP = 5
+    NE_ERR_HIP = 5,
+    NE_ERR_SCRATCH = 6  /* ne_attn_bwd_noalloc: the shape needs more than its static scratch */
 };
 
 enum ne_dtype {
@@ -113,6 +115,25 @@ int ne_attn_bwd_ex(const void *q, const void *k, const void *v, const void *o,
                    const float *lse, const void *dO, void *dq, void *dk, void *dv,
                    void *workspace, int B, int Hq, int Hkv, int T, int D, int causal,
                    int dtype, float rope_base, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * or training loops, harnesses that forbid allocation): ne_attn_bwd_ex without the workspace
+ * argument.  Its scratch (delta and, with RoPE, the rotated q and k: ne_attn_workspace_bytes(...)
+ * bytes) is a static device array of 64 MiB inside the library; each GPU the call runs on
+ * holds its own copy until the process ends.  The call allocates nothing.  Its first call on a
+ * device looks up that device's copy once (hipGetSymbolAddress, which may make the runtime load
+ * the library's device code there): make that first call outside graph capture.
+ * A shape whose scratch exceeds 64 MiB returns NE_ERR_SCRATCH before any launch (bf16 with RoPE
+ * at B 16, Hq 16, Hkv 4, T 1024, D 64 needs 41 MiB).  All calls on one GPU share its array and
+ * nothing in it survives a call that matters to the next: calls that overlap on one GPU (other
+ * streams, other host threads) race on it and must be ordered by the caller.  Results are
+ * bitwise those of ne_attn_bwd_ex.  Other arguments and errors as for ne_attn_bwd_ex.
+ */
+int ne_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                        const float *lse, const void *dO, void *dq, void *dk, void *dv, int B,
+                        int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
+                        hipStream_t stream);
 
 /*
  * The two passes that ne_attn_bwd_ex runs back to back, as separate calls for callers that

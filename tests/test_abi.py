@@ -32,11 +32,11 @@ def test_library_exports_every_declared_symbol(ne):
 
 def test_strerror_covers_every_status(ne):
     seen = set()
-    for st in range(6):
+    for st in range(7):
         s = ne.ne_attn_strerror(st)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 6
+    assert len(seen) == 7
     assert ne.ne_attn_strerror(99) == "unknown status"
     assert ne.ne_attn_strerror(-1) == "unknown status"
 
@@ -340,3 +340,33 @@ def test_block_binding_checks_output_shapes(ne):
         with pytest.raises(ValueError, match=f"{name} must be"):
             ne.ne_attn_block_bwd(x, g, wqkv, wo, args["dy"], args["dx"], args["dgamma"],
                                  args["dw_qkv"], args["dw_o"], ws, Hq, Hkv, D)
+
+
+def noalloc(ne, ptrs=None, B=1, Hq=4, Hkv=2, T=64, D=32, causal=1, dtype=0, rope=0.0):
+    p = ptrs or [A] * 9
+    return ne.load().ne_attn_bwd_noalloc(*[VP(x) for x in p], B, Hq, Hkv, T, D, causal, dtype,
+                                         rope, VP(0))
+
+
+@pytest.mark.parametrize("which", range(9))
+def test_noalloc_backward_validates(ne, which):
+    p = [A] * 9
+    p[which] = 0
+    assert noalloc(ne, p) == ne.NE_ERR_NULL
+    p[which] = A + 4
+    assert noalloc(ne, p) == ne.NE_ERR_ALIGN
+    assert noalloc(ne, Hq=4, Hkv=3) == ne.NE_ERR_SHAPE
+    assert noalloc(ne, D=48) == ne.NE_ERR_UNSUPPORTED
+
+
+def test_noalloc_backward_scratch_limit(ne):
+    """Shapes whose scratch (ne_attn_workspace_bytes) exceeds the static 64 MiB are refused
+    before any launch; the largest workloads it is meant for fit."""
+    lim = 64 << 20
+    big = dict(B=64, Hq=16, Hkv=4, T=1024, D=64, dtype=1, rope=10000.0)
+    assert ne.ne_attn_workspace_bytes(64, 16, 4, 1024, 64, 1, 10000.0) > lim
+    assert noalloc(ne, **big) == ne.NE_ERR_SCRATCH
+    assert noalloc(ne, B=64, Hq=16, Hkv=4, T=1 << 15, D=64, dtype=0) == ne.NE_ERR_SCRATCH
+    for shape in [(16, 16, 4, 1024, 64, 1, 10000.0), (16, 12, 4, 512, 64, 0, 0.0),
+                  (4, 12, 4, 4096, 64, 0, 0.0), (8, 16, 4, 1024, 128, 1, 10000.0)]:
+        assert 0 < ne.ne_attn_workspace_bytes(*shape) <= lim, shape
