@@ -15,6 +15,9 @@
 //                 merged, and the split's (o / l, lse) goes to the workspace.
 //   decode_merge  per (batch, query head): log-sum-exp of the splits' lse, weighted sum of their
 //                 outputs.  Splits past lens[b] are neither computed nor read.
+// When one split covers the whole cache (Tc <= 512: 4 or 8 waves of 64 keys), the split kernel
+// writes o and lse itself and the merge launch is skipped: for short caches the step is then a
+// single launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,7 +31,8 @@ namespace {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecKeysPerWave = 64;
-constexpr int kDecSplit = kDecWaves * kDecKeysPerWave;  // keys per split
+constexpr int kDecSplit = kDecWaves * kDecKeysPerWave;  // keys per split (several splits)
+constexpr int kDecWavesOne = 8;                         // waves of a single split (Tc <= 512)
 
 struct DecArgs {
     const void *q, *k, *v;
@@ -121,8 +125,10 @@ __device__ __forceinline__ void dec_merge(DecState<E> &a, float m2, float l2, co
     a.m = mn;
 }
 
-template <int D, typename T, int GC>
-__global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
+// NW waves of 64 keys per work-group.  ONE: a single split covers the cache, so the work-group
+// writes o and lse (o = 0, lse = -inf for an empty cache) instead of its workspace entries.
+template <int D, typename T, int GC, int NW, bool ONE>
+__global__ void __launch_bounds__(64 * NW) decode_split(DecArgs a) {
     using C = DecCfg<D, T, GC>;
     constexpr int E = C::E;
     const int s = blockIdx.x;
@@ -132,8 +138,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
     const int g = y % a.Hkv;
     const int b = y / a.Hkv;
     const int len = min(max(a.lens[b], 0), a.Tc);
-    const int k0 = s * kDecSplit;
-    if (k0 >= len) return;  // past the cached length: the merge does not read this split
+    const int k0 = s * NW * kDecKeysPerWave;
+    if (!ONE && k0 >= len) return;  // past the cached length: the merge does not read this split
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int sub = lane % C::LPK, kl = lane / C::LPK;
@@ -221,7 +227,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
         }
 
     // Merge the waves in LDS (fixed order), then lanes 0 .. LPK-1 of wave 0 write the split.
-    __shared__ float red[kDecWaves][GC][D + 2];
+    __shared__ float red[NW][GC][D + 2];
     if (kl == 0)
 #pragma unroll
         for (int gi = 0; gi < GC; ++gi) {
@@ -242,7 +248,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
         t.l = red[0][gi][D + 1];
 #pragma unroll
         for (int e = 0; e < E; ++e) t.o[e] = red[0][gi][sub * E + e];
-        for (int w = 1; w < kDecWaves; ++w) {
+        for (int w = 1; w < NW; ++w) {
             float o2[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) o2[e] = red[w][gi][sub * E + e];
@@ -251,11 +257,19 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_split(DecArgs a) {
         const size_t bh = (size_t)b * a.Hq + h0 + gi;
         const size_t ps = (size_t)s * a.B * a.Hq + bh;
         const float inv = t.l > 0.f ? 1.0f / t.l : 0.f;
-        float *po = a.part_o + ps * D + sub * E;
+        const float ls = t.l > 0.f ? (t.m + __log2f(t.l)) * kLn2 : -INFINITY;
+        if constexpr (ONE) {
+            T *orow = static_cast<T *>(a.o) + bh * D + sub * E;
 #pragma unroll
-        for (int e = 0; e < E; e += 4) *reinterpret_cast<f32x4 *>(po + e) =
-            f32x4{t.o[e] * inv, t.o[e + 1] * inv, t.o[e + 2] * inv, t.o[e + 3] * inv};
-        if (sub == 0) a.part_lse[ps] = t.l > 0.f ? (t.m + __log2f(t.l)) * kLn2 : -INFINITY;
+            for (int e = 0; e < E; ++e) orow[e] = to_elt<T>(t.o[e] * inv);
+            if (sub == 0) a.lse[bh] = ls;
+        } else {
+            float *po = a.part_o + ps * D + sub * E;
+#pragma unroll
+            for (int e = 0; e < E; e += 4) *reinterpret_cast<f32x4 *>(po + e) =
+                f32x4{t.o[e] * inv, t.o[e + 1] * inv, t.o[e + 2] * inv, t.o[e + 3] * inv};
+            if (sub == 0) a.part_lse[ps] = ls;
+        }
     }
 }
 
@@ -300,19 +314,31 @@ __global__ void __launch_bounds__(64) decode_merge(DecArgs a) {
     if (lane == 0) a.lse[bh] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
+template <int D, typename T, int NW, bool ONE>
+const void *pick_split(int gc) {
+    return gc == 1   ? (const void *)decode_split<D, T, 1, NW, ONE>
+           : gc == 2 ? (const void *)decode_split<D, T, 2, NW, ONE>
+           : gc == 4 ? (const void *)decode_split<D, T, 4, NW, ONE>
+                     : (const void *)decode_split<D, T, 8, NW, ONE>;
+}
+
 template <int D, typename T>
 hipError_t launch_decode_t(DecArgs &a, hipStream_t st) {
     // Query heads per work-group: the whole group when it is small, else chunks of 8.
     const int gc = a.G <= 1 ? 1 : a.G <= 2 ? 2 : a.G <= 4 ? 4 : 8;
     a.nhc = (a.G + gc - 1) / gc;
-    const void *fn = gc == 1   ? (const void *)decode_split<D, T, 1>
-                     : gc == 2 ? (const void *)decode_split<D, T, 2>
-                     : gc == 4 ? (const void *)decode_split<D, T, 4>
-                               : (const void *)decode_split<D, T, 8>;
     void *params[] = {&a};
     const long long gy = (long long)a.B * a.Hkv * a.nhc;
     if (gy > 65535) return hipErrorInvalidValue;
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)a.nsplit, (unsigned)gy), dim3(64 * kDecWaves),
+    // A cache of at most 512 keys is one split (4 or 8 waves): no merge.
+    if (a.Tc <= kDecWavesOne * kDecKeysPerWave) {
+        const int nw = a.Tc <= kDecSplit ? kDecWaves : kDecWavesOne;
+        const void *fn = nw == kDecWaves ? pick_split<D, T, kDecWaves, true>(gc)
+                                         : pick_split<D, T, kDecWavesOne, true>(gc);
+        return hipLaunchKernel(fn, dim3(1, (unsigned)gy), dim3(64 * nw), params, 0, st);
+    }
+    hipError_t e = hipLaunchKernel(pick_split<D, T, kDecWaves, false>(gc),
+                                   dim3((unsigned)a.nsplit, (unsigned)gy), dim3(64 * kDecWaves),
                                    params, 0, st);
     if (e != hipSuccess) return e;
     const long long nbh = (long long)a.B * a.Hq;
