@@ -8,8 +8,10 @@
 //   o = attention(q, k, v)    (the library's causal GQA forward, RoPE in the kernel)
 //   y = x + o Wo              (o as rows [B T][Hq D], Wo [Hq D][C])
 //
-// The products are plain GEMMs and go to rocBLAS; the row-wise RMSNorm, the head (un)packing
-// and the attention are the library's own kernels.  All matrices are row-major.
+// The products are plain GEMMs and go to rocBLAS; the row-wise RMSNorm and the attention are the
+// library's own kernels, the attention reading q, k, v from the projection rows and writing o
+// (and the gradients) as rows in place, through its strided layouts.  All matrices are
+// row-major.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
@@ -102,31 +104,6 @@ __global__ void __launch_bounds__(256) colsum_f32(const float *part, float *out,
     }
 }
 
-// Rows [B T][W] (W = heads_total D) <-> heads [B][H][T][D] for the heads h0 .. h0 + H - 1 of a
-// row; to_heads copies rows into heads, otherwise heads into rows.  One thread per 4 floats.
-__global__ void __launch_bounds__(256) rows_heads_f32(float *rows_, float *heads, int B, int T,
-                                                      int W, int h0, int H, int D, int to_heads) {
-    const long long n = (long long)B * H * T * (D / 4);
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
-         i += (long long)gridDim.x * 256) {
-        const int c = 4 * (int)(i % (D / 4));
-        long long j = i / (D / 4);
-        const int t = (int)(j % T);
-        j /= T;
-        const int h = (int)(j % H);
-        const int b = (int)(j / H);
-        float *hp = heads + (((size_t)b * H + h) * T + t) * D + c;
-        float *rp = rows_ + ((size_t)b * T + t) * W + (size_t)(h0 + h) * D + c;
-        if (to_heads) st4(hp, ld4(rp));
-        else st4(rp, ld4(hp));
-    }
-}
-
-unsigned grid_for(long long n) {
-    const long long g = (n + 255) / 256;
-    return (unsigned)(g < 65536 ? (g > 0 ? g : 1) : 65536);
-}
-
 }  // namespace
 
 namespace {
@@ -190,14 +167,6 @@ hipError_t launch_rmsnorm_bwd(const float *x, const float *gamma, const float *r
     void *q[] = {&part, &dgamma, &nb, &C};
     return hipLaunchKernel((const void *)colsum_f32, dim3((unsigned)((C + 31) / 32)), dim3(256),
                            q, 0, st);
-}
-
-hipError_t launch_rows_heads(float *rows_, float *heads, int B, int T, int W, int h0, int H,
-                             int D, bool to_heads, hipStream_t st) {
-    int th = to_heads ? 1 : 0;
-    void *p[] = {&rows_, &heads, &B, &T, &W, &h0, &H, &D, &th};
-    return hipLaunchKernel((const void *)rows_heads_f32,
-                           dim3(grid_for((long long)B * H * T * (D / 4))), dim3(256), p, 0, st);
 }
 
 }  // namespace ne

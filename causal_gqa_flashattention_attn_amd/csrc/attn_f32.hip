@@ -106,7 +106,16 @@ struct Args {
     float qscale;      // scale * log2(e)
     float scale;       // 1 / sqrt(D)
     RopeArgs rope;
+    TLays L;           // tensor layouts
 };
+
+// First element of head h of batch b in a tensor of layout l.
+__device__ __forceinline__ const float *head_at(const float *p, const TLay &l, int b, int h) {
+    return p + b * l.sb + (size_t)h * l.sh;
+}
+__device__ __forceinline__ float *head_at(float *p, const TLay &l, int b, int h) {
+    return p + b * l.sb + (size_t)h * l.sh;
+}
 
 struct QTile {
     int b, g, h, qt, r0;  // r0: first query row of this wave
@@ -164,16 +173,18 @@ struct KVStager {
     using C = Cfg<D>;
     f32x4 k[C::MAXC], v[C::MAXC];
 
-    __device__ __forceinline__ void load(const float *kg, const float *vg, int tile, int T,
-                                         int wave, int nw, int lane) {
+    // kg, vg: the heads' first rows; ks, vs: their row strides (elements).
+    __device__ __forceinline__ void load(const float *kg, const float *vg, int ks, int vs,
+                                         int tile, int T, int wave, int nw,
+                                         int lane) {
         const int c4 = 4 * (lane % C::C4);
 #pragma unroll
         for (int i = 0; i < C::MAXC; ++i) {
             const int c = wave + i * nw;
             if (c < C::CH) {
                 const int row = min(tile * 32 + c * C::RPC + lane / C::C4, T - 1);
-                k[i] = ld4(kg + (size_t)row * D + c4);
-                v[i] = ld4(vg + (size_t)row * D + c4);
+                k[i] = ld4(kg + row * ks + c4);
+                v[i] = ld4(vg + row * vs + c4);
             }
         }
     }
@@ -195,11 +206,13 @@ struct KVStager {
 };
 
 // This lane's query row, columns NS*half .. NS*half+NS-1, scaled; rotated first with RoPE.
+// base: the head's first row; rs: the row stride (elements).
 template <int D, bool ROPE>
-__device__ __forceinline__ void load_row_half(float (&dst)[Cfg<D>::NS], const float *base, int row,
-                                             int T, int half, float mul, const RopeArgs &rp) {
+__device__ __forceinline__ void load_row_half(float (&dst)[Cfg<D>::NS], const float *base,
+                                             int rs, int row, int T, int half, float mul,
+                                             const RopeArgs &rp) {
     using C = Cfg<D>;
-    const float *src = base + (size_t)min(row, T - 1) * D + C::NS * half;
+    const float *src = base + min(row, T - 1) * rs + C::NS * half;
 #pragma unroll
     for (int c = 0; c < C::NS / 4; ++c) {
         f32x4 t = ld4(src + 4 * c);
@@ -274,11 +287,12 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     const int qrow = c.r0 + col;
     const int p0 = c.r0 + qo;  // position of the wave's first row
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
-    const float *kg = a.k + bg * Tk * D;
-    const float *vg = a.v + bg * Tk * D;
+    const float *kg = head_at(a.k, a.L.k, c.b, c.g);
+    const float *vg = head_at(a.v, a.L.v, c.b, c.g);
 
     float qr[C::NS];
-    load_row_half<D, ROPE>(qr, a.q + bh * T * D, qrow, T, half, a.qscale, a.rope);
+    load_row_half<D, ROPE>(qr, head_at(a.q, a.L.q, c.b, c.h), a.L.q.st, qrow, T, half, a.qscale,
+                           a.rope);
 
     f32x16 acc[C::ND];
 #pragma unroll
@@ -290,13 +304,13 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     const int ntiles = CAUSAL ? (wg_end - 1 + qo) / 32 + 1 : (Tk + 31) / 32;
 
     KVStager<D> stg;
-    stg.load(kg, vg, 0, Tk, wave, nw, lane);
+    stg.load(kg, vg, a.L.k.st, a.L.v.st, 0, Tk, wave, nw, lane);
     stg.store(sK[0], sV[0], 0, Tk, wave, nw, lane);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
         const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, Tk, wave, nw, lane);
+        if (more) stg.load(kg, vg, a.L.k.st, a.L.v.st, j + 1, Tk, wave, nw, lane);
         const int k0 = j * 32;
         if (c.r0 < T && (!CAUSAL || k0 <= p0 + 31)) {
             f32x16 s = scores_t<D>(sK[buf], qr, col, half);
@@ -332,7 +346,7 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     l += swap_halves(l);
     if (qrow < T) {
         const float inv = 1.0f / l;
-        float *orow = a.out_o + (bh * T + qrow) * D;
+        float *orow = head_at(a.out_o, a.L.o, c.b, c.h) + qrow * a.L.o.st;
 #pragma unroll
         for (int dd = 0; dd < C::ND; ++dd)
 #pragma unroll
@@ -369,11 +383,12 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
     const int T = a.T;
     const int qrow = c.r0 + col;
     const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
-    const float *kg = a.k + bg * T * D;
-    const float *vg = a.v + bg * T * D;
+    const float *kg = head_at(a.k, a.L.k, c.b, c.g);
+    const float *vg = head_at(a.v, a.L.v, c.b, c.g);
 
     float qr[C::NS], dor[C::NS];
-    load_row_half<D, ROPE>(qr, a.q + bh * T * D, qrow, T, half, ROPE ? 1.0f : a.qscale, a.rope);
+    load_row_half<D, ROPE>(qr, head_at(a.q, a.L.q, c.b, c.h), a.L.q.st, qrow, T, half,
+                           ROPE ? 1.0f : a.qscale, a.rope);
     if (ROPE) {  // each query row is loaded by exactly one wave: keep its rotation, then scale
         if (qrow < T) {
 #pragma unroll
@@ -384,13 +399,15 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
 #pragma unroll
         for (int i = 0; i < C::NS; ++i) qr[i] *= a.qscale;
     }
-    load_row_half<D, false>(dor, a.dO + bh * T * D, qrow, T, half, 1.0f, a.rope);
+    load_row_half<D, false>(dor, head_at(a.dO, a.L.dO, c.b, c.h), a.L.dO.st, qrow, T, half, 1.0f,
+                            a.rope);
 
     // delta_i = sum_d dO_id o_id over this row; written once per row for the dK/dV pass.
     float delta;
     {
         float orow[C::NS];
-        load_row_half<D, false>(orow, a.o + bh * T * D, qrow, T, half, 1.0f, a.rope);
+        load_row_half<D, false>(orow, head_at(a.o, a.L.o, c.b, c.h), a.L.o.st, qrow, T, half, 1.0f,
+                                a.rope);
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < C::NS; ++i) part += dor[i] * orow[i];
@@ -414,13 +431,13 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
     const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
 
     KVStager<D> stg;
-    stg.load(kg, vg, 0, T, wave, nw, lane);
+    stg.load(kg, vg, a.L.k.st, a.L.v.st, 0, T, wave, nw, lane);
     stg.store(sK[0], sV[0], 0, T, wave, nw, lane);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
         const bool more = j + 1 < ntiles;
-        if (more) stg.load(kg, vg, j + 1, T, wave, nw, lane);
+        if (more) stg.load(kg, vg, a.L.k.st, a.L.v.st, j + 1, T, wave, nw, lane);
         const int k0 = j * 32;
         if (c.r0 < T && (!CAUSAL || k0 <= c.r0 + 31)) {
             f32x16 p = scores_t<D>(sK[buf], qr, col, half);
@@ -443,7 +460,7 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
     }
 
     if (qrow < T) {
-        float *drow = a.dq + (bh * T + qrow) * D;
+        float *drow = head_at(a.dq, a.L.dq, c.b, c.h) + qrow * a.L.dq.st;
 #pragma unroll
         for (int dd = 0; dd < C::ND; ++dd)
 #pragma unroll
@@ -501,10 +518,20 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
     const int T = a.T;
     const size_t bg = (size_t)b * a.Hkv + g;
     const int krow = kb * 32 + col;
+    // The single-pass backward only runs on contiguous tensors: its layouts follow from the
+    // shape, which spares the scalar registers strides would hold through its loop.
+    const TLay Lq = FUSED ? contiguous_lay(a.Hq, T, D) : a.L.q;
+    const TLay Lk = FUSED ? contiguous_lay(a.Hkv, T, D) : a.L.k;
+    const TLay Lv = FUSED ? contiguous_lay(a.Hkv, T, D) : a.L.v;
+    const TLay LdO = FUSED ? contiguous_lay(a.Hq, T, D) : a.L.dO;
+    const TLay Ldq = FUSED ? contiguous_lay(a.Hq, T, D) : a.L.dq;
+    const TLay Ldk = FUSED ? contiguous_lay(a.Hkv, T, D) : a.L.dk;
+    const TLay Ldv = FUSED ? contiguous_lay(a.Hkv, T, D) : a.L.dv;
 
     float kr[C::NS], vr[C::NS];
-    load_row_half<D, false>(kr, a.k + bg * T * D, krow, T, half, a.qscale, a.rope);
-    load_row_half<D, false>(vr, a.v + bg * T * D, krow, T, half, 1.0f, a.rope);
+    load_row_half<D, false>(kr, head_at(a.k, Lk, b, g), Lk.st, krow, T, half, a.qscale,
+                            a.rope);
+    load_row_half<D, false>(vr, head_at(a.v, Lv, b, g), Lv.st, krow, T, half, 1.0f, a.rope);
 
     f32x16 dk[C::ND], dv[C::ND];
 #pragma unroll
@@ -527,7 +554,8 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
             const int r = idx / C::C4, cc = 4 * (idx % C::C4);
             const int row = kb * 32 + r;
             st4(sKt + r * C::LD + cc,
-                row < T ? ld4(a.k + (bg * T + row) * D + cc) : f32x4{0.f, 0.f, 0.f, 0.f});
+                row < T ? ld4(head_at(a.k, Lk, b, g) + row * Lk.st + cc)
+                        : f32x4{0.f, 0.f, 0.f, 0.f});
         }
         __syncthreads();
     }
@@ -540,8 +568,8 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
         const int hh = it / per_head;
         const int i = i0 + it % per_head;
         const size_t bh = (size_t)b * a.Hq + (size_t)g * a.G + hh;
-        const float *qh = a.q + bh * T * D;
-        const float *doh = a.dO + bh * T * D;
+        const float *qh = head_at(a.q, Lq, b, g * a.G + hh);
+        const float *doh = head_at(a.dO, LdO, b, g * a.G + hh);
         // Only this wave reads its staging area, so ordering within the wave is all that is
         // needed between the previous item's reads and these writes.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -550,8 +578,8 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
 #pragma unroll
             for (int ch = 0; ch < C::CH; ++ch) {
                 const int row = min(i * 32 + ch * C::RPC + lane / C::C4, T - 1);
-                tq[ch] = ld4(qh + (size_t)row * D + c4);
-                td[ch] = ld4(doh + (size_t)row * D + c4);
+                tq[ch] = ld4(qh + row * Lq.st + c4);
+                td[ch] = ld4(doh + row * LdO.st + c4);
             }
             float lsev = 0.f, dlv = 0.f;
             const int lrow = i * 32 + (lane & 31);
@@ -622,14 +650,14 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
                     aq[dd] = mfma32(av, sKt[key * C::LD + dd * 32 + col], aq[dd]);
             }
             // Register v holds query acc_row(v, half), head column dd * 32 + col.
-            float *dqh = a.dq + bh * T * D;
+            float *dqh = head_at(a.dq, Ldq, b, g * a.G + hh);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int qrow = i * 32 + acc_row(v, half);
                 if (qrow < T)
 #pragma unroll
                     for (int dd = 0; dd < C::ND; ++dd)
-                        unsafeAtomicAdd(dqh + (size_t)qrow * D + dd * 32 + col, aq[dd][v] * a.scale);
+                        unsafeAtomicAdd(dqh + qrow * Ldq.st + dd * 32 + col, aq[dd][v] * a.scale);
             }
         }
     }
@@ -661,9 +689,9 @@ __device__ __forceinline__ void dkdv_block(const Args &a, int b, int g, int kb, 
         if (row < T) {
             if (t == 0) {
                 if (ROPE) sum = rope4<D>(sum, row, cc, a.rope, true);
-                st4(a.dk + (bg * T + row) * D + cc, sum);
+                st4(head_at(a.dk, Ldk, b, g) + row * Ldk.st + cc, sum);
             } else {
-                st4(a.dv + (bg * T + row) * D + cc, sum);
+                st4(head_at(a.dv, Ldv, b, g) + row * Ldv.st + cc, sum);
             }
         }
     }
@@ -735,9 +763,10 @@ __global__ void __launch_bounds__(256) delta_zero_f32(const float *o, const floa
 // head) it visits.  The attention kernels that stream a tensor through LDS many times read this
 // rotated copy instead of rotating every staged tile again.
 // INV: the transpose R^T (a gradient rotated back), in place when x == y.
+// x: rows of head h of batch b at x + b xl.sb + h xl.sh + t xl.st (H heads per batch).
 template <int D, bool INV>
 __global__ void __launch_bounds__(256) rope_rows_f32(const float *x, float *y, long long nbh, int T,
-                                                     RopeTurns rt) {
+                                                     RopeTurns rt, TLay xl, int H) {
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= T * (D / 4)) return;
     const int t = idx / (D / 4);
@@ -750,7 +779,7 @@ __global__ void __launch_bounds__(256) rope_rows_f32(const float *x, float *y, l
     }
     for (long long bh = blockIdx.y; bh < nbh; bh += gridDim.y) {
         const size_t off = ((size_t)bh * T + t) * D + c;
-        const f32x4 v = ld4(x + off);
+        const f32x4 v = ld4(x + (bh / H) * xl.sb + (size_t)(bh % H) * xl.sh + t * xl.st + c);
         if (INV)
             st4(y + off, f32x4{v[0] * cs[0] + v[1] * sn[0], v[1] * cs[0] - v[0] * sn[0],
                                v[2] * cs[1] + v[3] * sn[1], v[3] * cs[1] - v[2] * sn[1]});
@@ -773,6 +802,13 @@ Args make_args(const Shape &s) {
     a.qscale = (float)(1.4426950408889634 / sqrt((double)s.D));
     a.rope.on = s.rope_base > 0.f;
     a.rope.log2_base = a.rope.on ? log2((double)s.rope_base) : 0.0;
+    if (s.lay) {
+        a.L = *s.lay;
+    } else {
+        const TLay lq = contiguous_lay(s.Hq, s.T, s.D), lk = contiguous_lay(s.Hkv, a.Tk, s.D);
+        const TLay lkb = contiguous_lay(s.Hkv, s.T, s.D);
+        a.L = TLays{lq, lk, lk, lq, lq, lq, lkb, lkb};
+    }
     return a;
 }
 
@@ -966,10 +1002,12 @@ hipError_t launch_bwd_fused_f32(const Shape &s, const float *q, const float *k, 
 }
 
 hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long rows,
-                           hipStream_t st, bool inv) {
+                           hipStream_t st, bool inv, const TLay *xl_, int H) {
     RopeTurns rt = rope_turns(s);
     long long nbh = rows / s.T;
     int T = s.T;
+    TLay xl = xl_ ? *xl_ : contiguous_lay(1, T, s.D);
+    if (!xl_) H = 1;
     const long long per_pos = (long long)T * (s.D / 4);
     const unsigned gx = (unsigned)((per_pos + 255) / 256);
     const long long gy = std::max(1LL, std::min(nbh, std::max(nbh / 8, 2048LL / (long long)gx)));
@@ -979,7 +1017,7 @@ hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long r
                          : (s.D == 128  ? (const void *)rope_rows_f32<128, false>
                             : s.D == 64 ? (const void *)rope_rows_f32<64, false>
                                         : (const void *)rope_rows_f32<32, false>);
-    void *params[] = {&x, &y, &nbh, &T, &rt};
+    void *params[] = {&x, &y, &nbh, &T, &rt, &xl, &H};
     return hipLaunchKernel(fn, dim3(gx, (unsigned)std::min(gy, 65535LL)), dim3(256), params, 0, st);
 }
 

@@ -7,6 +7,28 @@
 
 namespace ne {
 
+// Where the rows of a [B][H][T][D] tensor live: element (b, h, t, d) at b sb + h sh + t st + d
+// (elements).  Contiguous: sb = H T D, sh = T D, st = D.  The attention sub-block reads q, k, v
+// straight from the rows of its projection ([B T][W]: sb = T W, sh = D, st = W) and writes o,
+// dq, dk, dv as rows.
+// Element (b, h, t, d) of a tensor sits at b sb + h sh + t st + d (d contiguous).  sh is at most
+// T D <= 2^31 (contiguous heads), st at most the width of a row of the attention sub-block's
+// projections, so both fit 32 bits; they are kept narrow to spare scalar registers.
+struct TLay {
+    long long sb;
+    unsigned sh;
+    int st;
+};
+// Layouts of every tensor the float32 kernels read or write (lse and delta are always
+// contiguous [B][Hq][T]).
+struct TLays {
+    TLay q, k, v, o, dO, dq, dk, dv;
+};
+
+__host__ __device__ inline TLay contiguous_lay(int H, int T, int D) {
+    return TLay{(long long)H * T * D, (unsigned)T * (unsigned)D, D};
+}
+
 // One problem instance.  Element offsets are computed in 64-bit inside the kernels.
 struct Shape {
     int B, Hq, Hkv, T, D, G;  // G = Hq / Hkv
@@ -15,6 +37,8 @@ struct Shape {
     // Forward only: keys/values of length Tk >= T, query row i at position i + Tk - T (a chunk
     // of T new queries against a cache).  0: Tk = T.
     int Tk = 0;
+    // float32 kernels: tensor layouts; null: all contiguous.
+    const TLays *lay = nullptr;
 };
 
 // Work-group composition of the query-tile kernels (forward and dQ): each work-group serves
@@ -97,8 +121,6 @@ int rmsnorm_bwd_blocks(long long rows);
 hipError_t launch_rmsnorm_bwd(const float *x, const float *gamma, const float *rstd,
                               const float *dxn, const float *dy, float *dx, float *part,
                               float *dgamma, long long rows, int C, hipStream_t st);
-hipError_t launch_rows_heads(float *rows_, float *heads, int B, int T, int W, int h0, int H,
-                             int D, bool to_heads, hipStream_t st);
 
 // bfloat16 variants: tensors are bf16 (passed untyped), lse and delta fp32.
 hipError_t launch_fwd_bf16(const Shape &s, const void *q, const void *k, const void *v, void *o,
@@ -123,9 +145,10 @@ inline RopeTurns rope_turns(const Shape &s) {
     return r;
 }
 
-// RoPE applied to a whole tensor [rows / T][T][D] (s.rope_base > 0), x -> y.
+// RoPE applied to a whole tensor [rows / T][T][D] (s.rope_base > 0), x -> y; y contiguous, x
+// in layout xl over H heads (null: contiguous).
 hipError_t launch_rope_f32(const Shape &s, const float *x, float *y, long long rows,
-                           hipStream_t st, bool inv = false);
+                           hipStream_t st, bool inv = false, const TLay *xl = nullptr, int H = 1);
 hipError_t launch_rope_bf16(const Shape &s, const void *x, void *y, long long rows,
                             hipStream_t st);
 

@@ -75,16 +75,23 @@ WsLayout ws_layout(const ne::Shape &s, int dtype) {
     return w;
 }
 
+// Rotates the keys (or queries) x of H heads into the contiguous copy y; xl: x's layout (fp32
+// only; null: contiguous).
 hipError_t launch_rope(const ne::Shape &s, int dtype, const void *x, void *y, long long rows,
-                       hipStream_t stream) {
+                       hipStream_t stream, const ne::TLay *xl = nullptr, int H = 1) {
     return dtype == NE_BF16 ? ne::launch_rope_bf16(s, x, y, rows, stream)
                             : ne::launch_rope_f32(s, static_cast<const float *>(x),
-                                                  static_cast<float *>(y), rows, stream);
+                                                  static_cast<float *>(y), rows, stream, false,
+                                                  xl, H);
 }
 
+// The entry points below take an optional `lay` (float32 only): the layouts of the caller's
+// tensors, for the attention sub-block, which keeps q, k, v, o and the gradients as rows of its
+// projections (null: every tensor contiguous).  Copies the kernels make in the workspace
+// (rotated k and q) are contiguous, and `lay` is adjusted to say so.
 int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, void *ws, int B,
              int Hq, int Hkv, int T, int D, int causal, int dtype, float rope_base,
-             hipStream_t stream) {
+             hipStream_t stream, const ne::TLays *lay = nullptr) {
     if (!q || !k || !v || !o || !lse) return NE_ERR_NULL;
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
@@ -92,13 +99,20 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, v
     const bool rope = s.rope_base > 0.f;
     if (rope && !ws) return NE_ERR_NULL;
     if (any_misaligned({q, k, v, o, lse}) || (rope && misaligned(ws))) return NE_ERR_ALIGN;
+    ne::TLays L{};
+    if (lay) {
+        L = *lay;
+        s.lay = &L;
+    }
     const void *kk = k;
     if (rope) {
         // Keys rotated once into the workspace; each query row is rotated as it is loaded.
         void *kr = static_cast<char *>(ws) + ws_layout(s, dtype).kr;
-        if (launch_rope(s, dtype, k, kr, (long long)B * Hkv * T, stream) != hipSuccess)
+        if (launch_rope(s, dtype, k, kr, (long long)B * Hkv * T, stream, lay ? &lay->k : nullptr,
+                        Hkv) != hipSuccess)
             return NE_ERR_HIP;
         kk = kr;
+        L.k = ne::contiguous_lay(Hkv, T, D);
     }
     const hipError_t e =
         dtype == NE_BF16
@@ -111,13 +125,18 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, v
 
 int dq_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
             const void *dO, void *dq, void *ws, int B, int Hq, int Hkv, int T, int D, int causal,
-            int dtype, float rope_base, hipStream_t stream) {
+            int dtype, float rope_base, hipStream_t stream, const ne::TLays *lay = nullptr) {
     if (!q || !k || !v || !o || !lse || !dO || !dq || !ws) return NE_ERR_NULL;
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
     if (any_misaligned({q, k, v, o, lse, dO, dq, ws})) return NE_ERR_ALIGN;
     const WsLayout L = ws_layout(s, dtype);
+    ne::TLays TL{};
+    if (lay) {
+        TL = *lay;
+        s.lay = &TL;
+    }
     float *delta = static_cast<float *>(ws);
     const void *kk = k;
     void *qr = nullptr;
@@ -125,9 +144,11 @@ int dq_impl(const void *q, const void *k, const void *v, const void *o, const fl
         // Keys rotated once into the workspace for both passes; the dQ pass rotates each query
         // row as it loads it and leaves the rotated rows in the workspace for the dK/dV pass.
         void *kr = static_cast<char *>(ws) + L.kr;
-        if (launch_rope(s, dtype, k, kr, (long long)B * Hkv * T, stream) != hipSuccess)
+        if (launch_rope(s, dtype, k, kr, (long long)B * Hkv * T, stream, lay ? &lay->k : nullptr,
+                        Hkv) != hipSuccess)
             return NE_ERR_HIP;
         kk = kr;
+        TL.k = ne::contiguous_lay(Hkv, T, D);
         qr = static_cast<char *>(ws) + L.qr;
     }
     const hipError_t e =
@@ -142,18 +163,26 @@ int dq_impl(const void *q, const void *k, const void *v, const void *o, const fl
 
 int dkdv_impl(const void *q, const void *k, const void *v, const float *lse, const void *dO,
               const void *ws, void *dk, void *dv, int B, int Hq, int Hkv, int T, int D,
-              int causal, int dtype, float rope_base, hipStream_t stream) {
+              int causal, int dtype, float rope_base, hipStream_t stream,
+              const ne::TLays *lay = nullptr) {
     if (!q || !k || !v || !lse || !dO || !ws || !dk || !dv) return NE_ERR_NULL;
     ne::Shape s;
     const int rc = check_shape(B, Hq, Hkv, T, D, causal, dtype, rope_base, s);
     if (rc != NE_OK) return rc;
     if (any_misaligned({q, k, v, lse, dO, ws, dk, dv})) return NE_ERR_ALIGN;
     const WsLayout L = ws_layout(s, dtype);
+    ne::TLays TL{};
+    if (lay) {
+        TL = *lay;
+        s.lay = &TL;
+    }
     const float *delta = static_cast<const float *>(ws);
     const void *qq = q, *kk = k;
     if (s.rope_base > 0.f) {  // rotated by the dQ pass
         qq = static_cast<const char *>(ws) + L.qr;
         kk = static_cast<const char *>(ws) + L.kr;
+        TL.q = ne::contiguous_lay(Hq, T, D);
+        TL.k = ne::contiguous_lay(Hkv, T, D);
     }
     const hipError_t e =
         dtype == NE_BF16
@@ -167,7 +196,8 @@ int dkdv_impl(const void *q, const void *k, const void *v, const float *lse, con
 
 int bwd_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
              const void *dO, void *dq, void *dk, void *dv, void *ws, int B, int Hq, int Hkv,
-             int T, int D, int causal, int dtype, float rope_base, hipStream_t stream) {
+             int T, int D, int causal, int dtype, float rope_base, hipStream_t stream,
+             const ne::TLays *lay = nullptr) {
     // Check everything (including dk, dv) before the first pass is enqueued.
     if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !ws) return NE_ERR_NULL;
     ne::Shape s;
@@ -175,10 +205,10 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     if (rc != NE_OK) return rc;
     if (any_misaligned({q, k, v, o, lse, dO, dq, dk, dv, ws})) return NE_ERR_ALIGN;
     const int r1 = dq_impl(q, k, v, o, lse, dO, dq, ws, B, Hq, Hkv, T, D, causal, dtype,
-                           rope_base, stream);
+                           rope_base, stream, lay);
     if (r1 != NE_OK) return r1;
     return dkdv_impl(q, k, v, lse, dO, ws, dk, dv, B, Hq, Hkv, T, D, causal, dtype, rope_base,
-                     stream);
+                     stream, lay);
 }
 
 int bwd_fused_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -245,37 +275,40 @@ int bwd_noalloc_impl(const void *q, const void *k, const void *v, const void *o,
                     rope_base, stream);
 }
 
-// Attention sub-block workspace (float32): what the forward saves for the backward, then
-// scratch of either pass, each region 256-aligned.
+// Attention sub-block workspace (float32): what the forward saves for the backward (the
+// normalised rows, the projection rows [B T][(Hq + 2 Hkv) D] that hold q, k, v, the attention
+// output rows [B T][Hq D] and lse), the attention workspace, then the backward's scratch (the
+// gradient of the projection rows, one [B T][Hq D] buffer for d(o rows) then dxn, the RMSNorm
+// partial sums) and the rocBLAS scratch; each region 256-aligned.  The attention kernels read
+// and write these rows in place (strided), so no tensor is repacked into heads.
 struct BlkLayout {
-    size_t xn, rstd, q, k, v, o, lse, attn, rows_a, rows_b, hq, hk, hv, hd, part, blas, total;
+    size_t xn, rstd, qkv, o, lse, attn, dqkv, rows_b, part, blas, total;
 };
 
 BlkLayout blk_layout(const ne::Shape &s) {
     const size_t N = (size_t)s.B * s.T, C = (size_t)s.Hq * s.D;
     const size_t W = (size_t)(s.Hq + 2 * s.Hkv) * s.D;
-    const size_t nq = N * C, nk = N * (size_t)s.Hkv * s.D;
     BlkLayout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t at = off; off += up256(bytes); return at; };
-    L.xn = take(4 * nq);
+    L.xn = take(4 * N * C);
     L.rstd = take(4 * N);
-    L.q = take(4 * nq);
-    L.k = take(4 * nk);
-    L.v = take(4 * nk);
-    L.o = take(4 * nq);
+    L.qkv = take(4 * N * W);
+    L.o = take(4 * N * C);
     L.lse = take(4 * N * s.Hq);
     L.attn = take(ws_layout(s, NE_F32).total);
-    L.rows_a = take(4 * N * W);   // qkv rows; in the backward dqkv rows
-    L.rows_b = take(4 * nq);      // o rows; in the backward also d(o rows) and dxn
-    L.hq = take(4 * nq);          // backward: dO, then dq
-    L.hk = take(4 * nk);          // backward: dk
-    L.hv = take(4 * nk);          // backward: dv
-    L.hd = take(4 * nq);          // backward: o rows
+    L.dqkv = take(4 * N * W);
+    L.rows_b = take(4 * N * C);
     L.part = take(4 * (size_t)ne::rmsnorm_bwd_blocks((long long)N) * C);
     L.blas = take(ne::kBlasWorkspaceBytes);  // rocBLAS workspace of the projections
     L.total = off;
     return L;
+}
+
+// Layout of H heads of D columns inside rows of `width` elements: (b, h, t, d) at
+// (b T + t) width + h D + d (the head's first column is added to the tensor's pointer).
+ne::TLay rows_lay(int T, int width, int D) {
+    return ne::TLay{(long long)T * width, (unsigned)D, width};
 }
 
 int blk_check(int B, int T, int Hq, int Hkv, int D, float eps, float rope_base, ne::Shape &s) {
@@ -284,8 +317,10 @@ int blk_check(int B, int T, int Hq, int Hkv, int D, float eps, float rope_base, 
     if (!(eps > 0.f) || !isfinite(eps)) return NE_ERR_UNSUPPORTED;
     const long long C = (long long)Hq * D, W = (long long)(Hq + 2 * Hkv) * D;
     const long long N = (long long)B * T;
-    // C <= 8192: the RMSNorm backward keeps four rows of C floats in LDS (128 KB).
-    if (C > 8192 || W > 0x7fffffffLL / 4 || N > 0x7fffffffLL || N * W > (1LL << 40))
+    // C <= 8192: the RMSNorm backward keeps four rows of C floats in LDS (128 KB).  The
+    // attention kernels index a batch element's projection rows in 32 bits: T W < 2^31.
+    if (C > 8192 || W > 0x7fffffffLL / 4 || N > 0x7fffffffLL || N * W > (1LL << 40) ||
+        (long long)T * W > 0x7fffffffLL)
         return NE_ERR_SHAPE;
     return NE_OK;
 }
@@ -396,18 +431,22 @@ int ne_attn_block_fwd(const float *x, const float *gamma, const float *w_qkv, co
     auto F = [&](size_t off) { return reinterpret_cast<float *>(w + off); };
     const long long N = (long long)B * T;
     const int C = Hq * D, W = (Hq + 2 * Hkv) * D;
+    void *bw = w + L.blas;
+    const size_t bn = ne::kBlasWorkspaceBytes;
+    // xn = rmsnorm(x); [q | k | v] rows = xn w_qkv
     hipError_t e = ne::launch_rmsnorm_fwd(x, gamma, F(L.xn), F(L.rstd), N, C, eps, stream);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, false, false, (int)N, W, C, F(L.xn), w_qkv, F(L.rows_a), 0.f);
-    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.q), B, T, W, 0, Hq, D, true, stream);
-    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.k), B, T, W, Hq, Hkv, D, true, stream);
-    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.v), B, T, W, Hq + Hkv, Hkv, D, true, stream);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, bw, bn, false, false, (int)N, W, C, F(L.xn), w_qkv, F(L.qkv), 0.f);
     if (e != hipSuccess) return NE_ERR_HIP;
-    const int ra = fwd_impl(F(L.q), F(L.k), F(L.v), F(L.o), F(L.lse), w + L.attn, B, Hq, Hkv, T, D,
-                            1, NE_F32, rope_base, stream);
+    // attention straight on the projection rows, o written as rows
+    const ne::TLay lq = rows_lay(T, W, D), lo = rows_lay(T, C, D);
+    const ne::TLays lay{lq, lq, lq, lo, lo, lq, lq, lq};
+    const float *q = F(L.qkv), *k = q + (size_t)Hq * D, *v = k + (size_t)Hkv * D;
+    const int ra = fwd_impl(q, k, v, F(L.o), F(L.lse), w + L.attn, B, Hq, Hkv, T, D, 1, NE_F32,
+                            rope_base, stream, &lay);
     if (ra != NE_OK) return ra;
-    e = ne::launch_rows_heads(F(L.rows_b), F(L.o), B, T, C, 0, Hq, D, false, stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(y, x, sizeof(float) * (size_t)N * C, hipMemcpyDeviceToDevice, stream);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, false, false, (int)N, C, C, F(L.rows_b), w_o, y, 1.f);
+    // y = x + (o rows) w_o
+    e = hipMemcpyAsync(y, x, sizeof(float) * (size_t)N * C, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, bw, bn, false, false, (int)N, C, C, F(L.o), w_o, y, 1.f);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
@@ -427,22 +466,24 @@ int ne_attn_block_bwd(const float *x, const float *gamma, const float *w_qkv, co
     auto F = [&](size_t off) { return reinterpret_cast<float *>(w + off); };
     const long long N = (long long)B * T;
     const int C = Hq * D, W = (Hq + 2 * Hkv) * D;
-    // d(o rows) = dy Wo^T;  dWo = (o rows)^T dy
-    hipError_t e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, false, true, (int)N, C, C, dy, w_o, F(L.rows_b), 0.f);
-    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.hd), F(L.o), B, T, C, 0, Hq, D, false, stream);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, true, false, C, C, (int)N, F(L.hd), dy, dw_o, 0.f);
-    // dO heads, then the attention backward (two passes) into dq, dk, dv heads
-    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_b), F(L.hd), B, T, C, 0, Hq, D, true, stream);
+    void *bw = w + L.blas;
+    const size_t bn = ne::kBlasWorkspaceBytes;
+    // d(o rows) = dy w_o^T;  dw_o = (o rows)^T dy
+    hipError_t e = ne::gemm_rm(stream, bw, bn, false, true, (int)N, C, C, dy, w_o, F(L.rows_b), 0.f);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, bw, bn, true, false, C, C, (int)N, F(L.o), dy, dw_o, 0.f);
     if (e != hipSuccess) return NE_ERR_HIP;
-    const int ra = bwd_impl(F(L.q), F(L.k), F(L.v), F(L.o), F(L.lse), F(L.hd), F(L.hq), F(L.hk),
-                            F(L.hv), w + L.attn, B, Hq, Hkv, T, D, 1, NE_F32, rope_base, stream);
+    // the attention backward on the rows: q, k, v and o as the forward left them, dO = d(o rows),
+    // dq, dk, dv written as the rows of d[q | k | v]
+    const ne::TLay lq = rows_lay(T, W, D), lo = rows_lay(T, C, D);
+    const ne::TLays lay{lq, lq, lq, lo, lo, lq, lq, lq};
+    const float *q = F(L.qkv), *k = q + (size_t)Hq * D, *v = k + (size_t)Hkv * D;
+    float *dq = F(L.dqkv), *dk = dq + (size_t)Hq * D, *dv = dk + (size_t)Hkv * D;
+    const int ra = bwd_impl(q, k, v, F(L.o), F(L.lse), F(L.rows_b), dq, dk, dv, w + L.attn, B, Hq,
+                            Hkv, T, D, 1, NE_F32, rope_base, stream, &lay);
     if (ra != NE_OK) return ra;
-    // dqkv rows; dWqkv = xn^T dqkv; dxn = dqkv Wqkv^T; RMSNorm backward
-    e = ne::launch_rows_heads(F(L.rows_a), F(L.hq), B, T, W, 0, Hq, D, false, stream);
-    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.hk), B, T, W, Hq, Hkv, D, false, stream);
-    if (e == hipSuccess) e = ne::launch_rows_heads(F(L.rows_a), F(L.hv), B, T, W, Hq + Hkv, Hkv, D, false, stream);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, true, false, C, W, (int)N, F(L.xn), F(L.rows_a), dw_qkv, 0.f);
-    if (e == hipSuccess) e = ne::gemm_rm(stream, w + L.blas, ne::kBlasWorkspaceBytes, false, true, (int)N, C, W, F(L.rows_a), w_qkv, F(L.rows_b), 0.f);
+    // dw_qkv = xn^T d[q | k | v];  dxn = d[q | k | v] w_qkv^T;  RMSNorm backward
+    e = ne::gemm_rm(stream, bw, bn, true, false, C, W, (int)N, F(L.xn), F(L.dqkv), dw_qkv, 0.f);
+    if (e == hipSuccess) e = ne::gemm_rm(stream, bw, bn, false, true, (int)N, C, W, F(L.dqkv), w_qkv, F(L.rows_b), 0.f);
     if (e == hipSuccess)
         e = ne::launch_rmsnorm_bwd(x, gamma, F(L.rstd), F(L.rows_b), dy, dx, F(L.part), dgamma, N, C, stream);
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;

@@ -306,6 +306,8 @@ def test_block_validates(ne, which, n):
     assert block_call(ne, which, eps=float("nan")) == ne.NE_ERR_UNSUPPORTED
     assert block_call(ne, which, rope=-1.0) == ne.NE_ERR_UNSUPPORTED
     assert block_call(ne, which, Hq=130, Hkv=2, D=64) == ne.NE_ERR_SHAPE  # C = 8320 > 8192
+    # the attention reads one batch element's projection rows with 32-bit offsets: T W < 2^31
+    assert block_call(ne, which, T=1 << 20, Hq=64, Hkv=8, D=128) == ne.NE_ERR_SHAPE
 
 
 def test_block_workspace_bytes(ne):
