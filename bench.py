@@ -130,6 +130,18 @@ def measured_traffic(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, min_seconds: float):
     """The fp64 oracle, as it stands, on batch elements 0, 1, 2, ... of the same inputs (one
     oracle forward + backward call per element, cycling) until `min_seconds` have passed."""
@@ -145,10 +157,10 @@ def cpu_baseline(w, x, min_seconds: float):
         oracle.attn_bwd(q, k, v, dO, causal=w.causal, rope_base=w.rope_base)
         done += 1
         el = time.perf_counter() - t0
-        if el >= min_seconds or done >= 64 * w.B:
+        if el >= min_seconds or done >= 100000:
             break
     return {"value": one.flops_fwd_bwd() * done / el / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"{done} single-batch-element fwd+bwd calls of {w.name} "
                       f"(B=1 Hq{w.Hq} Hkv{w.Hkv} T{w.T} D{w.D}), {el:.1f} s, fp64"}
 
@@ -166,12 +178,68 @@ def cpu_baseline_decode(w, x, min_seconds: float):
         nbytes += dataclasses.replace(w, B=1).cache_bytes(x["lens"][sl])
         done += 1
         el = time.perf_counter() - t0
-        if el >= min_seconds or done >= 64 * w.B:
+        if el >= min_seconds or done >= 100000:
             break
     return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "cpu": cpu_model(),
             "kind": "oracle",
             "sample": f"{done} single-row decode steps of {w.name} (B=1 Hq{w.Hq} Hkv{w.Hkv} "
                       f"Tc{w.Tc} D{w.D}, lengths of the batch rows cycled), {el:.1f} s, fp64"}
+
+
+GRAPH_STEPS = 10  # steps captured in one graph by the single-launch benches (--graph)
+
+
+def timed_steps(torch, np, dev, a, make_step):
+    """Runs a.warmup then a.steps steps of a single-launch workload (decode, prefill); returns
+    (wall-clock ms per step, mean HIP-event ms per step).  Eager: one call per step, an event
+    after each.  With --graph: GRAPH_STEPS steps captured in one HIP graph, replayed
+    a.steps / GRAPH_STEPS times, so the host's per-call launch cost (larger than a short
+    kernel) is out of the timed region; events then bracket each replay."""
+    step = make_step(torch.cuda.current_stream(dev))
+    if not a.graph:
+        for _ in range(a.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+        gc.disable()
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(a.steps):
+            step()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gc.enable()
+        return ((t1 - t0) * 1e3 / a.steps,
+                float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)])))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        make_step(s)()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = make_step(torch.cuda.current_stream())
+        for _ in range(GRAPH_STEPS):
+            st()
+    reps = max(1, a.steps // GRAPH_STEPS)
+    for _ in range(max(1, a.warmup // GRAPH_STEPS)):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    gc.disable()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    n = reps * GRAPH_STEPS
+    return ((t1 - t0) * 1e3 / n,
+            float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) / GRAPH_STEPS)
 
 
 def main_decode(a):
@@ -196,32 +264,20 @@ def main_decode(a):
                      dtype=torch.uint8, device=dev)
     L = ne.lib()
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    args = (P(q), P(k), P(v), P(lens), P(o), P(lse), P(ws), w.B, w.Hq, w.Hkv, w.Tc, w.D, code,
-            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
 
-    def step():
-        rc = L.ne_attn_decode(*args)
-        if rc != ne.NE_OK:
-            raise ne.NeAttnError(rc, "ne_attn_decode")
+    def make_step(stream):
+        args = (P(q), P(k), P(v), P(lens), P(o), P(lse), P(ws), w.B, w.Hq, w.Hkv, w.Tc, w.D, code,
+                ctypes.c_void_p(stream.cuda_stream))
+
+        def step():
+            rc = L.ne_attn_decode(*args)
+            if rc != ne.NE_OK:
+                raise ne.NeAttnError(rc, "ne_attn_decode")
+        return step
 
     if a.copy_mib > 0:
         calibration_copies(torch, dev, a.copy_mib)
-
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    gc.disable()
-    t0 = time.perf_counter()
-    ev[0].record()
-    for i in range(a.steps):
-        step()
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gc.enable()
-    ms_per_step = (t1 - t0) * 1e3 / a.steps
-    ev_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)]))
+    ms_per_step, ev_ms = timed_steps(torch, np, dev, a, make_step)
     nbytes = w.cache_bytes(x["lens"])
     line = {
         "metric": f"attn decode GB/s (cache bytes read per step), B{w.B} Hq{w.Hq}/Hkv{w.Hkv} "
@@ -238,8 +294,9 @@ def main_decode(a):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tc": w.Tc,
-                   "D": w.D, "cached_positions": int(np.sum(x["lens"])), "seed": a.seed},
-        "roofline": {"bound": "hbm", "kernel": "decode step (split + merge)",
+                   "D": w.D, "cached_positions": int(np.sum(x["lens"])), "seed": a.seed,
+                   "launch": "hip_graph" if a.graph else "eager"},
+        "roofline": {"bound": "hbm", "kernel": "decode step",
                      "achieved": round(nbytes / (ev_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(nbytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("decode", w.name),
@@ -260,10 +317,10 @@ def cpu_baseline_prefill(w, x, min_seconds: float):
         oracle.attn_prefill(x["q"][sl], x["k"][sl], x["v"][sl])
         done += 1
         el = time.perf_counter() - t0
-        if el >= min_seconds or done >= 64 * w.B:
+        if el >= min_seconds or done >= 100000:
             break
     return {"value": dataclasses.replace(w, B=1).flops() * done / el / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"{done} single-batch-element prefill chunks of {w.name} (B=1 Hq{w.Hq} "
                       f"Hkv{w.Hkv} Tq{w.Tq} Tk{w.Tk} D{w.D}), {el:.1f} s, fp64"}
 
@@ -287,31 +344,20 @@ def main_prefill(a):
     code = ne.NE_BF16 if w.dtype == "bf16" else ne.NE_F32
     L = ne.lib()
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    args = (P(q), P(k), P(v), P(o), P(lse), w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.D, code,
-            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
 
-    def step():
-        rc = L.ne_attn_prefill(*args)
-        if rc != ne.NE_OK:
-            raise ne.NeAttnError(rc, "ne_attn_prefill")
+    def make_step(stream):
+        args = (P(q), P(k), P(v), P(o), P(lse), w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.D, code,
+                ctypes.c_void_p(stream.cuda_stream))
+
+        def step():
+            rc = L.ne_attn_prefill(*args)
+            if rc != ne.NE_OK:
+                raise ne.NeAttnError(rc, "ne_attn_prefill")
+        return step
 
     if a.copy_mib > 0:
         calibration_copies(torch, dev, a.copy_mib)
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    gc.disable()
-    t0 = time.perf_counter()
-    ev[0].record()
-    for i in range(a.steps):
-        step()
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gc.enable()
-    ms_per_step = (t1 - t0) * 1e3 / a.steps
-    ev_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)]))
+    ms_per_step, ev_ms = timed_steps(torch, np, dev, a, make_step)
     fl = w.flops()
     peak = MFMA_PEAK[w.dtype]
     line = {
@@ -329,7 +375,7 @@ def main_prefill(a):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq, "Tk": w.Tk,
-                   "D": w.D, "seed": a.seed},
+                   "D": w.D, "seed": a.seed, "launch": "hip_graph" if a.graph else "eager"},
         "roofline": {"bound": "mfma", "kernel": "forward with a query offset",
                      "achieved": round(fl / (ev_ms * 1e-3) / 1e12, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(fl / (ev_ms * 1e-3) / 1e12 / peak, 4),
@@ -358,7 +404,7 @@ def cpu_baseline_block(w, x, min_seconds: float):
         if el >= min_seconds:
             break
     return {"value": one.flops() * done / el / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"{done} single-batch-element sub-block forward + backward calls of "
                       f"{w.name} (B=1 T{w.T} Hq{w.Hq} Hkv{w.Hkv} D{w.D}), {el:.1f} s, fp64"}
 
@@ -602,6 +648,8 @@ def main():
                    "backward": "single-pass, dq by fp32 atomics" if a.fused_bwd
                    else "two passes, atomics-free"},
         "pct_mfma_peak": round(100 * tflops / MFMA_PEAK[w.dtype], 2),
+        # algorithmic HBM bytes of the step (inputs read and outputs written once per pass)
+        "step_gbs": round(w.bytes_fwd_bwd() / (ms_per_step * 1e-3) / 1e9, 2),
         "kernels": {n: {kk: round(vv, 4) for kk, vv in d.items()} for n, d in kern.items()},
         "roofline": roof,
         "cpu_baseline": None if a.no_cpu_baseline else cpu_baseline(w, x, a.cpu_seconds),
