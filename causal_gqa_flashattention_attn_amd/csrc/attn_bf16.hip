@@ -743,14 +743,29 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     const int lrow = lane / C::NCH;
     const int chb = 16 * chunk_swizzle<D>(lrow, lane % C::NCH);
     const int off0 = lrow * C::RB + chb;
-    // Starts the copies of item `it` into `st`, through buffer resources on the head's q and dO.
-    // Rows past the end read row T - 1; their lse is replaced by +inf once the item has landed,
-    // so their probabilities are 0.
-    auto issue = [&](int it, unsigned char *st) {
-        // (item indices and counts are non-negative: unsigned division needs no sign fix-ups)
-        const int hh = (int)((unsigned)it / (unsigned)per_head);
-        const int i = i0 + (int)((unsigned)it % (unsigned)per_head);
-        const size_t bh = (size_t)b * a.Hq + (size_t)g * a.G + hh;
+    // A wave takes the items wave, wave + nw, ... in order, both when it copies them and when it
+    // uses them: (head hh of the group, query block i0 + ii) of the next item to copy and of the
+    // next to use are advanced by nw items at a time, so the loop divides nothing.
+    struct ItemPos {
+        int hh, ii;
+        __device__ __forceinline__ void advance(int n, int per) {
+            ii += n;
+            while (ii >= per) {
+                ii -= per;
+                ++hh;
+            }
+        }
+    };
+    const size_t bh0 = (size_t)b * a.Hq + (size_t)g * a.G;  // the group's first query head
+    ItemPos cp{(int)((unsigned)wave / (unsigned)per_head), (int)((unsigned)wave % (unsigned)per_head)};
+    ItemPos up = cp;
+    // Starts the copies of the next item (cp) into `st`, through buffer resources on the
+    // head's q and dO.  Rows past the end read row T - 1; their lse is replaced by +inf once
+    // the item has landed, so their probabilities are 0.
+    auto issue = [&](unsigned char *st) {
+        const int i = i0 + cp.ii;
+        const size_t bh = bh0 + cp.hh;
+        cp.advance(nw, per_head);
         const unsigned bytes = (unsigned)T * C::RB;
         const buf_rsrc_t rq = raw_rsrc(a.q + bh * T * D, bytes);
         const buf_rsrc_t ro = raw_rsrc(a.dO + bh * T * D, bytes);
@@ -790,8 +805,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     // The first two items are requested before the K, V rows, so the latencies overlap; all of
     // it has landed before the loop, so the compiler places no wait for the rows inside it.
     unsigned char *wbuf = smem_b + wave * dkdv_wave_bytes_b<D>();
-    if (wave < nitems) issue(wave, wbuf);
-    if (wave + nw < nitems) issue(wave + nw, wbuf + S::SB);
+    if (wave < nitems) issue(wbuf);
+    if (wave + nw < nitems) issue(wbuf + S::SB);
     bf16x8 kv[C::KS], vv[C::KS];
     load_operand_row<D, false>(kv, a.k + bg * T * D, krow, T, half, a);
     load_operand_row<D, false>(vv, a.v + bg * T * D, krow, T, half, a);
@@ -801,7 +816,8 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
     // One item in stage ST (compile-time, so that every LDS offset of the item is an immediate).
     auto item = [&](int it, auto stage) {
         constexpr int ST = decltype(stage)::value;
-        const int i = i0 + (int)((unsigned)it % (unsigned)per_head);
+        const int i = i0 + up.ii;
+        up.advance(nw, per_head);
         unsigned char *st = wbuf + ST * S::SB;
         const unsigned char *sQ = st;
         const unsigned char *sO = st + S::TBQ;
@@ -855,7 +871,7 @@ __device__ __forceinline__ void dkdv_block_b(const ArgsB &a, int b, int g, int k
         const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
         accum_tr<D, 0>(dk, tq, db);
         // The stage is free once this item's reads are done: copy the item after next into it.
-        if (it + 2 * nw < nitems) issue(it + 2 * nw, st);
+        if (it + 2 * nw < nitems) issue(st);
     };
     for (int it = wave; it < nitems; it += 2 * nw) {
         item(it, std::integral_constant<int, 0>{});
