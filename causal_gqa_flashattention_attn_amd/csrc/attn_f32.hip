@@ -27,6 +27,10 @@
 #include <math.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <utility>
 
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
@@ -833,13 +837,35 @@ hipError_t launch(const void *fn, long long blocks, int threads, size_t lds, hip
 // decode_qwork): compute units / work-groups per tile index, when every work-group of the
 // launch is resident at once (then the order decides which work shares a unit) and the shape
 // divides evenly; otherwise 0, longest tile first, which suits launches of several rounds.
+// Compute units of the current device and resident work-groups of `fn` per compute unit,
+// queried once per (device, kernel, work-group size) and kept for the process.
+bool residency(const void *fn, int threads, int &cus, int &per_cu) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void *, int>, std::pair<int, int>> seen;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    const auto key = std::make_tuple(dev, fn, threads);
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        const auto it = seen.find(key);
+        if (it != seen.end()) {
+            cus = it->second.first;
+            per_cu = it->second.second;
+            return true;
+        }
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess)
+        return false;
+    std::lock_guard<std::mutex> lk(mu);
+    seen[key] = {cus, per_cu};
+    return true;
+}
+
 int mirror_step(const Shape &s, const QTileGeom &g, const void *fn) {
     if (!s.causal || g.paired) return 0;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * g.nwaves, 0) != hipSuccess)
-        return 0;
+    int cus = 0, per_cu = 0;
+    if (!residency(fn, 64 * g.nwaves, cus, per_cu)) return 0;
     if (g.nblocks > (long long)per_cu * cus) return 0;
     const long long per = (long long)s.B * s.Hkv * (s.G / g.hpw);
     if (per <= 0 || cus % per != 0) return 0;
