@@ -11,8 +11,10 @@
 //   decode_split  grid (split, batch x kv head x query-head chunk), 4 waves of 64 keys each;
 //                 one work-group serves every query head of its key/value head, so each cache
 //                 row is read once.  Each lane keeps an online softmax (running maximum, sum,
-//                 output slice) per query head over the keys it saw; lanes, then waves, are
-//                 merged, and the split's (o / l, lse) goes to the workspace.
+//                 output slice) per query head over the keys it saw; lanes are merged by
+//                 shuffles, then wave 0 merges the waves (one query head per group of lanes,
+//                 every wave's state read at once), and the split's (o / l, lse) goes to the
+//                 workspace.
 //   decode_merge  per (batch, query head): log-sum-exp of the splits' lse, weighted sum of their
 //                 outputs.  Splits past lens[b] are neither computed nor read.
 // When one split covers the whole cache (Tc <= 512: 4 or 8 waves of 64 keys), the split kernel
@@ -34,6 +36,7 @@ constexpr int kDecKeysPerWave = 64;
 constexpr int kDecSplit = kDecWaves * kDecKeysPerWave;  // keys per split (several splits)
 constexpr int kDecWavesOne = 8;                         // waves of a single split (Tc <= 512)
 
+
 struct DecArgs {
     const void *q, *k, *v;
     const int *lens;
@@ -41,19 +44,22 @@ struct DecArgs {
     float *lse;
     float *part_o, *part_lse;  // workspace: [nsplit][B][Hq][D] and [nsplit][B][Hq]
     int B, Hq, Hkv, Tc, G, nhc, nsplit;
+    int xcd;  // 1: blockIdx.y interleaved so that a key/value head's head chunks share an XCD
     float qscale;  // log2(e) / sqrt(D): scores in base-2 units
 };
 
 // Lane geometry: a lane streams E elements (16 bytes) of a row; LPK lanes cover a row of D;
-// one wave-wide load covers KPI rows; a wave's 64 keys take NIT loads, issued PASS at a time
-// (fewer at once for wide head groups, whose per-head state takes the registers).
-template <int D, typename T, int GC>
+// one wave-wide load covers KPI rows; a wave's KPW keys take NIT loads, issued PASS at a time
+// (fewer at once for wide head groups, whose per-head state takes the registers).  WIDE: up
+// to 16 at once (a single split: with two waves per SIMD, each has the registers), so that a
+// wave's keys are one round of loads.
+template <int D, typename T, int GC, int KPW = kDecKeysPerWave, bool WIDE = false>
 struct DecCfg {
     static constexpr int E = 16 / sizeof(T);
     static constexpr int LPK = D / E;
     static constexpr int KPI = 64 / LPK;
-    static constexpr int NIT = kDecKeysPerWave / KPI;
-    static constexpr int PMAX = GC <= 4 ? 8 : 4;
+    static constexpr int NIT = KPW / KPI;
+    static constexpr int PMAX = WIDE && GC * E <= 16 ? 16 : GC <= 4 ? 8 : 4;
     static constexpr int PASS = NIT < PMAX ? NIT : PMAX;
     static_assert(LPK >= 1 && 64 % LPK == 0 && NIT % PASS == 0, "unsupported head size");
 };
@@ -125,20 +131,30 @@ __device__ __forceinline__ void dec_merge(DecState<E> &a, float m2, float l2, co
     a.m = mn;
 }
 
-// NW waves of 64 keys per work-group.  ONE: a single split covers the cache, so the work-group
+// NW waves of KPW keys per work-group.  ONE: a single split covers the cache, so the work-group
 // writes o and lse (o = 0, lse = -inf for an empty cache) instead of its workspace entries.
-template <int D, typename T, int GC, int NW, bool ONE>
+template <int D, typename T, int GC, int NW, bool ONE, int KPW = kDecKeysPerWave>
 __global__ void __launch_bounds__(64 * NW) decode_split(DecArgs a) {
-    using C = DecCfg<D, T, GC>;
+    using C = DecCfg<D, T, GC, KPW, ONE && NW <= 8>;
     constexpr int E = C::E;
-    const int s = blockIdx.x;
-    int y = blockIdx.y;
-    const int hc = y % a.nhc;
-    y /= a.nhc;
+    // Grid: (split, batch x kv head x head chunk); a single split is a 1-D grid of the latter.
+    const int s = ONE ? 0 : blockIdx.x;
+    int y = ONE ? blockIdx.x : blockIdx.y;
+    int hc;
+    if (a.xcd) {
+        // Work-groups are dealt to the 8 XCDs in turn, so y, y + 8, ... share an XCD (and its
+        // L2): those take the head chunks of one key/value head, whose rows each of them reads.
+        const int lane8 = y % 8, rest = y / 8;
+        hc = rest % a.nhc;
+        y = (rest / a.nhc) * 8 + lane8;
+    } else {
+        hc = y % a.nhc;
+        y /= a.nhc;
+    }
     const int g = y % a.Hkv;
     const int b = y / a.Hkv;
     const int len = min(max(a.lens[b], 0), a.Tc);
-    const int k0 = s * NW * kDecKeysPerWave;
+    const int k0 = s * NW * KPW;
     if (!ONE && k0 >= len) return;  // past the cached length: the merge does not read this split
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -165,7 +181,7 @@ __global__ void __launch_bounds__(64 * NW) decode_split(DecArgs a) {
     const size_t row0 = ((size_t)b * a.Hkv + g) * a.Tc;
     const T *kb = static_cast<const T *>(a.k) + row0 * D + sub * E;
     const T *vb = static_cast<const T *>(a.v) + row0 * D + sub * E;
-    const int kw = k0 + wave * kDecKeysPerWave;
+    const int kw = k0 + wave * KPW;
 #pragma unroll
     for (int p0 = 0; p0 < C::NIT; p0 += C::PASS) {
         if (kw + p0 * C::KPI >= len) break;  // wave-uniform
@@ -226,7 +242,7 @@ __global__ void __launch_bounds__(64 * NW) decode_split(DecArgs a) {
             dec_merge<E>(st[gi], m2, l2, o2);
         }
 
-    // Merge the waves in LDS (fixed order), then lanes 0 .. LPK-1 of wave 0 write the split.
+    // Each wave's state goes to LDS for wave 0 to merge.
     __shared__ float red[NW][GC][D + 2];
     if (kl == 0)
 #pragma unroll
@@ -239,35 +255,45 @@ __global__ void __launch_bounds__(64 * NW) decode_split(DecArgs a) {
             }
         }
     __syncthreads();
-    if (wave != 0 || kl != 0) return;
+    if (wave != 0) return;
+    // Wave 0 merges the waves' states: each group of LPK lanes takes one query head (the lanes'
+    // slices of its output), reads every wave's (m, l, o) at once, and sums them weighted by
+    // 2^(m_w - M) with M the largest m, in wave order.
+    constexpr int HPP = 64 / C::LPK;  // heads merged at once
+    for (int g0 = 0; g0 < GC; g0 += HPP) {
+        const int gi = g0 + kl;
+        if (gi >= gn) continue;
+        float mw[NW];
+        float M = kNegBig;
 #pragma unroll
-    for (int gi = 0; gi < GC; ++gi) {
-        if (gi >= gn) break;
-        DecState<E> t;
-        t.m = red[0][gi][D];
-        t.l = red[0][gi][D + 1];
+        for (int w = 0; w < NW; ++w) {
+            mw[w] = red[w][gi][D];
+            M = fmaxf(M, mw[w]);
+        }
+        float L = 0.f, O[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) t.o[e] = red[0][gi][sub * E + e];
-        for (int w = 1; w < NW; ++w) {
-            float o2[E];
+        for (int e = 0; e < E; ++e) O[e] = 0.f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) o2[e] = red[w][gi][sub * E + e];
-            dec_merge<E>(t, red[w][gi][D], red[w][gi][D + 1], o2);
+        for (int w = 0; w < NW; ++w) {
+            const float sw = fast_exp2(mw[w] - M);
+            L = fmaf(red[w][gi][D + 1], sw, L);
+#pragma unroll
+            for (int e = 0; e < E; ++e) O[e] = fmaf(red[w][gi][sub * E + e], sw, O[e]);
         }
         const size_t bh = (size_t)b * a.Hq + h0 + gi;
         const size_t ps = (size_t)s * a.B * a.Hq + bh;
-        const float inv = t.l > 0.f ? 1.0f / t.l : 0.f;
-        const float ls = t.l > 0.f ? (t.m + __log2f(t.l)) * kLn2 : -INFINITY;
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
+        const float ls = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
         if constexpr (ONE) {
             T *orow = static_cast<T *>(a.o) + bh * D + sub * E;
 #pragma unroll
-            for (int e = 0; e < E; ++e) orow[e] = to_elt<T>(t.o[e] * inv);
+            for (int e = 0; e < E; ++e) orow[e] = to_elt<T>(O[e] * inv);
             if (sub == 0) a.lse[bh] = ls;
         } else {
             float *po = a.part_o + ps * D + sub * E;
 #pragma unroll
             for (int e = 0; e < E; e += 4) *reinterpret_cast<f32x4 *>(po + e) =
-                f32x4{t.o[e] * inv, t.o[e + 1] * inv, t.o[e + 2] * inv, t.o[e + 3] * inv};
+                f32x4{O[e] * inv, O[e + 1] * inv, O[e + 2] * inv, O[e + 3] * inv};
             if (sub == 0) a.part_lse[ps] = ls;
         }
     }
@@ -314,29 +340,35 @@ __global__ void __launch_bounds__(64) decode_merge(DecArgs a) {
     if (lane == 0) a.lse[bh] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
-template <int D, typename T, int NW, bool ONE>
+template <int D, typename T, int NW, bool ONE, int KPW = kDecKeysPerWave>
 const void *pick_split(int gc) {
-    return gc == 1   ? (const void *)decode_split<D, T, 1, NW, ONE>
-           : gc == 2 ? (const void *)decode_split<D, T, 2, NW, ONE>
-           : gc == 4 ? (const void *)decode_split<D, T, 4, NW, ONE>
-                     : (const void *)decode_split<D, T, 8, NW, ONE>;
+    return gc == 1   ? (const void *)decode_split<D, T, 1, NW, ONE, KPW>
+           : gc == 2 ? (const void *)decode_split<D, T, 2, NW, ONE, KPW>
+           : gc == 4 ? (const void *)decode_split<D, T, 4, NW, ONE, KPW>
+                     : (const void *)decode_split<D, T, 8, NW, ONE, KPW>;
 }
 
 template <int D, typename T>
 hipError_t launch_decode_t(DecArgs &a, hipStream_t st) {
-    // Query heads per work-group: the whole group when it is small, else chunks of 8.
-    const int gc = a.G <= 1 ? 1 : a.G <= 2 ? 2 : a.G <= 4 ? 4 : 8;
+    // Query heads per work-group: with several splits, the whole group when it is small, else
+    // chunks of 8 (each cache row is read once).  A single split has too few work-groups to
+    // fill the chip that way, so it takes one query head per work-group: the heads of a group
+    // read its rows again, from the L2 of their XCD.
+    const bool one = a.Tc <= kDecWavesOne * kDecKeysPerWave;
+    const int gc = one || a.G <= 1 ? 1 : a.G <= 2 ? 2 : a.G <= 4 ? 4 : 8;
     a.nhc = (a.G + gc - 1) / gc;
+    a.xcd = a.nhc > 1 && ((long long)a.B * a.Hkv) % 8 == 0;
     void *params[] = {&a};
     const long long gy = (long long)a.B * a.Hkv * a.nhc;
-    if (gy > 65535) return hipErrorInvalidValue;
     // A cache of at most 512 keys is one split (4 or 8 waves): no merge.
-    if (a.Tc <= kDecWavesOne * kDecKeysPerWave) {
+    if (one) {
+        if (gy > 0x7fffffffLL) return hipErrorInvalidValue;
         const int nw = a.Tc <= kDecSplit ? kDecWaves : kDecWavesOne;
         const void *fn = nw == kDecWaves ? pick_split<D, T, kDecWaves, true>(gc)
                                          : pick_split<D, T, kDecWavesOne, true>(gc);
-        return hipLaunchKernel(fn, dim3(1, (unsigned)gy), dim3(64 * nw), params, 0, st);
+        return hipLaunchKernel(fn, dim3((unsigned)gy), dim3(64 * nw), params, 0, st);
     }
+    if (gy > 65535) return hipErrorInvalidValue;
     hipError_t e = hipLaunchKernel(pick_split<D, T, kDecWaves, false>(gc),
                                    dim3((unsigned)a.nsplit, (unsigned)gy), dim3(64 * kDecWaves),
                                    params, 0, st);

@@ -62,6 +62,12 @@ CASES = [
     (1, 24, 3, 4097, 64, [4097]),             # group of 8, ragged last split
     (2, 8, 2, 600, 128, [600, 300]),          # head size 128 (fp32: 32 lanes per row)
     (1, 16, 2, 1030, 128, [1030]),            # head size 128, group of 8
+    # caches of at most 512 keys: one launch, no merge
+    (2, 12, 4, 512, 64, [512, 200]),          # 16 waves of 32 keys, groups of 3 (as 4)
+    (2, 16, 2, 480, 32, [480, 17]),           # group of 8 at D 32: 16 waves (fp32) or 8 of 64
+    (1, 8, 1, 400, 64, [400]),                # group of 8: 8 waves of 64 keys
+    (2, 4, 2, 500, 128, [500, 260]),          # head size 128, 16 waves
+    (2, 16, 2, 200, 128, [200, 33]),          # head size 128, group of 8, 8 waves of 32 keys
 ]
 
 
