@@ -41,6 +41,13 @@
 #ifndef NE_BF16_DKDV_WAVES_PER_EU
 #define NE_BF16_DKDV_WAVES_PER_EU 2
 #endif
+// Stages of the forward's K/V ring at D <= 64.  Two (32 KB at D = 64) let four work-groups of
+// four waves share a compute unit, which the forward's registers allow; with each tile's copies
+// issued as soon as the barrier frees its stage, they still overlap a whole tile of work.  This
+// measured 5-7 % faster than three stages (48 KB, three work-groups) at B 16, Hq 16, T 1024.
+#ifndef NE_BF16_FWD_NST
+#define NE_BF16_FWD_NST 2
+#endif
 
 namespace ne {
 
@@ -195,10 +202,10 @@ __device__ __forceinline__ QTileB qtile_of_b(const ArgsB &a, const QWorkB &w, in
 // shorter share copies its first piece again, so every wave issues lpw copies per tile and can
 // wait on a fixed count.  Rows past the end read row T - 1: those keys are masked, so only
 // finiteness matters.
-template <int D>
+template <int D, int NSTAGES = 3>
 struct KVRingB {
     using C = CfgB<D>;
-    static constexpr int NST = 3;                 // stages
+    static constexpr int NST = NSTAGES;           // stages
     static constexpr int PD = NST - 1;            // tiles requested ahead of the one in use
     static constexpr int TB = C::BN * C::RB;      // bytes of one K (or V) tile
     static constexpr int SB = 2 * TB;             // bytes of one stage
@@ -450,7 +457,7 @@ __device__ __forceinline__ void fwd_step(const ArgsB &a, FwdState<D> &st, const 
 template <int D, bool CAUSAL, bool ROPE, int NWC>
 __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsigned char *ring) {
     using C = CfgB<D>;
-    using R = KVRingB<D>;
+    using R = KVRingB<D, D == 128 ? 3 : NE_BF16_FWD_NST>;
     const int nw = NWC ? NWC : blockDim.x >> 6;  // a compile-time count makes the waits immediates
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -501,18 +508,23 @@ __device__ __forceinline__ void fwd_tile_b(const ArgsB &a, const QTileB &c, unsi
         // complete and stage (j + PD) % NST, last read for tile j-1, is free.
         wait_vm_lgkm0(min(R::PD - 1, ntiles - 1 - j) * kv.lpw);
         __builtin_amdgcn_s_barrier();
+        // Stage (j + PD) % NST held tile j - 1, which every wave has finished: with two stages
+        // its copies start now, so that they overlap this tile's work.
+        if (R::NST == 2 && j + R::PD < ntiles)
+            kv.issue(kg, vg, j + R::PD, Tk, ring + ((ST + R::PD) % R::NST) * R::SB);
         const unsigned char *sK = ring + ST * R::SB;
         if (live) fwd_step<D, CAUSAL, ST * R::SB + R::TB>(a, st, sK, tra, j * C::BN, r0 + qo, Tk, qv, lane);
         // Issued after this tile's reads: the compiler makes transposed LDS reads wait for every
         // copy in flight, and by the next tile's reads these have landed.
-        if (j + R::PD < ntiles)
+        if (R::NST != 2 && j + R::PD < ntiles)
             kv.issue(kg, vg, j + R::PD, Tk, ring + ((ST + R::PD) % R::NST) * R::SB);
     };
-    static_assert(R::NST == 3, "the loop below is unrolled over three stages");
-    for (int j = 0; j < ntiles; j += 3) {
+    static_assert(R::NST == 2 || R::NST == 3, "the loop below is unrolled over two or three stages");
+    for (int j = 0; j < ntiles; j += R::NST) {
         iter(j, std::integral_constant<int, 0>{});
         if (j + 1 < ntiles) iter(j + 1, std::integral_constant<int, 1>{});
-        if (j + 2 < ntiles) iter(j + 2, std::integral_constant<int, 2>{});
+        if constexpr (R::NST == 3)
+            if (j + 2 < ntiles) iter(j + 2, std::integral_constant<int, 2>{});
     }
 
     const float l = sum_halves((st.l4[0] + st.l4[1]) + (st.l4[2] + st.l4[3]));
@@ -537,7 +549,8 @@ template <int D, bool CAUSAL, bool ROPE, int NWC>
 __global__ void __launch_bounds__(D == 128 ? 256 : 512)
 __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : NE_BF16_FWD_WAVES_PER_EU)))
 fwd_bf16(ArgsB a) {
-    __shared__ __attribute__((aligned(16))) unsigned char ring[KVRingB<D>::NST * KVRingB<D>::SB];
+    using R = KVRingB<D, D == 128 ? 3 : NE_BF16_FWD_NST>;
+    __shared__ __attribute__((aligned(16))) unsigned char ring[R::NST * R::SB];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const QWorkB w = decode_qwork_b(a);
     fwd_tile_b<D, CAUSAL, ROPE, NWC>(a, qtile_of_b(a, w, w.qt0, wave), ring);
