@@ -419,14 +419,19 @@ __device__ __forceinline__ void fwd_half(const ArgsB &a, FwdState<D> &st, const 
     // then skip the rescale of l and O entirely.  The test is per lane, on raw scores; the row
     // maximum over both lane halves is only formed when m moves.
     if (__builtin_amdgcn_ballot_w64(lmax > st.mthr) != 0) {
-        const float mnew = fmaxf(st.m, max_halves(lmax) * a.qscale);
-        const float alpha = fast_exp2(st.m - mnew);
-        st.m = mnew;
-        st.mthr = (mnew + 8.0f) / a.qscale;
+        // Only the rows whose maximum exceeds the threshold move: a row's m (and so its
+        // rounding) never depends on the other rows of the wave.
+        const float rmax = max_halves(lmax);
+        if (rmax > st.mthr) {
+            const float mnew = fmaxf(st.m, rmax * a.qscale);
+            const float alpha = fast_exp2(st.m - mnew);
+            st.m = mnew;
+            st.mthr = (mnew + 8.0f) / a.qscale;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st.l4[i] *= alpha;
+            for (int i = 0; i < 4; ++i) st.l4[i] *= alpha;
 #pragma unroll
-        for (int dd = 0; dd < CfgB<D>::ND; ++dd) st.acc[dd] *= alpha;
+            for (int dd = 0; dd < CfgB<D>::ND; ++dd) st.acc[dd] *= alpha;
+        }
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = fast_exp2(fmaf(s[v], a.qscale, -st.m));

@@ -325,22 +325,35 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
                     if ((CAUSAL && key > qrow + qo) || key >= Tk) s[v] = -INFINITY;
                 }
             }
-            float mx = s[0];
+            // Lazy rescale: the reference maximum m only moves when a score of this lane's row
+            // exceeds it by more than 2^8 (probabilities up to 256 are exact enough in fp32
+            // sums), so most tiles skip the rescale of l and O.  The row maximum over both
+            // lane halves is only formed when some lane needs it.
+            const auto mx3 = [](float x, float y, float z) {
+                return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+            };
+            const float lmax = __builtin_elementwise_maximum(
+                mx3(mx3(s[0], s[1], s[2]), mx3(s[3], s[4], s[5]), mx3(s[6], s[7], s[8])),
+                mx3(mx3(s[9], s[10], s[11]), mx3(s[12], s[13], s[14]), s[15]));
+            if (__builtin_amdgcn_ballot_w64(lmax > m + 8.0f) != 0) {
+                // Only the rows that need it move (others keep m bit for bit, whatever the
+                // other rows of the wave hold).
+                const float rmax = fmaxf(lmax, swap_halves(lmax));
+                if (rmax > m + 8.0f) {
+                    const float alpha = fast_exp2(m - rmax);
+                    m = rmax;
+                    l *= alpha;
 #pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-            mx = fmaxf(mx, swap_halves(mx));
-            const float mnew = fmaxf(m, mx);
-            const float alpha = fast_exp2(m - mnew);
-            m = mnew;
+                    for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
+                }
+            }
             float ps = 0.f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                s[v] = fast_exp2(s[v] - mnew);
+                s[v] = fast_exp2(s[v] - m);
                 ps += s[v];
             }
-            l = l * alpha + ps;
-#pragma unroll
-            for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
+            l += ps;
             accum_t<D>(acc, sV[buf], s, col, half);
         }
         if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, Tk, wave, nw, lane);

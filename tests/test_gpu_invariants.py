@@ -30,20 +30,26 @@ def test_bitwise_determinism(ne, name):
         assert np.array_equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 @pytest.mark.parametrize("t", [63, 200, 255])
-def test_causality_is_bitwise(ne, t):
+def test_causality_is_bitwise(ne, t, bf16):
     """Changing q, k, v, dO at positions > t leaves o and lse at positions <= t bit-identical
-    (masked probabilities are exactly 0); changing queries and dO at positions < 32*floor(t/32)
-    leaves dk, dv at keys >= 32*floor(t/32) bit-identical."""
+    (masked probabilities are exactly 0, and a row's running maximum depends on its own scores
+    only); changing queries and dO at positions < 32*floor(t/32) leaves dk, dv at keys
+    >= 32*floor(t/32) bit-identical."""
+    import torch
+    dt = torch.bfloat16 if bf16 else torch.float32
     B, Hq, Hkv, T, D = 2, 6, 2, 300, 64
     x = qkvd(B, Hq, Hkv, T, D, 40)
     y = {n: a.copy() for n, a in x.items()}
     r = np.random.default_rng(41)
     for n in y:
         y[n][:, :, t + 1:] = r.standard_normal(y[n][:, :, t + 1:].shape)
-    print(f"\n[case] causality t={t}", flush=True)
-    a = gpu_fwd_bwd(ne, x, with_bwd=False)
-    b = gpu_fwd_bwd(ne, y, with_bwd=False)
+    # rows that make the running maximum move late: boosted queries after row t
+    y["q"][:, :, t + 1::7] *= 6.0
+    print(f"\n[case] causality t={t} bf16={bf16}", flush=True)
+    a = gpu_fwd_bwd(ne, x, with_bwd=False, dtype=dt)
+    b = gpu_fwd_bwd(ne, y, with_bwd=False, dtype=dt)
     assert np.array_equal(a["o"][:, :, :t + 1], b["o"][:, :, :t + 1])
     assert np.array_equal(a["lse"][:, :, :t + 1], b["lse"][:, :, :t + 1])
     assert not np.array_equal(a["o"][:, :, t + 1:], b["o"][:, :, t + 1:])
@@ -51,8 +57,8 @@ def test_causality_is_bitwise(ne, t):
     z = {n: a_.copy() for n, a_ in x.items()}
     z["q"][:, :, :tb] = r.standard_normal(z["q"][:, :, :tb].shape)
     z["dO"][:, :, :tb] = r.standard_normal(z["dO"][:, :, :tb].shape)
-    ga = gpu_fwd_bwd(ne, x)
-    gz = gpu_fwd_bwd(ne, z)
+    ga = gpu_fwd_bwd(ne, x, dtype=dt)
+    gz = gpu_fwd_bwd(ne, z, dtype=dt)
     assert np.array_equal(ga["dk"][:, :, tb:], gz["dk"][:, :, tb:])
     assert np.array_equal(ga["dv"][:, :, tb:], gz["dv"][:, :, tb:])
 
