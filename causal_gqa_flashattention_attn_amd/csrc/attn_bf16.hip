@@ -304,6 +304,21 @@ __device__ __forceinline__ void load_operand_row(bf16x8 (&dst)[CfgB<D>::KS], con
         dst[s] = load_row8<D, ROPE>(base, row, T, 16 * s + 8 * half, tpos, a.rt, 8 * s);
 }
 
+// The rotation of a row loaded raw by load_operand_row<D, false> (chunks as there), for callers
+// that request other reads before the rotation waits for these.
+template <int D>
+__device__ __forceinline__ void rotate_operand_row(bf16x8 (&v)[CfgB<D>::KS], int row, int half,
+                                                   const ArgsB &a) {
+    const double tpos = (double)row * (half ? a.rope_shift4 : 1.0);
+#pragma unroll
+    for (int s = 0; s < CfgB<D>::KS; ++s) {
+        float x[8];
+        unpack8(v[s], x);
+        rope_rotate<8>(x, tpos, a.rt, 8 * s, false);
+        v[s] = round8(x);
+    }
+}
+
 // S^T block (32 keys of the tile from row r0 x this wave's 32 rows) = M_tile x X^T.
 template <int D>
 __device__ __forceinline__ f32x16 block_scores(const unsigned char *tile, int r0,
@@ -591,20 +606,19 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
 #pragma unroll
     for (int t = 0; t < R::PD; ++t)
         if (t < ntiles) kv.issue(kg, vg, t, T, ring + t * R::SB);
-    bf16x8 qv[C::KS], dov[C::KS];
-    load_operand_row<D, ROPE>(qv, a.q + bh * T * D, qrow, T, half, a);
-    if (ROPE && qrow < T) {  // each query row is loaded by exactly one wave: keep its rotation
-#pragma unroll
-        for (int st = 0; st < C::KS; ++st)
-            *reinterpret_cast<bf16x8 *>(a.qrot + (bh * T + qrow) * D + 16 * st + 8 * half) = qv[st];
-    }
+    // Every global read of the row (q, dO, o, lse) is requested before any is used, so their
+    // latencies overlap: the rotation of q and delta wait for one round trip, not several.
+    bf16x8 qv[C::KS], dov[C::KS], ov[C::KS];
+    load_operand_row<D, false>(qv, a.q + bh * T * D, qrow, T, half, a);
     load_operand_row<D, false>(dov, a.dO + bh * T * D, qrow, T, half, a);
+    load_operand_row<D, false>(ov, a.o + bh * T * D, qrow, T, half, a);
+    const float lse_row = a.lse[bh * T + min(qrow, T - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    if (ROPE) rotate_operand_row<D>(qv, qrow, half, a);
 
     // delta_i = sum_d dO_id o_id over this row (fp32), written once for the dK/dV pass.
     float delta;
     {
-        bf16x8 ov[C::KS];
-        load_operand_row<D, false>(ov, a.o + bh * T * D, qrow, T, half, a);
         float part = 0.f;
 #pragma unroll
         for (int s = 0; s < C::KS; ++s)
@@ -614,11 +628,16 @@ __device__ __forceinline__ void dq_tile_b(const ArgsB &a, const QTileB &c, unsig
     }
     float lse2;
     if (qrow < T) {
-        lse2 = a.lse[bh * T + qrow] * kLog2e;
+        lse2 = lse_row * kLog2e;
         if (half == 0) a.delta[bh * T + qrow] = delta;
     } else {
         lse2 = INFINITY;
         delta = 0.f;
+    }
+    if (ROPE && qrow < T) {  // each query row is loaded by exactly one wave: keep its rotation
+#pragma unroll
+        for (int st = 0; st < C::KS; ++st)
+            *reinterpret_cast<bf16x8 *>(a.qrot + (bh * T + qrow) * D + 16 * st + 8 * half) = qv[st];
     }
 
     f32x16 acc[C::ND];
