@@ -226,6 +226,21 @@ __device__ __forceinline__ void load_row_half(float (&dst)[Cfg<D>::NS], const fl
     }
 }
 
+// The rotation and scaling of a row half loaded raw by load_row_half<D, false> with mul = 1, for
+// callers that request other reads before the rotation waits for this one.
+template <int D>
+__device__ __forceinline__ void rotate_row_half(float (&x)[Cfg<D>::NS], int row, int half,
+                                                float mul, const RopeArgs &rp) {
+    using C = Cfg<D>;
+#pragma unroll
+    for (int c = 0; c < C::NS / 4; ++c) {
+        const f32x4 t = rope4<D>(f32x4{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]}, row,
+                                 C::NS * half + 4 * c, rp, false);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * c + i] = t[i] * mul;
+    }
+}
+
 // acc += sum_st A[st] * x[st], with A[st] = a[st] read from LDS in 16-byte groups: a chain of NS
 // dependent MFMAs over one row of a tile.  The reads are software-pipelined: group g+1 is
 // requested before the four MFMAs of group g are issued, and sched_barrier keeps the compiler
@@ -294,6 +309,13 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     const float *kg = head_at(a.k, a.L.k, c.b, c.g);
     const float *vg = head_at(a.v, a.L.v, c.b, c.g);
 
+    // The first K/V tile is requested before the query row, so the two latencies overlap.
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1 + qo) / 32 + 1 : (Tk + 31) / 32;
+    KVStager<D> stg;
+    stg.load(kg, vg, a.L.k.st, a.L.v.st, 0, Tk, wave, nw, lane);
+
     float qr[C::NS];
     load_row_half<D, ROPE>(qr, head_at(a.q, a.L.q, c.b, c.h), a.L.q.st, qrow, T, half, a.qscale,
                            a.rope);
@@ -303,12 +325,6 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
     float m = kNegBig, l = 0.f;
 
-    const int wg_rows = 32 * a.rb;
-    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
-    const int ntiles = CAUSAL ? (wg_end - 1 + qo) / 32 + 1 : (Tk + 31) / 32;
-
-    KVStager<D> stg;
-    stg.load(kg, vg, a.L.k.st, a.L.v.st, 0, Tk, wave, nw, lane);
     stg.store(sK[0], sV[0], 0, Tk, wave, nw, lane);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
@@ -403,9 +419,27 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
     const float *kg = head_at(a.k, a.L.k, c.b, c.g);
     const float *vg = head_at(a.v, a.L.v, c.b, c.g);
 
-    float qr[C::NS], dor[C::NS];
-    load_row_half<D, ROPE>(qr, head_at(a.q, a.L.q, c.b, c.h), a.L.q.st, qrow, T, half,
-                           ROPE ? 1.0f : a.qscale, a.rope);
+    // The first K/V tile, the row's q, dO and o and its lse are all requested before any is
+    // used, so their latencies overlap.
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
+    KVStager<D> stg;
+    stg.load(kg, vg, a.L.k.st, a.L.v.st, 0, T, wave, nw, lane);
+    float qr[C::NS], dor[C::NS], orow[C::NS];
+    load_row_half<D, false>(qr, head_at(a.q, a.L.q, c.b, c.h), a.L.q.st, qrow, T, half, 1.0f,
+                            a.rope);
+    load_row_half<D, false>(dor, head_at(a.dO, a.L.dO, c.b, c.h), a.L.dO.st, qrow, T, half, 1.0f,
+                            a.rope);
+    load_row_half<D, false>(orow, head_at(a.o, a.L.o, c.b, c.h), a.L.o.st, qrow, T, half, 1.0f,
+                            a.rope);
+    const float lse_row = a.lse[bh * T + min(qrow, T - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    if (ROPE) rotate_row_half<D>(qr, qrow, half, 1.0f, a.rope);
+    else {
+#pragma unroll
+        for (int i = 0; i < C::NS; ++i) qr[i] *= a.qscale;
+    }
     if (ROPE) {  // each query row is loaded by exactly one wave: keep its rotation, then scale
         if (qrow < T) {
 #pragma unroll
@@ -416,15 +450,10 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
 #pragma unroll
         for (int i = 0; i < C::NS; ++i) qr[i] *= a.qscale;
     }
-    load_row_half<D, false>(dor, head_at(a.dO, a.L.dO, c.b, c.h), a.L.dO.st, qrow, T, half, 1.0f,
-                            a.rope);
 
     // delta_i = sum_d dO_id o_id over this row; written once per row for the dK/dV pass.
     float delta;
     {
-        float orow[C::NS];
-        load_row_half<D, false>(orow, head_at(a.o, a.L.o, c.b, c.h), a.L.o.st, qrow, T, half, 1.0f,
-                                a.rope);
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < C::NS; ++i) part += dor[i] * orow[i];
@@ -432,7 +461,7 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
     }
     float lse2;
     if (qrow < T) {
-        lse2 = a.lse[bh * T + qrow] * kLog2e;
+        lse2 = lse_row * kLog2e;
         if (half == 0) a.delta[bh * T + qrow] = delta;
     } else {
         lse2 = INFINITY;  // padding row: P = 0
@@ -443,12 +472,6 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
 #pragma unroll
     for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
 
-    const int wg_rows = 32 * a.rb;
-    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
-    const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
-
-    KVStager<D> stg;
-    stg.load(kg, vg, a.L.k.st, a.L.v.st, 0, T, wave, nw, lane);
     stg.store(sK[0], sV[0], 0, T, wave, nw, lane);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
