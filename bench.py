@@ -8,7 +8,8 @@ One step is one pass of the whole path over one batch of synthetic inputs alread
 HBM: the forward (o, lse), then the two backward passes (dq + delta, then dk, dv), i.e. exactly
 what ne_attn_fwd_ex followed by ne_attn_bwd_ex enqueue.  With RoPE the forward and the dq pass
 each start with the pre-pass that rotates k (forward) or q and k (dq pass) into the workspace;
-their per-call durations include it.  The K timed steps are
+their per-call durations include it.  Untimed warm-up runs at least W steps and at least
+half a second, so that the GPU clock has settled; the K timed steps are then
 bracketed by device synchronisations; `value` is algorithmic TFLOP/s (causal FLOPs counted as
 half of dense; forward 2 GEMMs, backward 5) over the wall-clock time per step.
 
@@ -188,6 +189,25 @@ def cpu_baseline_decode(w, x, min_seconds: float):
 
 
 GRAPH_STEPS = 10  # steps captured in one graph by the single-launch benches (--graph)
+# Untimed warm-up lasts at least this long (and at least --warmup steps): the shader clock of an
+# idle MI355X ramps up over tens of milliseconds of sustained load, so a few warm-up steps time
+# the ramp rather than the sustained rate (the GPU model's step measured 0.367 ms over 20 steps
+# after 10 warm-up steps, 0.335 ms once the clock had settled).
+WARM_S = 0.5
+
+
+def warm_up(torch, run, n: int):
+    """Runs `run` n times, then keeps running it until WARM_S seconds have passed; returns the
+    seconds spent."""
+    t0 = time.perf_counter()
+    for _ in range(n):
+        run()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < WARM_S:
+        for _ in range(8):
+            run()
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def timed_steps(torch, np, dev, a, make_step):
@@ -198,9 +218,7 @@ def timed_steps(torch, np, dev, a, make_step):
     kernel) is out of the timed region; events then bracket each replay."""
     step = make_step(torch.cuda.current_stream(dev))
     if not a.graph:
-        for _ in range(a.warmup):
-            step()
-        torch.cuda.synchronize()
+        warm_up(torch, step, a.warmup)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
         gc.disable()
         t0 = time.perf_counter()
@@ -224,9 +242,7 @@ def timed_steps(torch, np, dev, a, make_step):
         for _ in range(GRAPH_STEPS):
             st()
     reps = max(1, a.steps // GRAPH_STEPS)
-    for _ in range(max(1, a.warmup // GRAPH_STEPS)):
-        g.replay()
-    torch.cuda.synchronize()
+    warm_up(torch, g.replay, max(1, a.warmup // GRAPH_STEPS))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     gc.disable()
     t0 = time.perf_counter()
@@ -451,9 +467,7 @@ def main_block(a):
         if e is not None:
             e[2].record()
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(torch, step, a.warmup)
     gc.disable()
     t0 = time.perf_counter()
     for i in range(a.steps):
@@ -585,9 +599,7 @@ def main():
         with torch.cuda.graph(graph):
             step(calls_=bind(torch.cuda.current_stream()))
 
-    for _ in range(a.warmup):
-        graph.replay() if graph is not None else step()
-    torch.cuda.synchronize()
+    warm_up(torch, graph.replay if graph is not None else step, a.warmup)
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
               for _ in range(a.steps)]
