@@ -293,6 +293,70 @@ __device__ __forceinline__ void accum_t(f32x16 (&acc)[Cfg<D>::ND], const float *
     }
 }
 
+// Online-softmax step of one S^T tile (32 keys x this wave's 32 queries, keys from k0): masks
+// keys after the query (position qpos) or past the end, moves the reference maximum m, rescaling
+// l and O when it does, and turns s into the tile's probabilities.  p0: position of the wave's
+// first query row.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_softmax(f32x16 &s, f32x16 (&acc)[Cfg<D>::ND], float &m,
+                                            float &l, int k0, int p0, int qpos, int Tk, int half) {
+    if ((CAUSAL && k0 + 31 > p0) || k0 + 32 > Tk) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int key = k0 + acc_row(v, half);
+            if ((CAUSAL && key > qpos) || key >= Tk) s[v] = -INFINITY;
+        }
+    }
+    // Lazy rescale: the reference maximum m only moves when a score of this lane's row
+    // exceeds it by more than 2^8 (probabilities up to 256 are exact enough in fp32 sums), so
+    // most tiles skip the rescale of l and O.  The row maximum over both lane halves is only
+    // formed when some lane needs it.
+    const auto mx3 = [](float x, float y, float z) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+    };
+    const float lmax = __builtin_elementwise_maximum(
+        mx3(mx3(s[0], s[1], s[2]), mx3(s[3], s[4], s[5]), mx3(s[6], s[7], s[8])),
+        mx3(mx3(s[9], s[10], s[11]), mx3(s[12], s[13], s[14]), s[15]));
+    if (__builtin_amdgcn_ballot_w64(lmax > m + 8.0f) != 0) {
+        // Only the rows that need it move (others keep m bit for bit, whatever the other rows
+        // of the wave hold).
+        const float rmax = fmaxf(lmax, swap_halves(lmax));
+        if (rmax > m + 8.0f) {
+            const float alpha = fast_exp2(m - rmax);
+            m = rmax;
+            l *= alpha;
+#pragma unroll
+            for (int dd = 0; dd < Cfg<D>::ND; ++dd) acc[dd] *= alpha;
+        }
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        s[v] = fast_exp2(s[v] - m);
+        ps += s[v];
+    }
+    l += ps;
+}
+
+// The forward's epilogue: O = acc / l and the natural-log LSE of the wave's rows.
+template <int D>
+__device__ __forceinline__ void fwd_store(const Args &a, int b, int h, int qrow, int half,
+                                          const f32x16 (&acc)[Cfg<D>::ND], float m, float l) {
+    l += swap_halves(l);
+    if (qrow < a.T) {
+        const float inv = 1.0f / l;
+        float *orow = head_at(a.out_o, a.L.o, b, h) + qrow * a.L.o.st;
+#pragma unroll
+        for (int dd = 0; dd < Cfg<D>::ND; ++dd)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                st4(orow + dd * 32 + 8 * u + 4 * half,
+                    f32x4{acc[dd][4 * u] * inv, acc[dd][4 * u + 1] * inv, acc[dd][4 * u + 2] * inv,
+                          acc[dd][4 * u + 3] * inv});
+        if (half == 0) a.out_lse[((size_t)b * a.Hq + h) * a.T + qrow] = m * kLn2 + logf(l);
+    }
+}
+
 template <int D, bool CAUSAL, bool ROPE>
 __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&sK)[2][32 * Cfg<D>::LD],
                                          float (&sV)[2][32 * Cfg<D>::LD]) {
@@ -305,7 +369,6 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     const int T = a.T, Tk = a.Tk, qo = a.qoff;
     const int qrow = c.r0 + col;
     const int p0 = c.r0 + qo;  // position of the wave's first row
-    const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
     const float *kg = head_at(a.k, a.L.k, c.b, c.g);
     const float *vg = head_at(a.v, a.L.v, c.b, c.g);
 
@@ -334,61 +397,13 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
         const int k0 = j * 32;
         if (c.r0 < T && (!CAUSAL || k0 <= p0 + 31)) {
             f32x16 s = scores_t<D>(sK[buf], qr, col, half);
-            if ((CAUSAL && k0 + 31 > p0) || k0 + 32 > Tk) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = k0 + acc_row(v, half);
-                    if ((CAUSAL && key > qrow + qo) || key >= Tk) s[v] = -INFINITY;
-                }
-            }
-            // Lazy rescale: the reference maximum m only moves when a score of this lane's row
-            // exceeds it by more than 2^8 (probabilities up to 256 are exact enough in fp32
-            // sums), so most tiles skip the rescale of l and O.  The row maximum over both
-            // lane halves is only formed when some lane needs it.
-            const auto mx3 = [](float x, float y, float z) {
-                return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
-            };
-            const float lmax = __builtin_elementwise_maximum(
-                mx3(mx3(s[0], s[1], s[2]), mx3(s[3], s[4], s[5]), mx3(s[6], s[7], s[8])),
-                mx3(mx3(s[9], s[10], s[11]), mx3(s[12], s[13], s[14]), s[15]));
-            if (__builtin_amdgcn_ballot_w64(lmax > m + 8.0f) != 0) {
-                // Only the rows that need it move (others keep m bit for bit, whatever the
-                // other rows of the wave hold).
-                const float rmax = fmaxf(lmax, swap_halves(lmax));
-                if (rmax > m + 8.0f) {
-                    const float alpha = fast_exp2(m - rmax);
-                    m = rmax;
-                    l *= alpha;
-#pragma unroll
-                    for (int dd = 0; dd < C::ND; ++dd) acc[dd] *= alpha;
-                }
-            }
-            float ps = 0.f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                s[v] = fast_exp2(s[v] - m);
-                ps += s[v];
-            }
-            l += ps;
+            fwd_softmax<D, CAUSAL>(s, acc, m, l, k0, p0, qrow + qo, Tk, half);
             accum_t<D>(acc, sV[buf], s, col, half);
         }
         if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, Tk, wave, nw, lane);
         __syncthreads();
     }
-
-    l += swap_halves(l);
-    if (qrow < T) {
-        const float inv = 1.0f / l;
-        float *orow = head_at(a.out_o, a.L.o, c.b, c.h) + qrow * a.L.o.st;
-#pragma unroll
-        for (int dd = 0; dd < C::ND; ++dd)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                st4(orow + dd * 32 + 8 * u + 4 * half,
-                    f32x4{acc[dd][4 * u] * inv, acc[dd][4 * u + 1] * inv, acc[dd][4 * u + 2] * inv,
-                          acc[dd][4 * u + 3] * inv});
-        if (half == 0) a.out_lse[bh * T + qrow] = m * kLn2 + logf(l);
-    }
+    fwd_store<D>(a, c.b, c.h, qrow, half, acc, m, l);
 }
 
 template <int D, bool CAUSAL, bool ROPE>
@@ -405,33 +420,22 @@ fwd_f32(Args a) {
     }
 }
 
-template <int D, bool CAUSAL, bool ROPE>
-__device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&sK)[2][32 * Cfg<D>::LD],
-                                        float (&sV)[2][32 * Cfg<D>::LD]) {
+// The dQ pass's row set-up for this lane's query row: q (rotated with RoPE, the rotation kept in
+// qrot for the dK/dV pass, then scaled) and dO in registers, delta_i = dO_i . o_i (written once
+// per row for the dK/dV pass) and lse * log2(e).  Rows past the end get P = 0.  The caller may
+// request other reads first: every read here is issued before any is used.
+template <int D, bool ROPE>
+__device__ __forceinline__ void dq_rows(const Args &a, int b, int h, int qrow, int half,
+                                        float (&qr)[Cfg<D>::NS], float (&dor)[Cfg<D>::NS],
+                                        float &lse2, float &delta) {
     using C = Cfg<D>;
-    const int nw = blockDim.x >> 6;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int half = lane >> 5, col = lane & 31;
     const int T = a.T;
-    const int qrow = c.r0 + col;
-    const size_t bh = (size_t)c.b * a.Hq + c.h, bg = (size_t)c.b * a.Hkv + c.g;
-    const float *kg = head_at(a.k, a.L.k, c.b, c.g);
-    const float *vg = head_at(a.v, a.L.v, c.b, c.g);
-
-    // The first K/V tile, the row's q, dO and o and its lse are all requested before any is
-    // used, so their latencies overlap.
-    const int wg_rows = 32 * a.rb;
-    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
-    const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
-    KVStager<D> stg;
-    stg.load(kg, vg, a.L.k.st, a.L.v.st, 0, T, wave, nw, lane);
-    float qr[C::NS], dor[C::NS], orow[C::NS];
-    load_row_half<D, false>(qr, head_at(a.q, a.L.q, c.b, c.h), a.L.q.st, qrow, T, half, 1.0f,
+    const size_t bh = (size_t)b * a.Hq + h;
+    float orow[C::NS];
+    load_row_half<D, false>(qr, head_at(a.q, a.L.q, b, h), a.L.q.st, qrow, T, half, 1.0f, a.rope);
+    load_row_half<D, false>(dor, head_at(a.dO, a.L.dO, b, h), a.L.dO.st, qrow, T, half, 1.0f,
                             a.rope);
-    load_row_half<D, false>(dor, head_at(a.dO, a.L.dO, c.b, c.h), a.L.dO.st, qrow, T, half, 1.0f,
-                            a.rope);
-    load_row_half<D, false>(orow, head_at(a.o, a.L.o, c.b, c.h), a.L.o.st, qrow, T, half, 1.0f,
+    load_row_half<D, false>(orow, head_at(a.o, a.L.o, b, h), a.L.o.st, qrow, T, half, 1.0f,
                             a.rope);
     const float lse_row = a.lse[bh * T + min(qrow, T - 1)];
     __builtin_amdgcn_sched_barrier(0);
@@ -450,16 +454,12 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
 #pragma unroll
         for (int i = 0; i < C::NS; ++i) qr[i] *= a.qscale;
     }
-
-    // delta_i = sum_d dO_id o_id over this row; written once per row for the dK/dV pass.
-    float delta;
     {
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < C::NS; ++i) part += dor[i] * orow[i];
         delta = part + swap_halves(part);
     }
-    float lse2;
     if (qrow < T) {
         lse2 = lse_row * kLog2e;
         if (half == 0) a.delta[bh * T + qrow] = delta;
@@ -467,6 +467,67 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
         lse2 = INFINITY;  // padding row: P = 0
         delta = 0.f;
     }
+}
+
+// One key tile of the dQ pass, from its S^T (p) and dP^T (ds): P^T = exp2(S^T - lse2), zero
+// for keys after the query or past the end, then dS^T = P^T (dP^T - delta).
+template <bool CAUSAL>
+__device__ __forceinline__ void dq_dscores(f32x16 &p, f32x16 &ds, float lse2, float delta, int k0,
+                                           int r0, int qrow, int T, int half) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = fast_exp2(p[v] - lse2);
+    if ((CAUSAL && k0 + 31 > r0) || k0 + 32 > T) {  // a block on the diagonal or the end
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int key = k0 + acc_row(v, half);
+            if ((CAUSAL && key > qrow) || key >= T) p[v] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
+}
+
+// dQ = scale * acc (rotated back with RoPE) for the wave's rows.
+template <int D, bool ROPE>
+__device__ __forceinline__ void dq_store(const Args &a, int b, int h, int qrow, int half,
+                                         const f32x16 (&acc)[Cfg<D>::ND]) {
+    if (qrow < a.T) {
+        float *drow = head_at(a.dq, a.L.dq, b, h) + qrow * a.L.dq.st;
+#pragma unroll
+        for (int dd = 0; dd < Cfg<D>::ND; ++dd)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int d = dd * 32 + 8 * u + 4 * half;
+                f32x4 x{acc[dd][4 * u] * a.scale, acc[dd][4 * u + 1] * a.scale,
+                        acc[dd][4 * u + 2] * a.scale, acc[dd][4 * u + 3] * a.scale};
+                if (ROPE) x = rope4<D>(x, qrow, d, a.rope, true);
+                st4(drow + d, x);
+            }
+    }
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&sK)[2][32 * Cfg<D>::LD],
+                                        float (&sV)[2][32 * Cfg<D>::LD]) {
+    using C = Cfg<D>;
+    const int nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const int T = a.T;
+    const int qrow = c.r0 + col;
+    const float *kg = head_at(a.k, a.L.k, c.b, c.g);
+    const float *vg = head_at(a.v, a.L.v, c.b, c.g);
+
+    // The first K/V tile, the row's q, dO and o and its lse are all requested before any is
+    // used, so their latencies overlap.
+    const int wg_rows = 32 * a.rb;
+    const int wg_end = min(c.qt * wg_rows + wg_rows, T);
+    const int ntiles = CAUSAL ? (wg_end - 1) / 32 + 1 : (T + 31) / 32;
+    KVStager<D> stg;
+    stg.load(kg, vg, a.L.k.st, a.L.v.st, 0, T, wave, nw, lane);
+    float qr[C::NS], dor[C::NS], lse2, delta;
+    dq_rows<D, ROPE>(a, c.b, c.h, qrow, half, qr, dor, lse2, delta);
 
     f32x16 acc[C::ND];
 #pragma unroll
@@ -482,36 +543,13 @@ __device__ __forceinline__ void dq_tile(const Args &a, const QTile &c, float (&s
         if (c.r0 < T && (!CAUSAL || k0 <= c.r0 + 31)) {
             f32x16 p = scores_t<D>(sK[buf], qr, col, half);
             f32x16 ds = scores_t<D>(sV[buf], dor, col, half);  // dP^T = V dO^T
-#pragma unroll
-            for (int v = 0; v < 16; ++v) p[v] = fast_exp2(p[v] - lse2);
-            if ((CAUSAL && k0 + 31 > c.r0) || k0 + 32 > T) {  // a block on the diagonal or the end
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = k0 + acc_row(v, half);
-                    if ((CAUSAL && key > qrow) || key >= T) p[v] = 0.f;
-                }
-            }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) ds[v] = p[v] * (ds[v] - delta);
+            dq_dscores<CAUSAL>(p, ds, lse2, delta, k0, c.r0, qrow, T, half);
             accum_t<D>(acc, sK[buf], ds, col, half);  // dQ^T += K^T dS^T
         }
         if (more) stg.store(sK[buf ^ 1], sV[buf ^ 1], j + 1, T, wave, nw, lane);
         __syncthreads();
     }
-
-    if (qrow < T) {
-        float *drow = head_at(a.dq, a.L.dq, c.b, c.h) + qrow * a.L.dq.st;
-#pragma unroll
-        for (int dd = 0; dd < C::ND; ++dd)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int d = dd * 32 + 8 * u + 4 * half;
-                f32x4 x{acc[dd][4 * u] * a.scale, acc[dd][4 * u + 1] * a.scale,
-                        acc[dd][4 * u + 2] * a.scale, acc[dd][4 * u + 3] * a.scale};
-                if (ROPE) x = rope4<D>(x, qrow, d, a.rope, true);
-                st4(drow + d, x);
-            }
-    }
+    dq_store<D, ROPE>(a, c.b, c.h, qrow, half, acc);
 }
 
 template <int D, bool CAUSAL, bool ROPE>
@@ -526,6 +564,174 @@ dq_f32(Args a) {
         __syncthreads();
         dq_tile<D, CAUSAL, ROPE>(a, qtile_of(a, w, w.qt1, wave), sK, sV);
     }
+}
+
+// Single-wave query-tile launches.  With a group of G query heads per kv head, the multi-wave
+// work-groups above put G waves on the 4 SIMDs of a compute unit; when G is not a multiple of 4
+// the SIMDs end up with unequal work (at G = 3 the paired dQ launch leaves half of them with one
+// wave and half with two).  Here every work-group is one wave, which the dispatcher spreads
+// evenly over the SIMDs, longest tiles first; each wave stages its own K/V tiles through a
+// single padded LDS buffer, the next tile's rows travelling in registers meanwhile.
+
+// One 32-row K or V tile of a single wave: all chunks into registers, then into LDS (padded
+// rows; rows past the end as zeros).
+template <int D>
+struct TileRegs {
+    using C = Cfg<D>;
+    f32x4 r[C::CH];
+    __device__ __forceinline__ void load(const float *gp, int rs, int tile, int T, int lane) {
+        const int c4 = 4 * (lane % C::C4);
+#pragma unroll
+        for (int i = 0; i < C::CH; ++i) {
+            const int row = min(tile * 32 + i * C::RPC + lane / C::C4, T - 1);
+            r[i] = ld4(gp + row * rs + c4);
+        }
+    }
+    __device__ __forceinline__ void store(float *sX, int tile, int T, int lane) const {
+        const int c4 = 4 * (lane % C::C4);
+        const f32x4 zero{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < C::CH; ++i) {
+            const int rr = i * C::RPC + lane / C::C4;
+            st4(sX + rr * C::LD + c4, tile * 32 + rr < T ? r[i] : zero);
+        }
+    }
+};
+
+// Keeps the compiler from moving this wave's LDS reads and writes across this point (the
+// hardware executes one wave's LDS instructions in order).
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct Work1 {
+    int b, g, h, qt;
+};
+
+// Work-group -> (batch, kv head, query head, 32-row tile), longest tiles first.  Work-groups go
+// round-robin over the 8 XCDs (XCD = blockIdx % 8); when the (batch, kv head) pairs divide
+// evenly, each XCD takes its own set of them, so the K/V rows its waves stream are shared
+// through its L2.
+__device__ __forceinline__ Work1 decode_1w(const Args &a) {
+    const int nbg = a.B * a.Hkv;
+    int bg, hl, t;
+    if (nbg % 8 == 0) {
+        const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+        const int per = (nbg / 8) * a.G;
+        t = y / per;
+        const int r = y % per;
+        hl = r % a.G;
+        bg = x * (nbg / 8) + r / a.G;
+    } else {
+        const int per = nbg * a.G;
+        t = blockIdx.x / per;
+        const int r = blockIdx.x % per;
+        hl = r % a.G;
+        bg = r / a.G;
+    }
+    Work1 w;
+    w.b = bg / a.Hkv;
+    w.g = bg % a.Hkv;
+    w.h = w.g * a.G + hl;
+    w.qt = a.nqt - 1 - t;
+    return w;
+}
+
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+fwd_f32_1w(Args a) {
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(16))) float sK[32 * Cfg<D>::LD];
+    __shared__ __attribute__((aligned(16))) float sV[32 * Cfg<D>::LD];
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const Work1 w = decode_1w(a);
+    const int T = a.T, Tk = a.Tk, qo = a.qoff;
+    const int r0 = w.qt * 32, qrow = r0 + col, p0 = r0 + qo;
+    const float *kg = head_at(a.k, a.L.k, w.b, w.g);
+    const float *vg = head_at(a.v, a.L.v, w.b, w.g);
+    const int ntiles = CAUSAL ? (min(r0 + 32, T) - 1 + qo) / 32 + 1 : (Tk + 31) / 32;
+    // The first K/V tile is requested before the query row, so the two latencies overlap.
+    TileRegs<D> tk, tv;
+    tk.load(kg, a.L.k.st, 0, Tk, lane);
+    tv.load(vg, a.L.v.st, 0, Tk, lane);
+    float qr[C::NS];
+    load_row_half<D, ROPE>(qr, head_at(a.q, a.L.q, w.b, w.h), a.L.q.st, qrow, T, half, a.qscale,
+                           a.rope);
+    f32x16 acc[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
+    float m = kNegBig, l = 0.f;
+    tk.store(sK, 0, Tk, lane);
+    tv.store(sV, 0, Tk, lane);
+    wave_lds_order();
+    for (int j = 0; j < ntiles; ++j) {
+        const bool more = j + 1 < ntiles;
+        if (more) {  // the next tile's rows travel in registers while this one is used
+            tk.load(kg, a.L.k.st, j + 1, Tk, lane);
+            tv.load(vg, a.L.v.st, j + 1, Tk, lane);
+        }
+        f32x16 s = scores_t<D>(sK, qr, col, half);
+        fwd_softmax<D, CAUSAL>(s, acc, m, l, j * 32, p0, qrow + qo, Tk, half);
+        accum_t<D>(acc, sV, s, col, half);
+        if (more) {
+            wave_lds_order();
+            tk.store(sK, j + 1, Tk, lane);
+            tv.store(sV, j + 1, Tk, lane);
+            wave_lds_order();
+        }
+    }
+    fwd_store<D>(a, w.b, w.h, qrow, half, acc, m, l);
+}
+
+// The dQ pass in single-wave work-groups.  One register tile carries the next rows: V's after
+// this tile's two score products (the last reads of V), then K's after dQ's (the last of K).
+template <int D, bool CAUSAL, bool ROPE>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+dq_f32_1w(Args a) {
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(16))) float sK[32 * Cfg<D>::LD];
+    __shared__ __attribute__((aligned(16))) float sV[32 * Cfg<D>::LD];
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5, col = lane & 31;
+    const Work1 w = decode_1w(a);
+    const int T = a.T;
+    const int r0 = w.qt * 32, qrow = r0 + col;
+    const float *kg = head_at(a.k, a.L.k, w.b, w.g);
+    const float *vg = head_at(a.v, a.L.v, w.b, w.g);
+    const int ntiles = CAUSAL ? (min(r0 + 32, T) - 1) / 32 + 1 : (T + 31) / 32;
+    TileRegs<D> tr;
+    tr.load(kg, a.L.k.st, 0, T, lane);
+    float qr[C::NS], dor[C::NS], lse2, delta;
+    dq_rows<D, ROPE>(a, w.b, w.h, qrow, half, qr, dor, lse2, delta);
+    tr.store(sK, 0, T, lane);
+    tr.load(vg, a.L.v.st, 0, T, lane);
+    f32x16 acc[C::ND];
+#pragma unroll
+    for (int dd = 0; dd < C::ND; ++dd) acc[dd] = zero16();
+    tr.store(sV, 0, T, lane);
+    wave_lds_order();
+    for (int j = 0; j < ntiles; ++j) {
+        const bool more = j + 1 < ntiles;
+        if (more) tr.load(vg, a.L.v.st, j + 1, T, lane);
+        f32x16 p = scores_t<D>(sK, qr, col, half);
+        f32x16 ds = scores_t<D>(sV, dor, col, half);  // dP^T = V dO^T
+        if (more) {
+            wave_lds_order();
+            tr.store(sV, j + 1, T, lane);
+            tr.load(kg, a.L.k.st, j + 1, T, lane);
+        }
+        dq_dscores<CAUSAL>(p, ds, lse2, delta, j * 32, r0, qrow, T, half);
+        accum_t<D>(acc, sK, ds, col, half);  // dQ^T += K^T dS^T
+        if (more) {
+            wave_lds_order();
+            tr.store(sK, j + 1, T, lane);
+        }
+        wave_lds_order();
+    }
+    dq_store<D, ROPE>(a, w.b, w.h, qrow, half, acc);
 }
 
 // Floats of LDS per dK/dV wave: a query tile and a dO tile (32 padded rows each), lse2, delta.
@@ -862,6 +1068,8 @@ NE_PICK(fwd_f32)
 NE_PICK(dq_f32)
 NE_PICK(dkdv_f32)
 NE_PICK(dkdvq_f32)
+NE_PICK(fwd_f32_1w)
+NE_PICK(dq_f32_1w)
 #undef NE_PICK
 
 hipError_t launch(const void *fn, long long blocks, int threads, size_t lds, hipStream_t st, Args &a) {
@@ -939,6 +1147,17 @@ KBlockGeom kblock_geometry(const Shape &s, bool pair) {
     return g;
 }
 
+// Single-wave query-tile work-groups (fwd_f32_1w, dq_f32_1w) for causal attention over the
+// sequence itself (tiles of unequal length) at head sizes up to 64, when the group of query
+// heads sharing a kv head does not fill the 4 SIMDs of a compute unit evenly.  A prefill chunk's
+// tiles all see the whole history, and there the multi-wave groups, which share each K/V tile
+// between the group's heads, measured faster.
+long long single_wave_blocks(const Shape &s) {
+    if (!s.causal || (s.Tk != 0 && s.Tk != s.T) || s.D > 64 || s.G % 4 == 0) return 0;
+    const long long n = (long long)s.B * s.Hq * ((s.T + 31) / 32);
+    return n <= 0x7fffffffLL ? n : 0;
+}
+
 hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const float *v, float *o,
                           float *lse, hipStream_t st) {
     Args a = make_args(s);
@@ -953,6 +1172,11 @@ hipError_t launch_fwd_f32(const Shape &s, const float *q, const float *k, const 
     a.nqt = g.nqt;
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
+    if (const long long n1 = single_wave_blocks(s)) {
+        a.nqt = (s.T + 31) / 32;
+        const void *f1 = s.D == 64 ? pick_fwd_f32_1w<64>(causal, rope) : pick_fwd_f32_1w<32>(causal, rope);
+        return launch(f1, n1, 64, 0, st, a);
+    }
     const void *fn = s.D == 128  ? pick_fwd_f32<128>(causal, rope)
                      : s.D == 64 ? pick_fwd_f32<64>(causal, rope)
                                  : pick_fwd_f32<32>(causal, rope);
@@ -979,6 +1203,11 @@ hipError_t launch_dq_f32(const Shape &s, const float *q, const float *k, const f
     a.nqt = g.nqt;
     a.paired = g.paired;
     const bool causal = s.causal != 0, rope = a.rope.on != 0;
+    if (const long long n1 = single_wave_blocks(s)) {
+        a.nqt = (s.T + 31) / 32;
+        const void *f1 = s.D == 64 ? pick_dq_f32_1w<64>(causal, rope) : pick_dq_f32_1w<32>(causal, rope);
+        return launch(f1, n1, 64, 0, st, a);
+    }
     const void *fn = s.D == 128  ? pick_dq_f32<128>(causal, rope)
                      : s.D == 64 ? pick_dq_f32<64>(causal, rope)
                                  : pick_dq_f32<32>(causal, rope);
