@@ -41,8 +41,10 @@ RAGGED = [
     (1, 5, 5, 96, 32), (1, 1, 1, 31, 64), (3, 2, 2, 7, 64),
     # group sizes 5..8: work-groups of 5..8 waves
     (1, 10, 2, 77, 64), (1, 6, 1, 100, 64), (1, 7, 1, 90, 32), (1, 8, 1, 200, 64),
-    # 256 work-groups per tile index: the forward's mirrored tile order with a stride of one row
+    # 256 (batch, kv head) pairs: single-wave fp32 launches with the per-XCD pair sets
     (64, 4, 4, 128, 32),
+    # 256 work-groups per tile index: the forward's mirrored tile order with a stride of one row
+    (64, 16, 4, 128, 32),
     # head size 128 (work-groups of at most 4 waves, one wave per SIMD)
     (1, 4, 2, 64, 128), (1, 3, 1, 77, 128), (2, 12, 4, 130, 128), (1, 8, 1, 100, 128),
     (1, 2, 2, 33, 128), (1, 16, 2, 257, 128),
