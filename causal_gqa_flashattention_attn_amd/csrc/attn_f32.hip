@@ -406,8 +406,10 @@ __device__ __forceinline__ void fwd_tile(const Args &a, const QTile &c, float (&
     fwd_store<D>(a, c.b, c.h, qrow, half, acc, m, l);
 }
 
+// At D = 128 the forward without RoPE fits two waves per SIMD without spilling (the rotation's
+// registers push the RoPE variant to one).
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(D == 128 ? 256 : 512) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : NE_FWD_WAVES_PER_EU)))
+__global__ void __launch_bounds__(D == 128 ? 256 : 512) __attribute__((amdgpu_waves_per_eu(D == 128 && ROPE ? 1 : NE_FWD_WAVES_PER_EU)))
 fwd_f32(Args a) {
     __shared__ __attribute__((aligned(16))) float sK[2][32 * Cfg<D>::LD];
     __shared__ __attribute__((aligned(16))) float sV[2][32 * Cfg<D>::LD];
