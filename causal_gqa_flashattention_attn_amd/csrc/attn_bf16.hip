@@ -8,8 +8,10 @@
 // (openai-hub), implementation details; grouped-query heads and RoPE on queries and keys:
 // README translations, section "Architecture").
 //
-// RoPE: the pair (x[2i], x[2i+1]) at position t is rotated by t * base^(-2i/D) in fp32 when q
-// and k are loaded; the rotated values are rounded to bf16 before they enter the matrix cores.
+// RoPE: the pair (x[2i], x[2i+1]) at position t is rotated by t * base^(-2i/D) in fp32: q when a
+// wave loads its rows (the dQ pass keeps its rotated rows in the workspace for the dK/dV pass),
+// k once by a pre-pass into the workspace (rope_rows_bf16), since the K/V tiles reach LDS by
+// direct copies; the rotated values are rounded to bf16 before they enter the matrix cores.
 // The angle is formed and reduced modulo one turn in double precision (per-pair turn rates are
 // evaluated on the host in double), so it is exact to float rounding at every position.  dq and
 // dk are rotated back (transpose) in fp32 before rounding, so they are gradients with respect to

@@ -19,11 +19,16 @@
 //   dq_f32    same decomposition; first computes delta_i = dO_i . o_i for its rows (written to
 //             the workspace for the dK/dV pass), then per tile S^T, P^T = exp2(S^T - lse2),
 //             dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
+//   fwd_f32_1w, dq_f32_1w
+//             the same per-tile work in one-wave work-groups, each wave staging its own K/V
+//             tiles: for causal self-attention when the group's query heads do not fill a
+//             compute unit's four SIMDs evenly (head sizes up to 64).
 //   dkdv_f32  one work-group per (batch, kv head, 32-key block); K and V stay in registers, the
 //             group's query heads are split over the waves, each streaming its own query
 //             blocks through LDS: S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
-//             The waves' partial sums are added in LDS in a fixed order: no atomics anywhere,
-//             so results are reproducible bit for bit.
+//             The waves' partial sums are added in LDS in a fixed order: the two-pass backward
+//             uses no atomics, so its results are reproducible bit for bit.
+//   dkdvq_f32 the single-pass backward: dkdv_f32 plus dQ added into dq with atomics.
 #include <math.h>
 
 #include <algorithm>
