@@ -30,6 +30,44 @@ def test_library_exports_every_declared_symbol(ne):
         assert hasattr(L, name), name
 
 
+C_CONSUMER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "ne_attn.h"
+int main(void) {
+    /* sizes: delta only without RoPE; 4 bytes per (batch, query head, position) */
+    if (ne_attn_workspace_bytes(2, 4, 2, 64, 32, NE_F32, 0.0f) != 4u * 2 * 4 * 64) return 1;
+    if (ne_attn_bwd_workspace_bytes(2, 4, 64) != 4u * 2 * 4 * 64) return 2;
+    /* argument errors come back before any launch */
+    if (ne_attn_fwd(NULL, NULL, NULL, NULL, NULL, 1, 4, 2, 64, 32, 1, NULL) != NE_ERR_NULL) return 3;
+    if (strlen(ne_attn_strerror(NE_ERR_SHAPE)) == 0) return 4;
+    printf("ok\n");
+    return 0;
+}
+"""
+
+
+def test_header_is_c99_and_the_library_links_from_c(ne, tmp_path):
+    """A plain C99 program (no C++, no torch) includes the header under -pedantic -Werror, links
+    the library and calls entry points that need no GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    lib_dir = os.path.dirname(ne.library_path())
+    src = tmp_path / "consumer.c"
+    exe = tmp_path / "consumer"
+    src.write_text(C_CONSUMER)
+    cmd = [gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I",
+           os.path.join(ROOT, "include"), str(src), "-o", str(exe), "-L", lib_dir, "-lne_attn",
+           "-Wl,-rpath," + lib_dir, "-Wl,-rpath-link,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
 def test_strerror_covers_every_status(ne):
     seen = set()
     for st in range(7):
